@@ -1,0 +1,265 @@
+"""CPU oracle for the VC-Attention hot path.
+
+TEST INFRASTRUCTURE ONLY: only the test-suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. It shares no code with
+the HIP library and never imports it.
+
+Two parts (paper: "VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+Attention", arXiv 2609.15810):
+
+* ``attention_exact`` -- the plain definition O = softmax(Q K^T / sqrt(d)) V in
+  binary64 (study-notes page, section 1-1).
+* the bit-level emulation of the quantised pipeline: ``kmeans`` (paper page,
+  method step (1)), ``quantize`` (step (2)), ``attention_emul`` (steps (3) and
+  (4)). The arithmetic lives in ``vc_oracle.c``; this module only marshals arrays.
+
+Every array here is one (batch, head) slice in row-major ``[N, d]`` order;
+bf16 tensors are passed as their raw ``uint16`` bit patterns.
+
+Parity status of each function is listed in ``PINS`` below.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vc_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FLAG_KSMOOTH = 1
+FLAG_VSMOOTH = 2
+MODE_EXPCAST = 0
+MODE_EXP_THEN_CAST = 1
+MODE_EXACT_PROB = 2
+BLOCK = 128
+
+# which test pins each oracle function (tests/test_oracle_*.py)
+PINS = {
+    "e4m3_decode/encode": "exhaustive 256-code table from the format definition; log-affine byte property",
+    "expcast": "closed-form per-octave agreement 79.61/15.80/4.58 %; TV bound 3.637 %",
+    "kmeans_assign": "brute force with Python integers on tiny inputs",
+    "kmeans_update": "exact rational means with fractions on tiny inputs",
+    "stable_argsort": "numpy.argsort(kind='stable')",
+    "quantize": "exactly representable constructions (codes, scales, means reproduced exactly)",
+    "attention_emul": "identity-quantiser special case equals exact attention; "
+                      "permutation invariance; mean restoration; brute-force scores",
+    "attention_exact": "permutation invariance; direct numpy evaluation on tiny inputs",
+}
+
+
+def build(force: bool = False) -> str:
+    """Compile vc_oracle.c into liboracle.so (gcc, OpenMP, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L = ctypes.c_int64
+        F = ctypes.c_float
+        _lib.or_e4m3_decode.restype = ctypes.c_double
+        _lib.or_e4m3_decode.argtypes = [ctypes.c_uint8]
+        _lib.or_e4m3_encode.restype = ctypes.c_uint8
+        _lib.or_e4m3_encode.argtypes = [F]
+        _lib.or_e4m3_encode_array.argtypes = [P, P, L]
+        _lib.or_e4m3_decode_array.argtypes = [P, P, L]
+        _lib.or_expcast.restype = ctypes.c_uint8
+        _lib.or_expcast.argtypes = [F, F, F]
+        _lib.or_expcast_array.argtypes = [P, P, P, P, L]
+        _lib.or_kmeans_assign.argtypes = [P, I, I, P, I, P]
+        _lib.or_stable_argsort.argtypes = [P, I, I, P]
+        _lib.or_kmeans_update.argtypes = [P, I, I, P, I, P]
+        _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
+        _lib.or_quantize.restype = I
+        _lib.or_quantize.argtypes = [P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
+        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P]
+        _lib.or_attention_exact.argtypes = [P, P, P, I, I, I, P, P]
+        _lib.or_exact_mean.restype = ctypes.c_double
+        _lib.or_exact_mean.argtypes = [P, L, I]
+        _lib.or_exact_sqdist_cmp.restype = I
+        _lib.or_exact_sqdist_cmp.argtypes = [P, P, P, I]
+        _lib.or_num_threads.restype = I
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(lib().or_num_threads())
+
+
+# ---------------------------------------------------------------- constants
+def log2e_over_sqrt_d(d: int) -> np.float32:
+    """c_L = fl32(log2(e) / sqrt(d)), from a 50-digit decimal evaluation."""
+    getcontext().prec = 50
+    v = (Decimal(1) / Decimal(2).ln()) / Decimal(d).sqrt()
+    return np.float32(float(v))  # the double carries > 50 bits; one more rounding to binary32
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------- E4M3 and ExpCast
+def e4m3_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().or_e4m3_decode_array(_p(c), _p(out), c.size)
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    a = _c(x, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().or_e4m3_encode_array(_p(a), _p(out), a.size)
+    return out
+
+
+def expcast(acc, scale8, bias) -> np.ndarray:
+    """c = clamp(rne(fma32(acc, scale8, bias)), 0, 120) elementwise (broadcasting)."""
+    acc, scale8, bias = np.broadcast_arrays(np.asarray(acc, np.float32), np.asarray(scale8, np.float32),
+                                            np.asarray(bias, np.float32))
+    a, s, b = _c(acc, np.float32), _c(scale8, np.float32), _c(bias, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().or_expcast_array(_p(a), _p(s), _p(b), _p(out), a.size)
+    return out
+
+
+# ---------------------------------------------------------------- k-means
+def kmeans_assign(V_bits: np.ndarray, chat: np.ndarray) -> np.ndarray:
+    V = _c(V_bits, np.uint16)
+    C = _c(chat, np.float32)
+    N, d = V.shape
+    labels = np.empty(N, np.int32)
+    lib().or_kmeans_assign(_p(V), N, d, _p(C), C.shape[0], _p(labels))
+    return labels
+
+
+def stable_argsort(labels: np.ndarray, K: int) -> np.ndarray:
+    z = _c(labels, np.int32)
+    perm = np.empty(z.shape[0], np.int32)
+    lib().or_stable_argsort(_p(z), z.shape[0], K, _p(perm))
+    return perm
+
+
+def kmeans_update(V_bits: np.ndarray, labels: np.ndarray, C: np.ndarray) -> np.ndarray:
+    V = _c(V_bits, np.uint16)
+    z = _c(labels, np.int32)
+    Cn = np.array(C, dtype=np.float32, copy=True, order="C")
+    N, d = V.shape
+    lib().or_kmeans_update(_p(V), N, d, _p(z), Cn.shape[0], _p(Cn))
+    return Cn
+
+
+def kmeans(V_bits: np.ndarray, K: int, iters: int, cold: bool, C: np.ndarray | None = None):
+    """Lloyd k-means on one head's value tokens. Returns (labels, perm, centroids)."""
+    V = _c(V_bits, np.uint16)
+    N, d = V.shape
+    Cn = np.zeros((K, d), np.float32) if C is None else np.array(C, dtype=np.float32, copy=True, order="C")
+    labels = np.empty(N, np.int32)
+    perm = np.empty(N, np.int32)
+    lib().or_kmeans(_p(V), N, d, K, iters, 1 if cold else 0, _p(Cn), _p(labels), _p(perm))
+    return labels, perm, Cn
+
+
+# ---------------------------------------------------------------- quantiser
+def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOTH) -> dict:
+    """Fused quantiser for one head. All outputs row-major; Vq rows are in permuted order."""
+    Q = _c(Q_bits, np.uint16)
+    K = _c(K_bits, np.uint16)
+    V = _c(V_bits, np.uint16)
+    N, d = Q.shape
+    nb = N // BLOCK
+    pm = None if perm is None else _c(perm, np.int32)
+    out = dict(
+        Qq=np.empty((N, d), np.uint8), sQ=np.empty(nb, np.float32),
+        Kq=np.empty((N, d), np.uint8), sK=np.empty(nb, np.float32),
+        Vq=np.empty((N, d), np.uint8), sV=np.empty(d, np.float32),
+        mu=np.zeros((nb, d), np.uint16), mu_scaled=np.zeros((nb, d), np.float32),
+        kbar=np.empty(d, np.float32),
+    )
+    rc = lib().or_quantize(_p(Q), _p(K), _p(V), None if pm is None else _p(pm), N, d, int(flags),
+                           float(log2e_over_sqrt_d(d)),
+                           _p(out["Qq"]), _p(out["sQ"]), _p(out["Kq"]), _p(out["sK"]), _p(out["Vq"]),
+                           _p(out["sV"]), _p(out["mu"]), _p(out["mu_scaled"]), _p(out["kbar"]))
+    if rc != 0:
+        raise ValueError("oracle quantize: N must be a multiple of 128")
+    out["flags"] = flags
+    return out
+
+
+# ---------------------------------------------------------------- attention
+def attention_emul(q: dict, rows, beta: float = -0.35, mode: int = MODE_EXPCAST, restore_mean: bool = True,
+                   dump_block: int = -1, want_m: bool = False):
+    """Online-softmax emulation on the given query rows. Returns O [rows, d] (binary64)
+    and, when dump_block >= 0, the probability bytes of that key block [rows, 128]."""
+    rows = _c(rows, np.int32)
+    N, d = q["Qq"].shape
+    O = np.empty((rows.size, d), np.float64)
+    dump = np.zeros((rows.size, BLOCK), np.uint8) if dump_block >= 0 else None
+    mm = np.zeros((rows.size, N // BLOCK), np.float32) if want_m else None
+    mu = q["mu_scaled"] if (restore_mean and (q["flags"] & FLAG_VSMOOTH)) else None
+    lib().or_attention_emul(_p(q["Qq"]), _p(q["sQ"]), _p(q["Kq"]), _p(q["sK"]), _p(q["Vq"]), _p(q["sV"]),
+                            None if mu is None else _p(_c(mu, np.float32)), N, d, float(np.float32(beta)),
+                            int(mode), rows.size, _p(rows), _p(O), int(dump_block),
+                            None if dump is None else _p(dump), None if mm is None else _p(mm))
+    res = [O]
+    if dump is not None:
+        res.append(dump)
+    if mm is not None:
+        res.append(mm)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def attention_exact(Q_bits, K_bits, V_bits, rows) -> np.ndarray:
+    Q = _c(Q_bits, np.uint16)
+    K = _c(K_bits, np.uint16)
+    V = _c(V_bits, np.uint16)
+    rows = _c(rows, np.int32)
+    N, d = Q.shape
+    O = np.empty((rows.size, d), np.float64)
+    lib().or_attention_exact(_p(Q), _p(K), _p(V), N, d, rows.size, _p(rows), _p(O))
+    return O
+
+
+def pipeline(Q_bits, K_bits, V_bits, rows, *, vsmooth=True, ksmooth=True, expcast_on=True,
+             perm=None, beta=-0.35):
+    """Full emulated pipeline for one head with a given permutation (None = identity)."""
+    flags = (FLAG_KSMOOTH if ksmooth else 0) | (FLAG_VSMOOTH if vsmooth else 0)
+    q = quantize(Q_bits, K_bits, V_bits, perm if vsmooth else None, flags)
+    mode = MODE_EXPCAST if expcast_on else MODE_EXP_THEN_CAST
+    return attention_emul(q, rows, beta=beta, mode=mode), q
+
+
+# ---------------------------------------------------------------- exact helpers (self-checks)
+def exact_mean(x, p: int = 24) -> float:
+    a = _c(x, np.float64)
+    return float(lib().or_exact_mean(_p(a), a.size, p))
+
+
+def exact_sqdist_cmp(v, a, b) -> int:
+    v, a, b = _c(v, np.float32), _c(a, np.float32), _c(b, np.float32)
+    return int(lib().or_exact_sqdist_cmp(_p(v), _p(a), _p(b), v.size))

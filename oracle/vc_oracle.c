@@ -1,0 +1,637 @@
+/*
+ * vc_oracle.c -- slow, plain CPU oracle for the VC-Attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file; only the test-suite, the smoke check and the CPU-baseline leg of
+ * the benchmark do. It shares no code, header, table or constant generator with
+ * the HIP library.
+ *
+ * Source: "VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+ * Attention" (arXiv 2609.15810) as summarised on the study-notes page
+ * (dimensionstp.github.io, sections 2-1 .. 2-4), the paper page on
+ * paper.rainbus.top ("Method steps" (1)-(4), prerequisites on online softmax
+ * and on E4M3) and the news page on wire.sakhanda.co (V-Smooth and ExpCast
+ * sections). Where the pages leave a step open, the reading used is stated at
+ * the function that takes it.
+ *
+ * Arithmetic conventions:
+ *   fl32(x)  round-to-nearest-even to binary32 (C float arithmetic, no
+ *            contraction: build with -ffp-contract=off, never -ffast-math).
+ *   Exact sums of bf16/fp32 values are taken with an exact fixed-point
+ *   accumulator (xacc below) and rounded once.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+#include <float.h>
+#include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> binary32                                                         */
+/* ------------------------------------------------------------------------ */
+static inline float bf16_val(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact accumulator: sum of values m * 2^e with |m| < 2^53, exact.          */
+/* Limb i holds the digit of weight 2^(32*i + XA_EMIN); digits are kept in    */
+/* int64 so that up to 2^30 additions never overflow before normalisation.    */
+/* ------------------------------------------------------------------------ */
+#define XA_LIMBS 26
+#define XA_EMIN (-480)
+typedef struct { int64_t w[XA_LIMBS]; } xacc;
+
+static void xa_zero(xacc* a) { memset(a, 0, sizeof(*a)); }
+
+static void xa_add_me(xacc* a, int64_t m, int e) {
+  if (m == 0) return;
+  int neg = m < 0;
+  uint64_t mag = neg ? (uint64_t)(-m) : (uint64_t)m;
+  int p = e - XA_EMIN;
+  if (p < 0 || p / 32 + 3 >= XA_LIMBS) abort(); /* outside the supported range */
+  int i = p / 32, s = p % 32;
+  uint64_t lo = mag & 0xffffffffu, hi = mag >> 32; /* hi < 2^21 */
+  uint64_t v0 = lo << s;                           /* < 2^63 */
+  uint64_t v1 = hi << s;                           /* < 2^53 */
+  int64_t d0 = (int64_t)(v0 & 0xffffffffu), d1 = (int64_t)(v0 >> 32);
+  int64_t d2 = (int64_t)(v1 & 0xffffffffu), d3 = (int64_t)(v1 >> 32);
+  if (neg) { d0 = -d0; d1 = -d1; d2 = -d2; d3 = -d3; }
+  a->w[i] += d0;
+  a->w[i + 1] += d1 + d2;
+  a->w[i + 2] += d3;
+}
+
+/* decompose a finite double into m * 2^e with m odd (or 0), |m| < 2^53 */
+static void dbl_me(double x, int64_t* m, int* e) {
+  if (x == 0) { *m = 0; *e = 0; return; }
+  int ex;
+  double f = frexp(x, &ex); /* x = f * 2^ex, 0.5 <= |f| < 1 */
+  int64_t mm = (int64_t)ldexp(f, 53);
+  int ee = ex - 53;
+  while ((mm & 1) == 0) { mm >>= 1; ee++; }
+  *m = mm;
+  *e = ee;
+}
+
+static void xa_add_double(xacc* a, double x) {
+  int64_t m; int e;
+  dbl_me(x, &m, &e);
+  xa_add_me(a, m, e);
+}
+
+/* a += x*y exactly, for x, y binary32 values (24-bit significands) */
+static void xa_add_prod(xacc* a, double x, double y) {
+  int64_t mx, my; int ex, ey;
+  dbl_me(x, &mx, &ex);
+  dbl_me(y, &my, &ey);
+  if (mx == 0 || my == 0) return;
+  xa_add_me(a, mx * my, ex + ey); /* |mx*my| < 2^48 for binary32 inputs */
+}
+
+/* normalise into sign + magnitude digits (each in [0, 2^32)); returns sign -1/0/+1 */
+static int xa_normalize(const xacc* a, uint32_t* mag /* XA_LIMBS */) {
+  int64_t w[XA_LIMBS];
+  memcpy(w, a->w, sizeof(w));
+  for (int i = 0; i < XA_LIMBS - 1; i++) {
+    int64_t c = w[i] >> 32; /* arithmetic shift: floor division */
+    w[i] -= c * ((int64_t)1 << 32);
+    w[i + 1] += c;
+  }
+  int sign = 0;
+  if (w[XA_LIMBS - 1] < 0) sign = -1;
+  else {
+    for (int i = XA_LIMBS - 1; i >= 0; i--) if (w[i] != 0) { sign = 1; break; }
+  }
+  if (sign == 0) { memset(mag, 0, sizeof(uint32_t) * XA_LIMBS); return 0; }
+  if (sign < 0) {
+    for (int i = 0; i < XA_LIMBS; i++) w[i] = -w[i];
+    for (int i = 0; i < XA_LIMBS - 1; i++) {
+      int64_t c = w[i] >> 32;
+      w[i] -= c * ((int64_t)1 << 32);
+      w[i + 1] += c;
+    }
+  }
+  for (int i = 0; i < XA_LIMBS; i++) mag[i] = (uint32_t)w[i];
+  return sign;
+}
+
+/* sign of (a - b) */
+static int xa_cmp(const xacc* a, const xacc* b) {
+  xacc d;
+  for (int i = 0; i < XA_LIMBS; i++) d.w[i] = a->w[i] - b->w[i];
+  uint32_t mag[XA_LIMBS];
+  return xa_normalize(&d, mag);
+}
+
+/*
+ * Round (sum / n) to a binary float with `p` significand bits, minimum normal
+ * exponent -126 (binary32: p = 24; bfloat16: p = 8), ties to even. The result
+ * is returned as a double that is exactly representable in the target format.
+ */
+static double xa_round_div(const xacc* a, uint32_t n, int p) {
+  uint32_t mag[XA_LIMBS];
+  int sign = xa_normalize(a, mag);
+  if (sign == 0) return 0.0;
+  /* quotient of (mag << 64) / n in base 2^32, two extra low limbs */
+  enum { QL = XA_LIMBS + 2 };
+  uint32_t q[QL];
+  uint64_t rem = 0;
+  for (int i = QL - 1; i >= 0; i--) {
+    uint64_t digit = (i >= 2) ? mag[i - 2] : 0;
+    uint64_t cur = (rem << 32) | digit;
+    q[i] = (uint32_t)(cur / n);
+    rem = cur % n;
+  }
+  int sticky = rem != 0;
+  /* bit position t of the leading one of q; q bit 0 has weight 2^(XA_EMIN-64) */
+  int t = -1;
+  for (int i = QL - 1; i >= 0 && t < 0; i--)
+    if (q[i]) { int b = 31; while (!((q[i] >> b) & 1)) b--; t = 32 * i + b; }
+  int E = t + XA_EMIN - 64;              /* value in [2^E, 2^(E+1)) */
+  int ulp_e = (E > -126 ? E : -126) - (p - 1);
+  int pu = ulp_e - (XA_EMIN - 64);       /* bit index of the ulp in q (>= 1 always) */
+  /* kept = q >> pu (at most p+1 bits), guard = bit pu-1, sticky = lower bits | rem */
+  uint64_t kept = 0;
+  for (int b = t; b >= pu; b--) kept = (kept << 1) | ((q[b / 32] >> (b % 32)) & 1u);
+  int guard = (q[(pu - 1) / 32] >> ((pu - 1) % 32)) & 1u;
+  for (int b = pu - 2; b >= 0 && !sticky; b--) if ((q[b / 32] >> (b % 32)) & 1u) sticky = 1;
+  if (guard && (sticky || (kept & 1))) kept += 1;
+  double v = ldexp((double)kept, ulp_e);
+  return sign < 0 ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP E4M3 (bias 7, no infinities, 0x7F/0xFF NaN, max 448).                */
+/* The paper page's prerequisite on E4M3 fixes 1 sign, 4 exponent (bias 7)  */
+/* and 3 mantissa bits.                                                      */
+/* ------------------------------------------------------------------------ */
+double or_e4m3_decode(uint8_t b) {
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);           /* subnormal: m * 2^-9 */
+  else v = ldexp(1.0 + m / 8.0, e - 7);           /* normal: (1+m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+static double g_e4m3_pos[127]; /* value of codes 0..126, increasing */
+__attribute__((constructor)) static void e4m3_table_init(void) {
+  for (int c = 0; c < 127; c++) g_e4m3_pos[c] = or_e4m3_decode((uint8_t)c);
+}
+
+/* Round-to-nearest-even onto the E4M3 grid, saturating at 448; the sign bit is
+ * kept (a negative value that rounds to zero gives 0x80). */
+uint8_t or_e4m3_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t s = signbit(x) ? 0x80 : 0;
+  double a = fabs((double)x);
+  if (a >= 448.0) return s | 126;
+  /* largest code with value <= a (binary search on the increasing table) */
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) / 2;
+    if (g_e4m3_pos[mid] <= a) lo = mid; else hi = mid - 1;
+  }
+  int c = lo;
+  if (g_e4m3_pos[c] != a) {
+    double dlo = a - g_e4m3_pos[c], dhi = g_e4m3_pos[c + 1] - a;
+    if (dhi < dlo || (dhi == dlo && ((c + 1) & 1) == 0)) c = c + 1;
+  }
+  return s | (uint8_t)c;
+}
+
+void or_e4m3_encode_array(const float* x, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_e4m3_encode(x[i]);
+}
+void or_e4m3_decode_array(const uint8_t* b, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_e4m3_decode(b[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* ExpCast-FP8 (paper page, method step (4); news page, ExpCast section).    */
+/* For a log2-domain score u = (s - m') log2 e <= 0 the byte is             */
+/* clip(Round(8(u+8) + 56 + beta), 0, 120), read as E4M3. With the score    */
+/* kept as a raw accumulator acc and u = sigma*acc - m', this is the single  */
+/* binary32 FMA  t = fma(acc, 8*sigma, fl32(C0 - 8 m')),  C0 = fl32(120+beta) */
+/* followed by round-half-even and the clamp (clamping integer bounds after  */
+/* rounding equals rounding after clamping). NaN t gives code 0.             */
+/* ------------------------------------------------------------------------ */
+uint8_t or_expcast(float acc, float scale8, float bias) {
+  float t = fmaf(acc, scale8, bias);
+  if (isnan(t)) return 0;
+  float r = nearbyintf(t); /* default rounding mode: nearest, ties to even */
+  if (r < 0.0f) r = 0.0f;
+  if (r > 120.0f) r = 120.0f;
+  return (uint8_t)r;
+}
+void or_expcast_array(const float* acc, const float* scale8, const float* bias, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_expcast(acc[i], scale8[i], bias[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* k-means on value tokens, one (batch, head) at a time.                    */
+/* Paper page, method step (1): online k-means labels z, pi = argsort(z),   */
+/* warm-started centroids. Reading: Lloyd iterations (assign, then update)  */
+/* on squared Euclidean distance to bf16-rounded centroids; ties go to the  */
+/* lowest cluster index; an empty cluster keeps its centroid; centroid =    */
+/* fl32(exact mean); labels come from the last assignment; pi is the stable */
+/* argsort; cold start takes C_k = V[floor((2k+1)N/(2K))].                  */
+/* ------------------------------------------------------------------------ */
+
+static uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(r >> 16);
+}
+
+/* exact squared distance accumulator of two binary32 vectors */
+static void exact_sqdist(const float* v, const float* c, int d, xacc* out) {
+  xa_zero(out);
+  for (int j = 0; j < d; j++) {
+    double a = v[j], b = c[j];
+    xa_add_prod(out, a, a);
+    xa_add_prod(out, a, -2.0 * b); /* -2b is exact */
+    xa_add_prod(out, b, b);
+  }
+}
+
+/*
+ * z = argmin_k ||v - chat_k||^2, exactly. A binary64 pass ranks the clusters;
+ * any cluster within a relative 1e-12 of the binary64 minimum (which
+ * comfortably covers the binary64 rounding of a 128-term sum of non-negative
+ * terms) is re-ranked with the exact accumulator. Ties: lowest index.
+ */
+static int32_t assign_one(const float* v, const float* chat, int K, int d, double* dist /* scratch K */) {
+  double best = INFINITY;
+  for (int k = 0; k < K; k++) {
+    const float* c = chat + (int64_t)k * d;
+    double s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    int j = 0;
+    for (; j + 4 <= d; j += 4) {
+      double a0 = (double)v[j] - c[j], a1 = (double)v[j + 1] - c[j + 1];
+      double a2 = (double)v[j + 2] - c[j + 2], a3 = (double)v[j + 3] - c[j + 3];
+      s0 += a0 * a0; s1 += a1 * a1; s2 += a2 * a2; s3 += a3 * a3;
+    }
+    for (; j < d; j++) { double a = (double)v[j] - c[j]; s0 += a * a; }
+    dist[k] = (s0 + s1) + (s2 + s3);
+    if (dist[k] < best) best = dist[k];
+  }
+  double thr = best + best * 1e-12;
+  int first = -1, ncand = 0;
+  for (int k = 0; k < K; k++) if (dist[k] <= thr) { if (first < 0) first = k; ncand++; }
+  if (ncand == 1) return first;
+  int bk = -1;
+  xacc bacc, cur;
+  for (int k = 0; k < K; k++) {
+    if (dist[k] > thr) continue;
+    exact_sqdist(v, chat + (int64_t)k * d, d, &cur);
+    if (bk < 0 || xa_cmp(&cur, &bacc) < 0) { bk = k; bacc = cur; }
+  }
+  return bk;
+}
+
+/* labels for all tokens against bf16-valued centroids chat (as floats) */
+void or_kmeans_assign(const uint16_t* V, int N, int d, const float* chat, int K, int32_t* labels) {
+#pragma omp parallel
+  {
+    double* dist = (double*)malloc(sizeof(double) * K);
+    float* v = (float*)malloc(sizeof(float) * d);
+#pragma omp for schedule(dynamic, 64)
+    for (int t = 0; t < N; t++) {
+      for (int j = 0; j < d; j++) v[j] = bf16_val(V[(int64_t)t * d + j]);
+      labels[t] = assign_one(v, chat, K, d, dist);
+    }
+    free(dist);
+    free(v);
+  }
+}
+
+/* stable argsort of labels in [0, K): counting sort, ties by ascending index */
+void or_stable_argsort(const int32_t* labels, int N, int K, int32_t* perm) {
+  int64_t* cnt = (int64_t*)calloc((size_t)K + 1, sizeof(int64_t));
+  for (int t = 0; t < N; t++) cnt[labels[t] + 1]++;
+  for (int k = 0; k < K; k++) cnt[k + 1] += cnt[k];
+  for (int t = 0; t < N; t++) perm[cnt[labels[t]]++] = t;
+  free(cnt);
+}
+
+/* C_k = fl32(exact mean of members); empty clusters unchanged */
+void or_kmeans_update(const uint16_t* V, int N, int d, const int32_t* labels, int K, float* C) {
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * N);
+  int64_t* start = (int64_t*)calloc((size_t)K + 1, sizeof(int64_t));
+  for (int t = 0; t < N; t++) start[labels[t] + 1]++;
+  for (int k = 0; k < K; k++) start[k + 1] += start[k];
+  or_stable_argsort(labels, N, K, perm);
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int k = 0; k < K; k++) {
+    int64_t a = start[k], b = start[k + 1];
+    if (b == a) continue;
+    for (int j = 0; j < d; j++) {
+      xacc s;
+      xa_zero(&s);
+      for (int64_t i = a; i < b; i++) xa_add_double(&s, bf16_val(V[(int64_t)perm[i] * d + j]));
+      C[(int64_t)k * d + j] = (float)xa_round_div(&s, (uint32_t)(b - a), 24);
+    }
+  }
+  free(perm);
+  free(start);
+}
+
+void or_kmeans(const uint16_t* V, int N, int d, int K, int iters, int cold,
+               float* C /* [K,d] in (warm) / out */, int32_t* labels, int32_t* perm) {
+  if (cold) {
+    for (int k = 0; k < K; k++) {
+      int64_t t = ((int64_t)(2 * k + 1) * N) / (2 * (int64_t)K);
+      for (int j = 0; j < d; j++) C[(int64_t)k * d + j] = bf16_val(V[t * d + j]);
+    }
+  }
+  float* chat = (float*)malloc(sizeof(float) * (size_t)K * d);
+  for (int it = 0; it < iters; it++) {
+    for (int64_t i = 0; i < (int64_t)K * d; i++) chat[i] = bf16_val(f32_to_bf16(C[i]));
+    or_kmeans_assign(V, N, d, chat, K, labels);
+    or_kmeans_update(V, N, d, labels, K, C);
+  }
+  or_stable_argsort(labels, N, K, perm);
+  free(chat);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantizer (paper page, method step (2); study notes 2-2).                 */
+/* Per (batch, head), N a multiple of 128, blocks of 128 rows:              */
+/*  K smoothing: kbar_c = fl32(exact sum_t K_tc / N); Kt = fl32(K - kbar).   */
+/*  Permute: K' = Kt[pi], V' = V[pi].                                        */
+/*  V-Smooth: mu_jc = bf16(exact block mean of V'); R = fl32(V' - mu).       */
+/*  V residual codes: a_c = max_t |R_tc|; s_c = fl32(a_c/448),              */
+/*  inv_c = fl32(448/a_c) (a_c = 0: s = 1, inv = 0); Rq = e4m3(fl32(R inv)); */
+/*  mu_scaled = fl32(mu / s).                                                */
+/*  Q, K' per 128-row block: a = block amax, s = fl32(a/448),               */
+/*  inv = fl32(448/a); codes e4m3(fl32(x inv)); sQ' = fl32(sQ * c_L) with    */
+/*  c_L = fl32(log2(e)/sqrt(d)) supplied by the caller.                      */
+/* Layout of every array here: row-major [N, d] (Vq too).                   */
+/* flags: 1 = K smoothing, 2 = V-Smooth (block means)                       */
+/* ------------------------------------------------------------------------ */
+static void quant_block(const float* x, int rows, int d, uint8_t* codes, float* scale) {
+  float a = 0.0f;
+  for (int64_t i = 0; i < (int64_t)rows * d; i++) { float m = fabsf(x[i]); if (m > a) a = m; }
+  float inv;
+  if (a > 0.0f) { *scale = a / 448.0f; inv = 448.0f / a; }
+  else { *scale = 1.0f; inv = 0.0f; }
+  for (int64_t i = 0; i < (int64_t)rows * d; i++) codes[i] = or_e4m3_encode(x[i] * inv);
+}
+
+int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                int N, int d, int flags, float cL,
+                uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                uint16_t* mu, float* mu_scaled, float* kbar_out) {
+  if (N % 128) return 2;
+  int nb = N / 128;
+  float* kbar = (float*)malloc(sizeof(float) * d);
+  for (int j = 0; j < d; j++) {
+    if (flags & 1) {
+      xacc s;
+      xa_zero(&s);
+      for (int t = 0; t < N; t++) xa_add_double(&s, bf16_val(K[(int64_t)t * d + j]));
+      kbar[j] = (float)xa_round_div(&s, (uint32_t)N, 24);
+    } else kbar[j] = 0.0f;
+    if (kbar_out) kbar_out[j] = kbar[j];
+  }
+  /* Q blocks (original order) */
+#pragma omp parallel for schedule(static)
+  for (int b = 0; b < nb; b++) {
+    float* x = (float*)malloc(sizeof(float) * 128 * d);
+    for (int i = 0; i < 128 * d; i++) x[i] = bf16_val(Q[(int64_t)b * 128 * d + i]);
+    float s;
+    quant_block(x, 128, d, Qq + (int64_t)b * 128 * d, &s);
+    sQ[b] = s * cL;
+    free(x);
+  }
+  /* K' blocks */
+#pragma omp parallel for schedule(static)
+  for (int b = 0; b < nb; b++) {
+    float* x = (float*)malloc(sizeof(float) * 128 * d);
+    for (int i = 0; i < 128; i++) {
+      int64_t src = perm ? perm[b * 128 + i] : (int64_t)(b * 128 + i);
+      for (int j = 0; j < d; j++) x[i * d + j] = bf16_val(K[src * d + j]) - kbar[j];
+    }
+    quant_block(x, 128, d, Kq + (int64_t)b * 128 * d, &sK[b]);
+    free(x);
+  }
+  /* V': block means and residual */
+  float* R = (float*)malloc(sizeof(float) * (size_t)N * d);
+#pragma omp parallel for schedule(static)
+  for (int b = 0; b < nb; b++) {
+    for (int j = 0; j < d; j++) {
+      float m = 0.0f;
+      if (flags & 2) {
+        xacc s;
+        xa_zero(&s);
+        for (int i = 0; i < 128; i++) {
+          int64_t src = perm ? perm[b * 128 + i] : (int64_t)(b * 128 + i);
+          xa_add_double(&s, bf16_val(V[src * d + j]));
+        }
+        uint16_t h = f32_to_bf16((float)xa_round_div(&s, 128u, 8)); /* exact in bf16 already */
+        mu[(int64_t)b * d + j] = h;
+        m = bf16_val(h);
+      } else if (mu) mu[(int64_t)b * d + j] = 0;
+      for (int i = 0; i < 128; i++) {
+        int64_t src = perm ? perm[b * 128 + i] : (int64_t)(b * 128 + i);
+        R[((int64_t)b * 128 + i) * d + j] = bf16_val(V[src * d + j]) - m;
+      }
+    }
+  }
+  for (int j = 0; j < d; j++) {
+    float a = 0.0f;
+    for (int t = 0; t < N; t++) { float m = fabsf(R[(int64_t)t * d + j]); if (m > a) a = m; }
+    float s, inv;
+    if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; }
+    else { s = 1.0f; inv = 0.0f; }
+    sV[j] = s;
+    for (int t = 0; t < N; t++) Vq[(int64_t)t * d + j] = or_e4m3_encode(R[(int64_t)t * d + j] * inv);
+    if (mu_scaled)
+      for (int b = 0; b < nb; b++) mu_scaled[(int64_t)b * d + j] = (flags & 2) ? bf16_val(mu[(int64_t)b * d + j]) / s : 0.0f;
+  }
+  free(R);
+  free(kbar);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention emulation on selected query rows (paper page, method steps (3) */
+/* and (4); study notes 2-3; online softmax prerequisite).                  */
+/* For every 128-key block j in ascending order:                            */
+/*   acc_it = fl32(exact sum_c dec(Qq_ic) dec(Kq_tc))                        */
+/*   sigma  = fl32(sQ'_I * sK_j)                                             */
+/*   m'     = max(m, fl32(sigma * max_t acc_it));  alpha = 2^(m - m')        */
+/* mode 0 (ExpCast): c = expcast(acc, 8 sigma, fl32(C0 - 8 m')), p = dec(c)  */
+/* mode 1 (exp-then-cast): P = fl32(2^(fl32(fl32(sigma acc) - m'))),        */
+/*        c = e4m3(fl32(256 P)), p = dec(c), row-sum term 256 P              */
+/* mode 2 (no probability quantisation): p = 256 * 2^(fl32(sigma acc) - m')  */
+/*        in binary64, row-sum term p                                       */
+/*   r = sum_t (row-sum term);  l = alpha l + r                             */
+/*   A = alpha A + sum_t p_t dec(Rq_t) + r mu_scaled_j                       */
+/* O = sV * A / l (binary64). A and l are binary64.                          */
+/* Optionally the codes of block `dump_block` for each row are written out.  */
+/* ------------------------------------------------------------------------ */
+static inline int32_t e4m3_units(uint8_t b) { /* value * 2^9, exact integer */
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  int32_t v = e == 0 ? m : ((8 + m) << (e - 1));
+  return s ? -v : v;
+}
+
+void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                       const uint8_t* Vq, const float* sV, const float* mu_scaled,
+                       int N, int d, float beta, int mode,
+                       int nrows, const int32_t* rows, double* O /* [nrows, d] */,
+                       int dump_block, uint8_t* dump_codes /* [nrows, 128] or NULL */,
+                       float* dump_m /* [nrows, N/128] running max after each block, or NULL */) {
+  int nb = N / 128;
+  const float C0 = 120.0f + beta;
+  /* decoded operand tables as exact integers */
+  int32_t* Ku = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * d);
+  int32_t* Vu = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * d);
+  for (int64_t i = 0; i < (int64_t)N * d; i++) { Ku[i] = e4m3_units(Kq[i]); Vu[i] = e4m3_units(Vq[i]); }
+#pragma omp parallel
+  {
+    int32_t* qu = (int32_t*)malloc(sizeof(int32_t) * d);
+    float* acc = (float*)malloc(sizeof(float) * 128);
+    double* A = (double*)malloc(sizeof(double) * d);
+    int32_t pu[128];
+    double pt[128];
+#pragma omp for schedule(dynamic, 1)
+    for (int ri = 0; ri < nrows; ri++) {
+      int i = rows[ri];
+      int I = i / 128;
+      for (int c = 0; c < d; c++) qu[c] = e4m3_units(Qq[(int64_t)i * d + c]);
+      double m = -INFINITY, l = 0.0;
+      for (int c = 0; c < d; c++) A[c] = 0.0;
+      for (int j = 0; j < nb; j++) {
+        float sigma = sQ[I] * sK[j];
+        float mx = -INFINITY;
+        for (int t = 0; t < 128; t++) {
+          const int32_t* kr = Ku + (int64_t)(j * 128 + t) * d;
+          int64_t s = 0;
+          for (int c = 0; c < d; c++) s += (int64_t)qu[c] * kr[c];
+          acc[t] = (float)ldexpl((long double)s, -18); /* exact integer in long double, one rounding */
+          if (acc[t] > mx) mx = acc[t];
+        }
+        float mnew = sigma * mx;
+        float mp = (float)m > mnew ? (float)m : mnew; /* m is always a binary32 value */
+        double alpha = (m == -INFINITY) ? 0.0 : exp2((double)((float)m) - (double)mp);
+        float bias = C0 - 8.0f * mp;
+        float s8 = 8.0f * sigma;
+        double r = 0.0;
+        for (int t = 0; t < 128; t++) {
+          if (mode == 0) {
+            uint8_t code = or_expcast(acc[t], s8, bias);
+            pu[t] = e4m3_units(code);
+            pt[t] = ldexp((double)pu[t], -9);
+            if (dump_codes && j == dump_block) dump_codes[(int64_t)ri * 128 + t] = code;
+          } else if (mode == 1) {
+            float u = sigma * acc[t] - mp;
+            float P = (float)exp2((double)u);
+            uint8_t code = or_e4m3_encode(256.0f * P);
+            pu[t] = e4m3_units(code);
+            pt[t] = 256.0 * (double)P;
+            if (dump_codes && j == dump_block) dump_codes[(int64_t)ri * 128 + t] = code;
+          } else {
+            pu[t] = 0;
+            pt[t] = 256.0 * exp2((double)(sigma * acc[t]) - (double)mp);
+          }
+          r += pt[t];
+        }
+        l = alpha * l + r;
+        for (int c = 0; c < d; c++) {
+          double pv;
+          if (mode == 2) {
+            pv = 0.0;
+            for (int t = 0; t < 128; t++) pv += pt[t] * ldexp((double)Vu[(int64_t)(j * 128 + t) * d + c], -9);
+          } else {
+            int64_t b = 0; /* exact: codes and residual bytes are multiples of 2^-9 */
+            for (int t = 0; t < 128; t++) b += (int64_t)pu[t] * Vu[(int64_t)(j * 128 + t) * d + c];
+            pv = ldexp((double)b, -18);
+          }
+          double mu = mu_scaled ? (double)mu_scaled[(int64_t)j * d + c] : 0.0;
+          A[c] = alpha * A[c] + pv + r * mu;
+        }
+        m = mp;
+        if (dump_m) dump_m[(int64_t)ri * nb + j] = mp;
+      }
+      for (int c = 0; c < d; c++) O[(int64_t)ri * d + c] = (double)sV[c] * A[c] / l;
+    }
+    free(qu); free(acc); free(A);
+  }
+  free(Ku);
+  free(Vu);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact attention in binary64 (study notes 1-1: O = softmax(QK^T/sqrt d) V) */
+/* on selected rows, from bf16 inputs. Non-causal: every query sees all keys. */
+/* ------------------------------------------------------------------------ */
+void or_attention_exact(const uint16_t* Q, const uint16_t* K, const uint16_t* V, int N, int d,
+                        int nrows, const int32_t* rows, double* O) {
+  double* Kd = (double*)malloc(sizeof(double) * (size_t)N * d);
+  double* Vd = (double*)malloc(sizeof(double) * (size_t)N * d);
+  for (int64_t i = 0; i < (int64_t)N * d; i++) { Kd[i] = bf16_val(K[i]); Vd[i] = bf16_val(V[i]); }
+  double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * N);
+    double* q = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+    for (int ri = 0; ri < nrows; ri++) {
+      int i = rows[ri];
+      for (int c = 0; c < d; c++) q[c] = bf16_val(Q[(int64_t)i * d + c]);
+      double mx = -INFINITY;
+      for (int t = 0; t < N; t++) {
+        double a = 0;
+        const double* kr = Kd + (int64_t)t * d;
+        for (int c = 0; c < d; c++) a += q[c] * kr[c];
+        s[t] = a * scale;
+        if (s[t] > mx) mx = s[t];
+      }
+      double den = 0;
+      for (int t = 0; t < N; t++) { s[t] = exp(s[t] - mx); den += s[t]; }
+      for (int c = 0; c < d; c++) O[(int64_t)ri * d + c] = 0.0;
+      for (int t = 0; t < N; t++) {
+        const double* vr = Vd + (int64_t)t * d;
+        double w = s[t] / den;
+        for (int c = 0; c < d; c++) O[(int64_t)ri * d + c] += w * vr[c];
+      }
+    }
+    free(s); free(q);
+  }
+  free(Kd);
+  free(Vd);
+}
+
+/* exposed for the self-checks of the exact arithmetic */
+double or_exact_mean(const double* x, int64_t n, int p) {
+  xacc s;
+  xa_zero(&s);
+  for (int64_t i = 0; i < n; i++) xa_add_double(&s, x[i]);
+  return xa_round_div(&s, (uint32_t)n, p);
+}
+int or_exact_sqdist_cmp(const float* v, const float* a, const float* b, int d) {
+  xacc da, db;
+  exact_sqdist(v, a, d, &da);
+  exact_sqdist(v, b, d, &db);
+  return xa_cmp(&da, &db);
+}
+int or_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,107 @@
+"""Pins for the oracle's k-means (paper page, method step (1)): exact argmin with
+lowest-index ties, exact rational centroid means, stable argsort, planted-cluster sanity."""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import synth
+from tests._exact import round_to_f32
+
+
+def _bits_to_fr(h):
+    return [Fraction(float(x)) for x in synth.bf16_to_f32(h)]
+
+
+def test_assign_brute_force_with_ties():
+    rng = np.random.default_rng(3)
+    N, d, K = 300, 8, 7
+    # small integers and halves: many exact ties between clusters
+    V = synth.bf16_bits((rng.integers(-4, 5, (N, d)) * 0.5).astype(np.float32))
+    C = (rng.integers(-4, 5, (K, d)) * 0.5).astype(np.float32)
+    C[3] = C[1]            # duplicate centroid: the lower index must win
+    chat = synth.bf16_to_f32(synth.bf16_bits(C))
+    got = oracle.kmeans_assign(V, chat)
+    Vf = [_bits_to_fr(V[t]) for t in range(N)]
+    Cf = [[Fraction(float(x)) for x in chat[k]] for k in range(K)]
+    for t in range(N):
+        dist = [sum((a - b) ** 2 for a, b in zip(Vf[t], Cf[k])) for k in range(K)]
+        want = min(range(K), key=lambda k: (dist[k], k))
+        assert got[t] == want, t
+    assert not np.any(got == 3)
+
+
+def test_assign_resolves_near_ties_exactly():
+    # two centroids whose binary64 distances agree to ~1e-16 but differ exactly
+    d = 128
+    rng = np.random.default_rng(9)
+    v = synth.bf16_to_f32(synth.bf16_bits(rng.standard_normal(d).astype(np.float32) * 100))
+    a = v.copy()
+    b = v.copy()
+    a[0] = (synth.bf16_to_f32(synth.bf16_bits(np.float32(v[0].item() + 2.0 ** -10 * abs(v[0].item())))))
+    b[1] = (synth.bf16_to_f32(synth.bf16_bits(np.float32(v[1].item() + 2.0 ** -10 * abs(v[1].item())))))
+    da = sum((Fraction(float(x)) - Fraction(float(y))) ** 2 for x, y in zip(v, a))
+    db = sum((Fraction(float(x)) - Fraction(float(y))) ** 2 for x, y in zip(v, b))
+    sign = (da > db) - (da < db)
+    assert oracle.exact_sqdist_cmp(v, a, b) == sign
+    lab = oracle.kmeans_assign(synth.bf16_bits(v)[None, :], np.stack([a, b]))
+    assert lab[0] == (0 if da <= db else 1)
+
+
+def test_stable_argsort_matches_numpy():
+    rng = np.random.default_rng(4)
+    z = rng.integers(0, 37, 5000).astype(np.int32)
+    assert np.array_equal(oracle.stable_argsort(z, 37), np.argsort(z, kind="stable"))
+
+
+def test_update_exact_rational_means():
+    rng = np.random.default_rng(6)
+    N, d, K = 400, 6, 9
+    V = synth.bf16_bits((rng.standard_normal((N, d)) * np.exp2(rng.integers(-20, 20, (N, d)))).astype(np.float32))
+    z = rng.integers(0, K - 1, N).astype(np.int32)       # cluster K-1 stays empty
+    C0 = rng.standard_normal((K, d)).astype(np.float32)
+    C = oracle.kmeans_update(V, z, C0)
+    Vf = synth.bf16_to_f32(V)
+    for k in range(K):
+        idx = np.nonzero(z == k)[0]
+        for j in range(d):
+            if idx.size == 0:
+                assert C[k, j] == C0[k, j]
+                continue
+            s = sum(Fraction(float(Vf[t, j])) for t in idx)
+            assert C[k, j] == round_to_f32(s / idx.size), (k, j)
+
+
+def test_exact_mean_rounding_bf16_and_f32():
+    x = np.array([1.0, 2.0 ** -30, 2.0 ** -30], np.float64)
+    # (1 + 2^-29)/3 rounded once
+    assert oracle.exact_mean(x, 24) == float(round_to_f32((Fraction(1) + Fraction(2) ** -29) / 3))
+    # ties to even at bf16 precision: mean exactly halfway between two bf16 neighbours of 1
+    y = np.array([1.0, 1.0 + 2.0 ** -7], np.float64)      # mean = 1 + 2^-8, halfway -> 1.0 (even)
+    assert oracle.exact_mean(y, 8) == 1.0
+    y2 = np.array([1.0 + 2.0 ** -7, 1.0 + 2.0 ** -6], np.float64)  # mean = 1 + 3*2^-8 -> 1 + 2^-6 (even)
+    assert oracle.exact_mean(y2, 8) == 1.0 + 2.0 ** -6
+
+
+def test_planted_clusters_recovered_on_tiny_workload():
+    h = synth.gen_head("tiny", 0, 0, 0, 1024, 128)
+    V, z_true, centres = h["V"], h["z_true"], h["centres"]
+    labels, perm, C = oracle.kmeans(V, 4, 3, cold=False, C=centres)
+    inlier = np.ones(V.shape[0], bool)
+    inlier[h["outliers"]] = False
+    # centres ~5.6 apart with unit noise: the Bayes error is ~0.8 %, so >= 98.5 % of the
+    # planted labels and >= 99.5 % agreement with the nearest-true-centre rule
+    nearest = oracle.kmeans_assign(V, synth.bf16_to_f32(synth.bf16_bits(centres)))
+    assert np.mean(labels[inlier] == z_true[inlier]) >= 0.985
+    assert np.mean(labels[inlier] == nearest[inlier]) >= 0.995
+    assert np.array_equal(perm, np.argsort(labels, kind="stable"))
+
+
+def test_cold_start_picks_strided_tokens():
+    rng = np.random.default_rng(8)
+    N, d, K = 256, 4, 5
+    V = synth.bf16_bits(rng.standard_normal((N, d)).astype(np.float32))
+    # one assignment against the cold-start centroids equals assigning to the strided tokens
+    labels, perm, C = oracle.kmeans(V, K, 1, cold=True)
+    init = synth.bf16_to_f32(V[[(2 * k + 1) * N // (2 * K) for k in range(K)]])
+    assert np.array_equal(labels, oracle.kmeans_assign(V, init))
