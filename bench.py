@@ -1,0 +1,187 @@
+"""Benchmark of the VC-Attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of the Wan2.2-shaped synthetic
+workload (B=1, H=40, N=70,400, d=128): warm-started k-means (550 clusters, 2
+iterations) -> fused quantiser -> VC-Attention (V-Smooth + ExpCast-FP8). Inputs are
+resident in HBM before the timed region. `value` is attention-equivalent TFLOPS of the
+whole step, 4*B*H*N^2*d / t_step; the per-stage times and the attention kernel's own
+TFLOPS (from HIP events on the launch stream) are reported beside it.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 VC-attention TFLOPS & % FP8 MFMA peak at N=70,400,H=40,d=128"
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (published)
+HBM_PEAK_GBS = 8000.0
+BETA = -0.35
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_inputs(kind, B, H, N, d, seed):
+    import numpy as np
+    import torch
+    import synth
+    t0 = time.time()
+    w = synth.gen(kind, seed=seed, B=B, H=H, N=N, d=d)
+    log("[bench] generated %s inputs B=%d H=%d N=%d d=%d in %.1fs" % (kind, B, H, N, d, time.time() - t0))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    out = {k: dev(v) for k, v in w.items() if k != "meta"}
+    return out, w
+
+
+def cpu_baseline(host, K_clusters, sample_rows, threads):
+    """Time the oracle on a bounded sample of the same workload (head 0)."""
+    import numpy as np
+    import oracle
+    Q, K, V, Vp = (host[k][0, 0] for k in ("Q", "K", "V", "V_prev"))
+    N, d = Q.shape
+    t0 = time.time()
+    _, _, Cw = oracle.kmeans(Vp, K_clusters, 1, cold=True)          # warm-start state (not timed)
+    t1 = time.time()
+    labels, perm, _ = oracle.kmeans(V, K_clusters, 2, cold=False, C=Cw)
+    t2 = time.time()
+    q = oracle.quantize(Q, K, V, perm, oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
+    t3 = time.time()
+    rows = np.linspace(0, N - 1, sample_rows).astype(np.int32)
+    oracle.attention_emul(q, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+    t4 = time.time()
+    t_head = (t2 - t1) + (t3 - t2) + (t4 - t3) * N / sample_rows
+    flops_head = 4.0 * N * N * d
+    return dict(value=flops_head / t_head / 1e12, unit="TFLOPS", cores=threads, kind="oracle",
+                sample="head 0 of the workload: k-means (2 warm iterations, 550 clusters) and quantiser in full, "
+                       "attention emulation on %d of %d query rows extrapolated x%.0f; per-head time %.1f s "
+                       "(kmeans %.1f s, quantise %.1f s, attention %.1f s measured)"
+                       % (sample_rows, N, N / sample_rows, t_head, t2 - t1, t3 - t2, t4 - t3),
+                seconds_measured=round(t4 - t1, 2), warm_start_seconds=round(t1 - t0, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the path shards by (batch, head) with no exchange, "
+              "but multi-GPU runs are not part of it (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_attention_video_online_amd as vc
+
+    torch.cuda.set_device(0)
+    if args.workload == "wan":
+        B, H, N, d, Kc, seed, kind = 1, 40, 70400, 128, 550, 2, "wan"
+    elif args.workload.startswith("sweep"):
+        import synth
+        i = int(args.workload[5:])
+        s = synth.SWEEP[i]
+        B, H, N, d, seed, kind = s["B"], s["H"], s["N"], s["d"], s["seed"], "sweep"
+        Kc = N // 128
+    else:
+        raise SystemExit("unknown workload %s" % args.workload)
+    dev, host = make_inputs(kind, B, H, N, d, seed)
+    Qd, Kd, Vd, Vpd = dev["Q"], dev["K"], dev["V"], dev["V_prev"]
+
+    # warm-start state: cold 4-iteration k-means on the previous step's values (untimed)
+    Cw = torch.zeros((B, H, Kc, d), dtype=torch.float32, device="cuda")
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    ws_c = vc.workspace(vc.vc_cluster_workspace_bytes(B, H, N, d, Kc))
+    vc.vc_cluster(Vpd, Kc, 4, True, Cw, lab, perm, ws=ws_c)
+    C = torch.empty_like(Cw)
+    q = vc.quantize_outputs(B, H, N, d)
+    ws_q = vc.workspace(vc.vc_quantize_workspace_bytes(B, H, N, d))
+    O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    flags_q = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k in ("cluster", "quantize", "attention")}
+
+    def step(record):
+        if args.attention_only:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+            if record:
+                e1.record(); ev["attention"].append((e0, e1))
+            return
+        es = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        C.copy_(Cw)
+        if record: es[0].record()
+        vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
+        if record: es[1].record()
+        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q)
+        if record: es[2].record()
+        vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+        if record:
+            es[3].record()
+            ev["cluster"].append((es[0], es[1])); ev["quantize"].append((es[1], es[2])); ev["attention"].append((es[2], es[3]))
+
+    if args.attention_only:
+        C.copy_(Cw)
+        vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
+        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q)
+    for i in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("[bench] warmup done (%d steps)" % args.warmup)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    avg = {k: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None) for k, v in ev.items()}
+    log("[bench] timed %d steps: %.3f ms/step; stage ms %s" % (args.steps, ms_step, avg))
+
+    flops = 4.0 * B * H * N * N * d
+    t_att = avg["attention"] / 1e3
+    att_tflops = flops / t_att / 1e12
+    value = flops / (ms_step / 1e3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": ("wan2.2-shaped VC-Attention step: B=%d H=%d N=%d d=%d, k-means %d clusters x 2 warm "
+                                "iterations, block 128, beta=-0.35, V-Smooth + ExpCast-FP8" % (B, H, N, d, Kc)),
+                   "global_batch": B, "seq_len": N, "heads": H, "head_dim": d, "clusters": Kc,
+                   "parallelism": "single GPU"},
+        "stage_ms": {k: (round(v, 3) if v is not None else None) for k, v in avg.items()},
+        "attention_tflops": round(att_tflops, 2),
+        "attention_pct_fp8_peak": round(100.0 * att_tflops / FP8_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_fwd<128,ExpCast,restore>", "algorithmic_flops_per_launch": flops},
+    }
+    if args.attention_only:
+        res["config"]["workload"] += " (attention kernel only)"
+    if not args.no_cpu_baseline and not args.attention_only:
+        import oracle
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(host, Kc, args.cpu_rows, oracle.num_threads())
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,198 @@
+"""VC-Attention hot path on AMD Instinct MI355X (gfx950): thin Python binding.
+
+Every computation runs in the HIP kernels of ``libvc.so`` behind the C ABI declared in
+``include/vc.h``; this module only checks tensor metadata, passes raw device pointers
+and the current HIP stream, and turns status codes into exceptions. PyTorch is used
+for device memory and streams only. There is no CPU fallback: if the library is not
+built, importing the functions raises.
+
+Entry points (same names as the C ABI):
+  vc_cluster, vc_quantize, vc_attention, vc_attention_dump, vc_debug_expcast,
+  vc_cluster_workspace_bytes, vc_quantize_workspace_bytes, vc_status_string.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvc.so")
+
+VC_F_KSMOOTH = 1
+VC_F_VSMOOTH = 2
+VC_F_EXPCAST = 4
+BLOCK = 128
+
+_STATUS = {0: "VC_OK", 1: "VC_E_NULLPTR", 2: "VC_E_SHAPE", 3: "VC_E_PARAM", 4: "VC_E_WORKSPACE",
+           5: "VC_E_UNSUPPORTED", 6: "VC_E_HIP", 7: "VC_E_ALIAS"}
+
+
+class VCError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvc.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libvc.so not found at %s: run `python bit_attention_video_online_amd/build.py` "
+                              "(or __graft_entry__.build()) first" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, U, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+        L.vc_status_string.restype = ctypes.c_char_p
+        L.vc_status_string.argtypes = [I]
+        L.vc_abi_version.restype = I
+        L.vc_cluster_workspace_bytes.restype = S
+        L.vc_cluster_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.vc_cluster.restype = I
+        L.vc_cluster.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, S, P]
+        L.vc_quantize_workspace_bytes.restype = S
+        L.vc_quantize_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.vc_quantize.restype = I
+        L.vc_quantize.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, S, P]
+        L.vc_attention.restype = I
+        L.vc_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, U, P, P]
+        L.vc_attention_dump.restype = I
+        L.vc_attention_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, U, P, I, P, P]
+        L.vc_debug_expcast.restype = I
+        L.vc_debug_expcast.argtypes = [P, P, P, P, S, P]
+        _lib = L
+    return _lib
+
+
+def vc_status_string(status: int) -> str:
+    return lib().vc_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise VCError(status, vc_status_string(status))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must live on the GPU (got %s)" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else ctypes.c_void_p(t.data_ptr() or 16)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dims(x: torch.Tensor):
+    if x.dim() != 4:
+        raise ValueError("expected [B,H,N,d]")
+    return tuple(int(v) for v in x.shape)
+
+
+def _need(t, dtype, shape, name):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must be %s%s, got %s%s" % (name, dtype, tuple(shape), t.dtype, tuple(t.shape)))
+
+
+# ------------------------------------------------------------------ workspaces
+def vc_cluster_workspace_bytes(B, H, N, d, K) -> int:
+    return int(lib().vc_cluster_workspace_bytes(B, H, N, d, K))
+
+
+def vc_quantize_workspace_bytes(B, H, N, d, block=BLOCK) -> int:
+    return int(lib().vc_quantize_workspace_bytes(B, H, N, d, block))
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+def vc_cluster(V, K, iters, cold_start, centroids, labels, perm, ws=None, stream=None):
+    """k-means on value tokens; centroids [B,H,K,d] f32 in/out, labels/perm [B,H,N] i32 out."""
+    B, H, N, d = _dims(V)
+    _need(V, torch.bfloat16, (B, H, N, d), "V")
+    _need(centroids, torch.float32, (B, H, K, d), "centroids")
+    _need(labels, torch.int32, (B, H, N), "labels")
+    _need(perm, torch.int32, (B, H, N), "perm")
+    need = vc_cluster_workspace_bytes(B, H, N, d, K)
+    if ws is None:
+        ws = workspace(need, V.device)
+    st = lib().vc_cluster(_ptr(V), B, H, N, d, int(K), int(iters), int(bool(cold_start)), _ptr(centroids),
+                          _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st)
+
+
+def quantize_outputs(B, H, N, d, device="cuda"):
+    nb = N // BLOCK
+    kw = dict(device=device)
+    return dict(
+        Qq=torch.empty((B, H, N, d), dtype=torch.uint8, **kw), sQ=torch.empty((B, H, nb), dtype=torch.float32, **kw),
+        Kq=torch.empty((B, H, N, d), dtype=torch.uint8, **kw), sK=torch.empty((B, H, nb), dtype=torch.float32, **kw),
+        Vq=torch.empty((B, H, nb, d, BLOCK), dtype=torch.uint8, **kw), sV=torch.empty((B, H, d), dtype=torch.float32, **kw),
+        mu=torch.empty((B, H, nb, d), dtype=torch.bfloat16, **kw),
+        mu_scaled=torch.empty((B, H, nb, d), dtype=torch.float32, **kw),
+    )
+
+
+def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK):
+    """Fused quantiser; `out` is a dict as returned by quantize_outputs()."""
+    B, H, N, d = _dims(Q)
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, (B, H, N, d), n)
+    if perm is not None:
+        _need(perm, torch.int32, (B, H, N), "perm")
+    need = vc_quantize_workspace_bytes(B, H, N, d, block)
+    if ws is None:
+        ws = workspace(need, Q.device)
+    st = lib().vc_quantize(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, int(block), int(flags),
+                           _ptr(out["Qq"]), _ptr(out["sQ"]), _ptr(out["Kq"]), _ptr(out["sK"]), _ptr(out["Vq"]),
+                           _ptr(out["sV"]), _ptr(out.get("mu")), _ptr(out.get("mu_scaled")), _ptr(ws), ws.numel(),
+                           _stream(stream))
+    _check(st)
+    return out
+
+
+def vc_attention(q, O, beta=-0.35, flags=VC_F_EXPCAST, restore_mean=True, stream=None, block=BLOCK):
+    """Attention over the quantised tensors `q` (dict from vc_quantize); O bf16 [B,H,N,d]."""
+    B, H, N, d = _dims(O)
+    mu = q["mu_scaled"] if restore_mean else None
+    st = lib().vc_attention(_ptr(q["Qq"]), _ptr(q["sQ"]), _ptr(q["Kq"]), _ptr(q["sK"]), _ptr(q["Vq"]), _ptr(q["sV"]),
+                            _ptr(mu), B, H, N, d, int(block), float(beta), int(flags), _ptr(O), _stream(stream))
+    _check(st)
+    return O
+
+
+def vc_attention_dump(q, O, dump_block, codes, beta=-0.35, flags=VC_F_EXPCAST, restore_mean=True, stream=None,
+                      block=BLOCK):
+    B, H, N, d = _dims(O)
+    _need(codes, torch.uint8, (B, H, N, BLOCK), "codes")
+    mu = q["mu_scaled"] if restore_mean else None
+    st = lib().vc_attention_dump(_ptr(q["Qq"]), _ptr(q["sQ"]), _ptr(q["Kq"]), _ptr(q["sK"]), _ptr(q["Vq"]),
+                                 _ptr(q["sV"]), _ptr(mu), B, H, N, d, int(block), float(beta), int(flags), _ptr(O),
+                                 int(dump_block), _ptr(codes), _stream(stream))
+    _check(st)
+    return O, codes
+
+
+def vc_debug_expcast(acc, scale8, bias, codes, stream=None):
+    n = acc.numel()
+    for t, name in ((acc, "acc"), (scale8, "scale8"), (bias, "bias")):
+        _need(t, torch.float32, tuple(acc.shape), name)
+    _need(codes, torch.uint8, tuple(acc.shape), "codes")
+    st = lib().vc_debug_expcast(_ptr(acc), _ptr(scale8), _ptr(bias), _ptr(codes), n, _stream(stream))
+    _check(st)
+    return codes

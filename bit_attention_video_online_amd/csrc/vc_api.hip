@@ -1,0 +1,173 @@
+// vc_api.hip -- the C ABI declared in include/vc.h: argument validation on the host,
+// then asynchronous launches on the caller's stream. Nothing here allocates,
+// synchronises or keeps state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/vc.h"
+
+extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
+                                  int d, uint32_t flags, float cL, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
+                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* ws, hipStream_t st);
+extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
+extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                                   const uint8_t* Vq, const float* sV, const float* mu, int B, int H, int N, int d,
+                                   float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
+extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
+                                 hipStream_t st);
+extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
+extern "C" int vc_launch_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold, float* C,
+                                 int32_t* labels, int32_t* perm, void* ws, hipStream_t st);
+extern "C" int vc_max_clusters(void);
+
+namespace {
+
+// fl32(log2(e) / sqrt(d)) for the supported head sizes, as exact binary32 bit patterns
+// (log2(e)/8 and log2(e)/sqrt(128) rounded to nearest).
+float log2e_over_sqrt_d(int d) {
+  uint32_t bits = d == 64 ? 0x3e38aa3bu : 0x3e0293eeu;
+  float f;
+  memcpy(&f, &bits, 4);
+  return f;
+}
+
+bool shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || (N % 128) != 0 || (d != 64 && d != 128)) return false;
+  const long long el = (long long)B * H * N * d;
+  return el < (1LL << 31);
+}
+bool aligned16(const void* p) { return p == nullptr || (((uintptr_t)p) & 15u) == 0; }
+
+struct Range {
+  const char* a;
+  size_t n;
+};
+bool overlaps(Range x, Range y) {
+  if (!x.a || !y.a || x.n == 0 || y.n == 0) return false;
+  return x.a < y.a + y.n && y.a < x.a + x.n;
+}
+
+}  // namespace
+
+extern "C" const char* vc_status_string(vc_status s) {
+  switch (s) {
+    case VC_OK: return "VC_OK";
+    case VC_E_NULLPTR: return "VC_E_NULLPTR: a required pointer is NULL";
+    case VC_E_SHAPE: return "VC_E_SHAPE: need B,H >= 1, N a positive multiple of 128, d in {64,128}, block 128";
+    case VC_E_PARAM: return "VC_E_PARAM: cluster count, iterations, beta or flags out of range";
+    case VC_E_WORKSPACE: return "VC_E_WORKSPACE: workspace smaller than required";
+    case VC_E_UNSUPPORTED: return "VC_E_UNSUPPORTED: misaligned buffer or unsupported device";
+    case VC_E_HIP: return "VC_E_HIP: a HIP launch failed";
+    case VC_E_ALIAS: return "VC_E_ALIAS: an output overlaps an input";
+    default: return "unknown vc_status";
+  }
+}
+
+extern "C" int vc_abi_version(void) { return VC_ABI_VERSION; }
+
+extern "C" size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K) {
+  if (!shape_ok(B, H, N, d) || K < 1 || K > N) return 0;
+  return vc_cluster_ws_bytes(B, H, N, d, K);
+}
+
+extern "C" vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
+                                float* centroids, int32_t* labels, int32_t* perm, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!V || !centroids || !labels || !perm || !workspace) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d)) return VC_E_SHAPE;
+  if (K < 1 || K > N || K > vc_max_clusters() || iters < 1 || iters > 1000) return VC_E_PARAM;
+  if (workspace_bytes < vc_cluster_ws_bytes(B, H, N, d, K)) return VC_E_WORKSPACE;
+  if (!aligned16(V) || !aligned16(centroids) || !aligned16(labels) || !aligned16(perm) || !aligned16(workspace))
+    return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N;
+  Range in{(const char*)V, el * d * 2};
+  if (overlaps(in, {(const char*)centroids, (size_t)B * H * K * d * 4}) || overlaps(in, {(const char*)labels, el * 4}) ||
+      overlaps(in, {(const char*)perm, el * 4}) || overlaps({(const char*)labels, el * 4}, {(const char*)perm, el * 4}))
+    return VC_E_ALIAS;
+  if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
+                        (hipStream_t)stream) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int block) {
+  if (!shape_ok(B, H, N, d) || block != 128) return 0;
+  return vc_quantize_ws_bytes(B, H, N, d);
+}
+
+extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
+                                 int d, int block, uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
+                                 uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || !workspace) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
+  if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST)) return VC_E_PARAM;
+  if (workspace_bytes < vc_quantize_ws_bytes(B, H, N, d)) return VC_E_WORKSPACE;
+  const void* ptrs[] = {Q, K, V, perm, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N * d, nbk = (size_t)B * H * (N / 128);
+  const Range ins[] = {{(const char*)Q, el * 2}, {(const char*)K, el * 2}, {(const char*)V, el * 2},
+                       {(const char*)perm, (size_t)B * H * N * 4}};
+  const Range outs[] = {{(const char*)Qq, el}, {(const char*)sQ, nbk * 4}, {(const char*)Kq, el},
+                        {(const char*)sK, nbk * 4}, {(const char*)Vq, el}, {(const char*)sV, (size_t)B * H * d * 4},
+                        {(const char*)mu, nbk * d * 2}, {(const char*)mu_scaled, nbk * d * 4}};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return VC_E_ALIAS;
+  if (vc_launch_quantize(Q, K, V, perm, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled,
+                         workspace, (hipStream_t)stream) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                                  const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N, int d,
+                                  int block, float beta, uint32_t flags, void* O, int dump_block, uint8_t* codes,
+                                  void* stream) {
+  if (!Qq || !sQ || !Kq || !sK || !Vq || !sV || !O) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
+  if (!isfinite(beta) || (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST))) return VC_E_PARAM;
+  const void* ptrs[] = {Qq, sQ, Kq, sK, Vq, sV, mu_scaled, O, codes};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N * d, nbk = (size_t)B * H * (N / 128);
+  const Range ins[] = {{(const char*)Qq, el}, {(const char*)sQ, nbk * 4}, {(const char*)Kq, el},
+                       {(const char*)sK, nbk * 4}, {(const char*)Vq, el}, {(const char*)sV, (size_t)B * H * d * 4},
+                       {(const char*)mu_scaled, nbk * d * 4}};
+  const Range outs[] = {{(const char*)O, el * 2}, {(const char*)codes, (size_t)B * H * N * 128}};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return VC_E_ALIAS;
+  if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
+  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, beta, (flags & VC_F_EXPCAST) ? 1 : 0,
+                          (uint16_t*)O, dump_block, codes, (hipStream_t)stream) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                                  const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N, int d,
+                                  int block, float beta, uint32_t flags, void* O, void* stream) {
+  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, block, beta, flags, O, -1, nullptr, stream);
+}
+
+extern "C" vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                                       const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N,
+                                       int d, int block, float beta, uint32_t flags, void* O, int dump_block,
+                                       uint8_t* codes, void* stream) {
+  if (!codes) return VC_E_NULLPTR;
+  if (N >= 128 && (dump_block < 0 || dump_block >= N / 128)) return VC_E_PARAM;
+  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, block, beta, flags, O, dump_block, codes,
+                          stream);
+}
+
+extern "C" vc_status vc_debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes, size_t n,
+                                      void* stream) {
+  if (n == 0) return VC_OK;
+  if (!acc || !scale8 || !bias || !codes) return VC_E_NULLPTR;
+  if (vc_launch_expcast(acc, scale8, bias, codes, n, (hipStream_t)stream) != 0) return VC_E_HIP;
+  return VC_OK;
+}

@@ -1,0 +1,297 @@
+// vc_attention.hip -- VC-Attention forward for gfx950 (MI355X).
+//
+// Paper page (paper.rainbus.top), method steps (3) and (4); study notes 2-3, 2-4;
+// online-softmax prerequisite. Non-causal; every query sees all keys.
+//
+// Work decomposition: one work-group = 4 waves = 128 query rows of one (b,h);
+// each wave owns 32 rows as two 16-row groups. The key loop walks the 128-key
+// blocks in ascending order (ExpCast bytes depend on the running maximum, so the
+// loop is never split or reordered).
+//
+// Per key block, per wave:
+//   S^T (keys x queries) = K_j Q^T with v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3,
+//   binary32 accumulate, one instruction covers d = 128). MFMA kb (0..7) takes the
+//   key rows kappa(kb, r) = 32*(r/4) + 4*kb + (r%4), so lane group g = lane/16 holds
+//   keys 32*g + 4*kb + i (i = 0..3) of its query: exactly the 32 K-slots that the
+//   PV MFMA's B operand expects from that lane in natural key order. The
+//   probability bytes therefore never leave the lane: the four accumulators of
+//   MFMA kb become dword kb of the B operand.
+//   Row max / row sum over a query's 128 keys: 32 values in-lane, then the four
+//   lane groups are combined with v_permlane16_swap and v_permlane32_swap.
+//   O^T (d x queries) += V_j^T P^T with the same instruction (K = 128 keys); V
+//   codes arrive block-transposed ([d][128]) so the A operand is contiguous.
+//   Mean restoration: O^T[c][q] += r_q * mu_scaled_j[c] (one FMA per accumulator).
+// K and V tiles are staged through LDS with a 16-byte XOR swizzle that keeps the
+// ds_read_b128 operand fetches free of bank conflicts; the next tile is prefetched
+// into registers while the current one is consumed.
+#include "vc_device.h"
+
+namespace vc {
+
+constexpr int kAThreads = 256;
+
+__device__ __forceinline__ float lane_max4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float lane_sum4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS swizzles (16-byte chunk index XOR): K tile rows are D bytes, V tile rows 128 bytes.
+template <int D>
+__device__ __forceinline__ int k_off(int row, int chunk) {
+  constexpr int CPR = D / 16;
+  int s = (((row >> 1) & 3) | (((row >> 5) & 1) << 2)) & (CPR - 1);
+  return row * D + ((chunk ^ s) << 4);
+}
+__device__ __forceinline__ int v_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+__device__ __forceinline__ v8i ld_frag(const uint8_t* base, int off0, int off1) {
+  uint4 a = *reinterpret_cast<const uint4*>(base + off0);
+  uint4 b = *reinterpret_cast<const uint4*>(base + off1);
+  v8i r;
+  r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+  r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+  return r;
+}
+
+template <int D, bool EXPCAST, bool RESTORE, bool DUMP>
+__global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
+                                                         const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
+                                                         const uint8_t* __restrict__ Vq, const float* __restrict__ sV,
+                                                         const float* __restrict__ mu_scaled, int N, int total,
+                                                         float C0, uint16_t* __restrict__ O, int dump_block,
+                                                         uint8_t* __restrict__ dump) {
+  constexpr int TILE = kBlock * D;              // bytes per K (or V) tile
+  constexpr int NCH = TILE / 16;                // 16-byte chunks per tile
+  constexpr int PF = NCH / kAThreads;           // chunks per thread per tile (4 or 2)
+  constexpr int DB = D / 16;                    // 16-row d blocks
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[TILE];
+  __shared__ __attribute__((aligned(16))) float mus[D];
+
+  const int nb = N / kBlock;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int bh = logical / nb, qb = logical % nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, lg = lane >> 4;
+
+  const uint8_t* Kh = Kq + (size_t)bh * N * D;
+  const uint8_t* Vh = Vq + (size_t)bh * N * D;
+  const float sq = sQ[(size_t)bh * nb + qb];
+
+  // ---- Q fragments (B operand of S^T): query row, bytes [32*lg, 32*lg+32)
+  v8i qf[2];
+  for (int g = 0; g < 2; g++) {
+    const int q = qb * kBlock + wave * 32 + g * 16 + r16;
+    if (D == 128 || lg < 2) {
+      const uint4* src = reinterpret_cast<const uint4*>(Qq + ((size_t)bh * N + q) * D + 32 * lg);
+      uint4 a = src[0], b = src[1];
+      qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
+      qf[g][4] = b.x; qf[g][5] = b.y; qf[g][6] = b.z; qf[g][7] = b.w;
+    } else {
+      for (int k = 0; k < 8; k++) qf[g][k] = 0;
+    }
+  }
+
+  // ---- tile staging helpers
+  uint4 pk[PF], pv[PF];
+  float pmu = 0.0f;
+  auto fetch = [&](int j) {
+    const uint4* ks = reinterpret_cast<const uint4*>(Kh + (size_t)j * TILE);
+    const uint4* vs = reinterpret_cast<const uint4*>(Vh + (size_t)j * TILE);
+    for (int i = 0; i < PF; i++) { pk[i] = ks[tid + i * kAThreads]; pv[i] = vs[tid + i * kAThreads]; }
+    if (RESTORE && tid < D) pmu = mu_scaled[((size_t)bh * nb + j) * D + tid];
+  };
+  auto stash = [&]() {
+    for (int i = 0; i < PF; i++) {
+      int q = tid + i * kAThreads;
+      int kr = q / (D / 16), kc = q % (D / 16);
+      *reinterpret_cast<uint4*>(Ks + k_off<D>(kr, kc)) = pk[i];
+      int vr = q >> 3, vc = q & 7;
+      *reinterpret_cast<uint4*>(Vs + v_off(vr, vc)) = pv[i];
+    }
+    if (RESTORE && tid < D) mus[tid] = pmu;
+  };
+
+  float m[2] = {-__builtin_inff(), -__builtin_inff()};
+  float lsum[2] = {0.0f, 0.0f};
+  v4f oacc[DB][2];
+  for (int db = 0; db < DB; db++)
+    for (int g = 0; g < 2; g++) oacc[db][g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  fetch(0);
+  stash();
+  __syncthreads();
+
+  for (int j = 0; j < nb; j++) {
+    if (j + 1 < nb) fetch(j + 1);
+
+    // ---- S^T = K_j Q^T
+    v4f sacc[8][2];
+    for (int kb = 0; kb < 8; kb++) {
+      const int krow = 32 * (r16 >> 2) + 4 * kb + (r16 & 3);
+      v8i a;
+      if (D == 128 || lg < 2) {
+        a = ld_frag(Ks, k_off<D>(krow, 2 * lg), k_off<D>(krow, 2 * lg + 1));
+      } else {
+        for (int k = 0; k < 8; k++) a[k] = 0;
+      }
+      for (int g = 0; g < 2; g++)
+        sacc[kb][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qf[g], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                       0, 0, 0, 0, 0, 0);
+    }
+    const float sigma = sq * sK[(size_t)bh * nb + j];
+
+    // ---- online softmax, probability bytes, row sums
+    v8i pf[2];
+    float rsum[2];
+    for (int g = 0; g < 2; g++) {
+      float mx = sacc[0][g][0];
+      for (int kb = 0; kb < 8; kb++)
+        for (int i = 0; i < 4; i++) mx = fmaxf(mx, sacc[kb][g][i]);
+      mx = lane_max4(mx);
+      const float mnew = sigma * mx;
+      const float mp = fmaxf(m[g], mnew);
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mp);
+      float r = 0.0f;
+      if (EXPCAST) {
+        const float bias = C0 - 8.0f * mp;
+        const float s8 = 8.0f * sigma;
+        for (int kb = 0; kb < 8; kb++) {
+          uint32_t w = 0;
+          w = expcast_byte(sacc[kb][g][0], s8, bias, w, 0);
+          w = expcast_byte(sacc[kb][g][1], s8, bias, w, 1);
+          w = expcast_byte(sacc[kb][g][2], s8, bias, w, 2);
+          w = expcast_byte(sacc[kb][g][3], s8, bias, w, 3);
+          pf[g][kb] = (int)w;
+          v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+          v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+          r += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        }
+      } else {
+        for (int kb = 0; kb < 8; kb++) {
+          float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][0] - mp);
+          float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][1] - mp);
+          float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][2] - mp);
+          float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][3] - mp);
+          pf[g][kb] = (int)e4m3x4_from_f32(p0, p1, p2, p3);
+          r += (p0 + p1) + (p2 + p3);
+        }
+      }
+      r = lane_sum4(r);
+      rsum[g] = r;
+      lsum[g] = alpha * lsum[g] + r;
+      if (__ballot(alpha != 1.0f)) {
+        for (int db = 0; db < DB; db++) oacc[db][g] *= alpha;
+      }
+      m[g] = mp;
+      if (DUMP && j == dump_block) {
+        const int q = qb * kBlock + wave * 32 + g * 16 + r16;
+        uint4* dst = reinterpret_cast<uint4*>(dump + ((size_t)bh * N + q) * kBlock + 32 * lg);
+        dst[0] = make_uint4(pf[g][0], pf[g][1], pf[g][2], pf[g][3]);
+        dst[1] = make_uint4(pf[g][4], pf[g][5], pf[g][6], pf[g][7]);
+      }
+    }
+
+    // ---- O^T += V_j^T P^T  (+ r * mu_j)
+    for (int db = 0; db < DB; db++) {
+      const int vrow = 16 * db + r16;
+      v8i a = ld_frag(Vs, v_off(vrow, 2 * lg), v_off(vrow, 2 * lg + 1));
+      for (int g = 0; g < 2; g++)
+        oacc[db][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf[g], oacc[db][g], 0, 0, 0, 0, 0, 0);
+    }
+    if (RESTORE) {
+      for (int db = 0; db < DB; db++) {
+        const float4 mu4 = *reinterpret_cast<const float4*>(mus + 16 * db + 4 * lg);
+        for (int g = 0; g < 2; g++) {
+          oacc[db][g][0] += rsum[g] * mu4.x;
+          oacc[db][g][1] += rsum[g] * mu4.y;
+          oacc[db][g][2] += rsum[g] * mu4.z;
+          oacc[db][g][3] += rsum[g] * mu4.w;
+        }
+      }
+    }
+    __syncthreads();
+    if (j + 1 < nb) {
+      stash();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: O = bf16(sV * A / l), rows in original order
+  for (int g = 0; g < 2; g++) {
+    const int q = qb * kBlock + wave * 32 + g * 16 + r16;
+    const float il = 1.0f / lsum[g];
+    uint16_t* orow = O + ((size_t)bh * N + q) * D;
+    for (int db = 0; db < DB; db++) {
+      const int c = 16 * db + 4 * lg;
+      const float4 s4 = *reinterpret_cast<const float4*>(sV + (size_t)bh * D + c);
+      uint32_t w0 = (uint32_t)f32_to_bf16(s4.x * oacc[db][g][0] * il) | ((uint32_t)f32_to_bf16(s4.y * oacc[db][g][1] * il) << 16);
+      uint32_t w1 = (uint32_t)f32_to_bf16(s4.z * oacc[db][g][2] * il) | ((uint32_t)f32_to_bf16(s4.w * oacc[db][g][3] * il) << 16);
+      *reinterpret_cast<uint2*>(orow + c) = make_uint2(w0, w1);
+    }
+  }
+}
+
+__global__ void expcast_kernel(const float* __restrict__ acc, const float* __restrict__ s8, const float* __restrict__ bias,
+                               uint8_t* __restrict__ out, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)expcast_byte(acc[i], s8[i], bias[i], 0u, 0);
+}
+
+template <int D, bool E, bool R, bool DU>
+static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
+                        const float* sV, const float* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
+                        uint8_t* dump, hipStream_t st) {
+  const int total = BH * (N / kBlock);
+  attn_fwd<D, E, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
+}
+
+template <int D, bool E, bool R>
+static void launch_attn_d(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
+                          const float* sV, const float* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
+                          uint8_t* dump, hipStream_t st) {
+  if (dump) launch_attn<D, E, R, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else launch_attn<D, E, R, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+}
+
+}  // namespace vc
+
+using namespace vc;
+
+extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                                   const uint8_t* Vq, const float* sV, const float* mu, int B, int H, int N, int d,
+                                   float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
+  const int BH = B * H;
+  const float C0 = 120.0f + beta;  // fl32(120 + beta)
+  const bool R = mu != nullptr;
+  if (d == 128) {
+    if (expcast) { if (R) launch_attn_d<128, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+                   else launch_attn_d<128, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
+    else { if (R) launch_attn_d<128, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+           else launch_attn_d<128, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
+  } else {
+    if (expcast) { if (R) launch_attn_d<64, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+                   else launch_attn_d<64, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
+    else { if (R) launch_attn_d<64, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+           else launch_attn_d<64, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
+                                 hipStream_t st) {
+  if (n == 0) return 0;
+  const size_t blocks = (n + 255) / 256;
+  expcast_kernel<<<(unsigned)blocks, 256, 0, st>>>(acc, s8, bias, out, n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

@@ -1,0 +1,164 @@
+/*
+ * vc.h -- C ABI of the VC-Attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "VC-Attention: Value Smoothing and Softmax Casting for Low-bit
+ * Attention" (arXiv 2609.15810). Non-causal FP8 flash attention with
+ *   - V-Smooth: online k-means on value tokens per (batch, head), one joint
+ *     permutation of K and V (exact for non-causal attention: P'V' = PV), removal
+ *     of each 128-token block's mean, E4M3 quantisation of the residual only, and
+ *     exact restoration of the mean inside the online softmax from the row sums;
+ *   - ExpCast-FP8: probability bytes written straight from log2-domain scores,
+ *     c = clip(Round(8(u+8) + 56 + beta), 0, 120), read as E4M3.
+ * (paper page paper.rainbus.top, "Method steps" (1)-(4); study notes on
+ * dimensionstp.github.io, sections 2-1 to 2-4.)
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise; `stream`
+ *     is a hipStream_t passed as void* (NULL = the default stream).
+ *   - The caller owns and allocates every buffer, workspaces included. The library
+ *     never allocates, frees or synchronises, keeps no global state, and may be
+ *     called concurrently on different streams with disjoint buffers.
+ *   - bf16 tensors are bfloat16 bit patterns; "[B,H,N,d]" means contiguous
+ *     row-major with d fastest.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and outputs are untouched. A launch failure is
+ *     reported as VC_E_HIP; faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP work.
+ *   - Supported shapes: d in {64, 128}; block == 128; N a positive multiple of
+ *     128; B, H >= 1; B*H*N*d < 2^31. Buffers must be 16-byte aligned.
+ *   - NaN or infinite inputs are not supported: outputs are then unspecified, but
+ *     every kernel still terminates.
+ */
+#ifndef VC_H
+#define VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t vc_status;
+enum {
+  VC_OK = 0,
+  VC_E_NULLPTR = 1,     /* a required pointer is NULL */
+  VC_E_SHAPE = 2,       /* B, H, N, d or block outside the supported set */
+  VC_E_PARAM = 3,       /* cluster count, iteration count, beta or flags invalid */
+  VC_E_WORKSPACE = 4,   /* workspace smaller than the *_workspace_bytes query */
+  VC_E_UNSUPPORTED = 5, /* no gfx950 device current, or a misaligned buffer */
+  VC_E_HIP = 6,         /* a HIP launch failed */
+  VC_E_ALIAS = 7        /* an output overlaps an input */
+};
+
+enum {
+  VC_F_KSMOOTH = 1u, /* subtract the per-channel key mean over all N tokens */
+  VC_F_VSMOOTH = 2u, /* block-mean removal of V' and mean restoration */
+  VC_F_EXPCAST = 4u  /* ExpCast-FP8 probability bytes (else exp2 then cast) */
+};
+
+/* Static description of a status code (host function, never NULL). */
+const char* vc_status_string(vc_status s);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int vc_abi_version(void);
+#define VC_ABI_VERSION 1
+
+/* ------------------------------------------------------------------------
+ * vc_cluster -- online k-means on value tokens (paper page, method step (1)):
+ * labels z per (batch, head), pi = argsort(z), warm-started centroids.
+ *
+ * Reading taken: Lloyd iterations (assign to the nearest bfloat16-rounded
+ * centroid by squared Euclidean distance, exact, ties to the lowest index; then
+ * centroid = binary32 rounding of the exact member mean; an empty cluster keeps
+ * its centroid). `iters` >= 1 assign/update rounds. Cold start first sets
+ * C_k = V[floor((2k+1)N/(2K))].
+ *
+ *   V          bf16 [B,H,N,d]                      input
+ *   K          clusters per head, 1 <= K <= N
+ *   centroids  float [B,H,K,d]  in: warm-start state (ignored when cold_start),
+ *                               out: centroids after the last update
+ *   labels     int32 [B,H,N]    out: labels of the last assignment
+ *   perm       int32 [B,H,N]    out: stable argsort of labels (ties by token index)
+ *   workspace  >= vc_cluster_workspace_bytes(B,H,N,d,K) bytes of device memory
+ *
+ * Scores: the assignment kernel ranks clusters in binary32 with a rigorous error
+ * bound and re-ranks every token whose best two candidates are within that bound
+ * in binary64, so labels equal the exact argmin whenever the binary64 squared
+ * distances are themselves exact (always, for values whose per-token exponent
+ * span is below 2^18).
+ * ------------------------------------------------------------------------ */
+size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K);
+vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
+                     float* centroids, int32_t* labels, int32_t* perm,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * vc_quantize -- fused quantiser (paper page, method step (2); study notes 2-2).
+ *
+ *   Q, K, V    bf16 [B,H,N,d]
+ *   perm       int32 [B,H,N], or NULL for the identity (plain FP8 path)
+ *   block      must be 128
+ *   flags      VC_F_KSMOOTH | VC_F_VSMOOTH (VC_F_EXPCAST ignored)
+ * Outputs (all written on success):
+ *   Qq   uint8 [B,H,N,d]           E4M3 codes of Q, original token order
+ *   sQ   float [B,H,N/128]         Q block scale times fl32(log2(e)/sqrt(d))
+ *   Kq   uint8 [B,H,N,d]           codes of K~' = (K - kbar)[perm], row i = token perm[i]
+ *   sK   float [B,H,N/128]         K' block scales
+ *   Vq   uint8 [B,H,N/128,d,128]   BLOCK-TRANSPOSED residual codes:
+ *                                  Vq[b,h,j,c,t] = code of R[128j+t, c], R = V[perm] - mu
+ *   sV   float [B,H,d]             per-channel residual scale (over all N tokens)
+ *   mu   bf16 [B,H,N/128,d]        block means of V' (zero when !VC_F_VSMOOTH); may be NULL
+ *   mu_scaled float [B,H,N/128,d]  fl32(mu / sV), consumed by vc_attention
+ * Arithmetic: block and channel scales are fl32(amax/448) with codes
+ * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
+ * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).
+ * workspace >= vc_quantize_workspace_bytes(B,H,N,d,block).
+ * ------------------------------------------------------------------------ */
+size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int block);
+vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm,
+                      int B, int H, int N, int d, int block, uint32_t flags,
+                      uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                      void* mu, float* mu_scaled, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * vc_attention -- non-causal attention over the quantised tensors (paper page,
+ * method steps (3) and (4); online-softmax prerequisite).
+ *
+ * For each query row i and every 128-key block j in ascending order:
+ *   S = Qq_i . Kq_j^T on FP8 matrix cores (binary32 accumulation),
+ *   sigma = fl32(sQ[i/128] * sK[j]),  m' = max(m, fl32(sigma * max S)),
+ *   VC_F_EXPCAST: c = clamp(rne(fma(S, 8 sigma, fl32(fl32(120 + beta) - 8 m'))), 0, 120)
+ *   otherwise:    c = e4m3(256 * exp2(fl32(sigma S) - m')),
+ *   r = row sum of the probabilities, l = 2^(m - m') l + r,
+ *   A = 2^(m - m') A + c . Vq_j + r * mu_scaled_j   (mu term only if mu_scaled != NULL),
+ * and finally O_i = bf16(sV * A / l), rows in original token order.
+ *
+ *   O      bf16 [B,H,N,d] output; must not overlap any input
+ *   beta   finite; the pages use -0.35
+ *   flags  VC_F_EXPCAST selects ExpCast; other bits ignored
+ * ------------------------------------------------------------------------ */
+vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                       const uint8_t* Vq, const float* sV, const float* mu_scaled,
+                       int B, int H, int N, int d, int block, float beta, uint32_t flags,
+                       void* O, void* stream);
+
+/* Same computation, additionally writing the probability bytes that key block
+ * `dump_block` received from every query: codes uint8 [B,H,N,128] (key order of
+ * the block). Test support for in-kernel byte parity. */
+vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                            const uint8_t* Vq, const float* sV, const float* mu_scaled,
+                            int B, int H, int N, int d, int block, float beta, uint32_t flags,
+                            void* O, int dump_block, uint8_t* codes, void* stream);
+
+/* ExpCast as a plain elementwise function: codes[i] = clamp(rne(fma(acc[i],
+ * scale8[i], bias[i])), 0, 120), evaluated by the same device function that
+ * vc_attention uses. All arrays have n elements (n may be 0). */
+vc_status vc_debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes,
+                           size_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_H */

@@ -1,0 +1,39 @@
+"""Helpers shared by the GPU tests: moving seeded numpy inputs onto the device and
+running the HIP path through the C ABI binding."""
+import numpy as np
+import torch
+
+import bit_attention_video_online_amd as vc
+
+
+def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_quantize(Q, K, V, perm, flags):
+    """Q, K, V: numpy bf16 bits [B,H,N,d]; perm numpy int32 [B,H,N] or None."""
+    B, H, N, d = Q.shape
+    out = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(to_dev_bf16(Q), to_dev_bf16(K), to_dev_bf16(V), None if perm is None else to_dev(perm), flags, out)
+    torch.cuda.synchronize()
+    return out
+
+
+def vq_rowmajor(Vq: np.ndarray) -> np.ndarray:
+    """[B,H,nb,d,128] block-transposed codes -> [B,H,N,d] row-major (permuted token order)."""
+    B, H, nb, d, T = Vq.shape
+    return np.ascontiguousarray(Vq.transpose(0, 1, 2, 4, 3).reshape(B, H, nb * T, d))
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))

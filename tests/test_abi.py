@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/vc.h declares, and rejects invalid arguments on the host before anything is
+enqueued (the pointers below are never dereferenced: validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc.h")
+
+vc = pytest.importorskip("bit_attention_video_online_amd")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:vc_status|size_t|int|const char\*)\s+(vc_\w+)\s*\(", txt, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vc.LIB_PATH):
+        pytest.skip("libvc.so not built")
+    return vc.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.vc_abi_version() == 1
+    for s in range(8):
+        assert vc.vc_status_string(s).startswith(("VC_OK", "VC_E_"))
+    assert vc.vc_status_string(99) == "unknown vc_status"
+
+
+FAKE = ctypes.c_void_p(4096)  # aligned, never dereferenced
+
+
+def _quant(L, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, perm=None, B=1, H=1, N=256, d=128, block=128, flags=3,
+             Qq=ctypes.c_void_p(1 << 20), sQ=ctypes.c_void_p(2 << 20), Kq=ctypes.c_void_p(3 << 20),
+             sK=ctypes.c_void_p(4 << 20), Vq=ctypes.c_void_p(5 << 20), sV=ctypes.c_void_p(6 << 20),
+             mu=ctypes.c_void_p(7 << 20), mus=ctypes.c_void_p(8 << 20), ws=ctypes.c_void_p(9 << 20),
+             wsb=1 << 30, st=None)
+    a.update(kw)
+    return L.vc_quantize(a["Q"], a["K"], a["V"], a["perm"], a["B"], a["H"], a["N"], a["d"], a["block"], a["flags"],
+                         a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"], a["mus"], a["ws"], a["wsb"],
+                         a["st"])
+
+
+def test_quantize_rejects_bad_arguments(L):
+    assert _quant(L, Q=None) == 1
+    assert _quant(L, N=200) == 2          # not a multiple of 128
+    assert _quant(L, N=0) == 2
+    assert _quant(L, d=96) == 2
+    assert _quant(L, block=64) == 2
+    assert _quant(L, B=0) == 2
+    assert _quant(L, flags=64) == 3
+    assert _quant(L, wsb=16) == 4
+    assert _quant(L, Qq=ctypes.c_void_p((1 << 20) + 4)) == 5   # misaligned
+    assert _quant(L, Qq=FAKE) == 7                             # output aliases the inputs
+
+
+def _attn(L, **kw):
+    a = dict(Qq=FAKE, sQ=ctypes.c_void_p(1 << 20), Kq=ctypes.c_void_p(2 << 20), sK=ctypes.c_void_p(3 << 20),
+             Vq=ctypes.c_void_p(4 << 20), sV=ctypes.c_void_p(5 << 20), mu=ctypes.c_void_p(6 << 20), B=1, H=1, N=256,
+             d=128, block=128, beta=-0.35, flags=4, O=ctypes.c_void_p(7 << 20), st=None)
+    a.update(kw)
+    return L.vc_attention(a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"], a["B"], a["H"], a["N"], a["d"],
+                          a["block"], a["beta"], a["flags"], a["O"], a["st"])
+
+
+def test_attention_rejects_bad_arguments(L):
+    assert _attn(L, O=None) == 1
+    assert _attn(L, N=130) == 2
+    assert _attn(L, d=32) == 2
+    assert _attn(L, beta=float("nan")) == 3
+    assert _attn(L, beta=float("inf")) == 3
+    assert _attn(L, flags=1 << 8) == 3
+    assert _attn(L, O=FAKE) == 7
+    assert _attn(L, Vq=ctypes.c_void_p((4 << 20) + 8)) == 5
+
+
+def test_attention_dump_rejects_bad_block(L):
+    st = L.vc_attention_dump(FAKE, ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20),
+                             ctypes.c_void_p(4 << 20), ctypes.c_void_p(5 << 20), None, 1, 1, 256, 128, 128, -0.35, 4,
+                             ctypes.c_void_p(7 << 20), 2, ctypes.c_void_p(8 << 20), None)
+    assert st == 3
+    st = L.vc_attention_dump(FAKE, ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20),
+                             ctypes.c_void_p(4 << 20), ctypes.c_void_p(5 << 20), None, 1, 1, 256, 128, 128, -0.35, 4,
+                             ctypes.c_void_p(7 << 20), 0, None, None)
+    assert st == 1
+
+
+def test_cluster_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(V=FAKE, B=1, H=1, N=256, d=128, K=8, iters=2, cold=1, C=ctypes.c_void_p(1 << 20),
+                 lab=ctypes.c_void_p(2 << 20), perm=ctypes.c_void_p(3 << 20), ws=ctypes.c_void_p(4 << 20),
+                 wsb=1 << 30)
+        a.update(kw)
+        return L.vc_cluster(a["V"], a["B"], a["H"], a["N"], a["d"], a["K"], a["iters"], a["cold"], a["C"], a["lab"],
+                            a["perm"], a["ws"], a["wsb"], None)
+    assert call(C=None) == 1
+    assert call(N=100) == 2
+    assert call(K=0) == 3
+    assert call(K=257) == 3          # more clusters than tokens
+    assert call(iters=0) == 3
+    assert call(wsb=8) == 4
+    assert call(lab=ctypes.c_void_p(3 << 20)) == 7   # labels alias perm
+
+
+def test_workspace_queries(L):
+    assert vc.vc_quantize_workspace_bytes(1, 40, 70400, 128) > 0
+    assert vc.vc_quantize_workspace_bytes(1, 1, 100, 128) == 0
+    assert vc.vc_cluster_workspace_bytes(1, 40, 70400, 128, 550) > 0
+    assert vc.vc_cluster_workspace_bytes(1, 1, 256, 128, 300) == 0
+
+
+def test_debug_expcast_zero_length_is_ok(L):
+    assert L.vc_debug_expcast(None, None, None, None, 0, None) == 0
+    assert L.vc_debug_expcast(None, None, None, None, 5, None) == 1
