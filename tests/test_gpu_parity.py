@@ -285,3 +285,23 @@ def test_perm_is_stable_sort_of_labels():
     for h in range(3):
         assert np.array_equal(np.sort(perm[0, h]), np.arange(4096))
         assert np.array_equal(perm[0, h], np.argsort(lab[0, h], kind="stable"))
+
+
+def test_attention_huge_scores_clamped_path():
+    """Scores whose running maximum exceeds 2^16 in log2 units take the kernel's clamped
+    ExpCast branch; output and dumped bytes must still match the emulation."""
+    N, d = 512, 128
+    rng = np.random.default_rng(31)
+    Q = synth.bf16_bits((rng.standard_normal((1, 1, N, d)) * 300).astype(np.float32))
+    K = synth.bf16_bits((rng.standard_normal((1, 1, N, d)) * 300).astype(np.float32))
+    V = synth.bf16_bits(rng.standard_normal((1, 1, N, d)).astype(np.float32))
+    out = gpu_quantize(Q, K, V, None, vc.VC_F_KSMOOTH)
+    q_or = oracle.quantize(Q[0, 0], K[0, 0], V[0, 0], None, oracle.FLAG_KSMOOTH)
+    rows = np.arange(N, dtype=np.int32)
+    _, c_or, m_or = oracle.attention_emul(q_or, rows, beta=BETA, mode=oracle.MODE_EXPCAST, dump_block=2, want_m=True)
+    assert np.abs(m_or).max() >= 65536.0
+    O, codes = _gpu_attention(out, N, d, 1, 1, True, False, dump_block=2)
+    O_or = oracle.attention_emul(q_or, rows, beta=BETA, mode=oracle.MODE_EXPCAST, restore_mean=False)
+    assert rel_l2(_o_f64(O[0, 0]), O_or) <= 2e-3
+    agree = np.mean(codes[0, 0] == c_or)
+    assert agree >= 0.99, agree
