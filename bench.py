@@ -44,6 +44,21 @@ def make_inputs(kind, B, H, N, d, seed):
     return out, w
 
 
+def profiled_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, valid only
+    while the kernel sources are the ones that were profiled (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_wan_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "bit_attention_video_online_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("vc_attention.hip", "vc_device.h"))
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return round((rec["fetch_bytes"] + rec["write_bytes"]) / 1e9, 3)
+
+
 def cpu_baseline(host, K_clusters, sample_rows, threads):
     """Time the oracle on a bounded sample of the same workload (head 0)."""
     import numpy as np
@@ -79,7 +94,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        x = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": x.numel()}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; the path shards by (batch, head) with no exchange, "
               "but multi-GPU runs are not part of it (use --gpus 1)", file=sys.stderr)
@@ -171,7 +197,8 @@ def main():
         "attention_tflops": round(att_tflops, 2),
         "attention_pct_fp8_peak": round(100.0 * att_tflops / FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": profiled_traffic(),
+                     "traffic_unit": "GB per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": "attn_fwd<128,ExpCast,restore>", "algorithmic_flops_per_launch": flops},
     }
     if args.attention_only:
