@@ -9,10 +9,10 @@
 //
 // Kernels, per iteration:
 //   cl_prep    chat = bf16(C) (as binary32), |chat|^2
-//   cl_assign  distances |c|^2 - 2 v.c in binary32 over a 64-token x 64-centroid LDS
-//              tile, with a rigorous per-distance error bound; a token whose best
-//              candidate is not separated from the rest by the bounds is re-ranked
-//              in binary64 (exact for bf16 data of moderate dynamic range).
+//   cl_assign_mfma  distances |c|^2 - 2 v.c with the dot products on bf16 MFMA, a
+//              rigorous per-distance error bound, and a binary64 re-rank of every token
+//              whose best candidate is not separated from the rest by the bounds (exact
+//              for bf16 data of moderate dynamic range).
 //   cl_hist / cl_scan / cl_scatter   stable counting sort of the labels (pi)
 //   cl_update  C_k = fl32(sum of members / count), binary64 sums in pi order
 // No atomics on floating-point data: every result is run-to-run deterministic.
@@ -20,8 +20,6 @@
 
 namespace vc {
 
-constexpr int kTok = 64;      // tokens per assign tile
-constexpr int kCen = 64;      // centroids per assign chunk
 constexpr int kChunk = 256;   // tokens per sort chunk
 constexpr int kMaxClusters = 8192;
 
@@ -71,104 +69,141 @@ __device__ __forceinline__ void cand_merge(Cand& a, const Cand& b) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Assignment on the matrix cores. S^T = chat V^T with v_mfma_f32_16x16x32_bf16: the
+// bf16 products are exact and the accumulation error of the instruction chain was
+// measured at <= 2^-21.3 sum|v_c chat_c| on adversarial wide-range data, far inside
+// the binary32 recursive-summation bound gamma_d sum|v_c chat_c| used below (doubled),
+// so the same certainty test and binary64 re-rank apply.
+// Work-group: 4 waves x 32 tokens (two 16-token groups). Centroid chunks of 64 rows of
+// bf16 are staged in LDS with a padded row stride (conflict-free 16-byte fragment
+// reads). Per MFMA the lane holds one token (lane % 16) and four centroids
+// (4 * (lane / 16) + i); the four lane groups of a token are merged at the end.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
 template <int D>
-__global__ __launch_bounds__(256) void cl_assign(const uint16_t* __restrict__ V, const float* __restrict__ chat,
-                                                 const float* __restrict__ cnorm, int N, int K,
-                                                 int32_t* __restrict__ labels) {
-  __shared__ __attribute__((aligned(16))) float Vt[D][kTok];   // transposed token tile
-  __shared__ __attribute__((aligned(16))) float Ct[D][kCen];   // transposed centroid chunk
-  __shared__ float vnorm[kTok];
-  __shared__ float cn[kCen];
-  __shared__ Cand rec[kTok][16];
-  __shared__ int unsure[kTok];
+__global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict__ V, const float* __restrict__ chat,
+                                                      const float* __restrict__ cnorm, int N, int K,
+                                                      int32_t* __restrict__ labels) {
+  constexpr int KS = D / 32;            // MFMA k-steps over the feature dimension
+  constexpr int ROWB = 2 * D + 16;      // padded LDS row stride (bytes)
+  constexpr int CCH = 64;               // centroids per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t Cs[CCH * ROWB];
+  __shared__ float cn_s[CCH], ca_s[CCH];
+  __shared__ Cand rec[128][4];
+  __shared__ int unsure[128];
   __shared__ int n_unsure;
   __shared__ double red_d[256];
   __shared__ int red_k[256];
 
-  const int bh = blockIdx.y, t0 = blockIdx.x * kTok;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int bh = blockIdx.y, t0 = blockIdx.x * 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, lg = lane >> 4;
   const uint16_t* Vh = V + (size_t)bh * N * D;
   const float* Ch = chat + (size_t)bh * K * D;
   const float* Nh = cnorm + (size_t)bh * K;
-  const int ntok = min(kTok, N - t0);
 
-  // token tile (transposed) and token norms
-  for (int i = tid; i < kTok * D; i += 256) {
-    int t = i / D, c = i % D;
-    Vt[c][t] = (t < ntok) ? bf16_to_f32(Vh[(size_t)(t0 + t) * D + c]) : 0.0f;
-  }
-  __syncthreads();
-  if (tid < kTok) {
+  // token fragments (B operand): token row, features [32 ks + 8 lg, +8)
+  bf16x8 vb[2][KS];
+  float vn[2];
+  for (int g = 0; g < 2; g++) {
+    const int t = t0 + wave * 32 + g * 16 + r16;
     float s = 0.0f;
-    for (int c = 0; c < D; c++) s = __builtin_fmaf(Vt[c][tid], Vt[c][tid], s);
-    vnorm[tid] = sqrtf(s) * 1.0001f;  // upper bound of |v|
+    for (int ks = 0; ks < KS; ks++) {
+      uint4 raw = *reinterpret_cast<const uint4*>(Vh + (size_t)t * D + 32 * ks + 8 * lg);
+      memcpy(&vb[g][ks], &raw, 16);
+      uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      for (int q = 0; q < 4; q++) {
+        float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xffff0000u);
+        s = __builtin_fmaf(lo, lo, s);
+        s = __builtin_fmaf(hi, hi, s);
+      }
+    }
+    // |v|^2 = sum over the four lane groups of this token
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    vn[g] = sqrtf(s) * 1.0001f;  // upper bound of |v|
   }
-  const float u = 5.9604645e-8f;                    // 2^-24
+  const float u = 5.9604645e-8f;  // 2^-24
   const float gam = (float)D * u / (1.0f - (float)D * u);
+  Cand cand[2];
+  for (int g = 0; g < 2; g++) cand[g] = Cand{__builtin_inff(), 0.0f, __builtin_inff(), 0x7fffffff};
+  const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
-  Cand cand[4];
-  for (int i = 0; i < 4; i++) cand[i] = Cand{__builtin_inff(), 0.0f, __builtin_inff(), 0x7fffffff};
-
-  for (int k0 = 0; k0 < K; k0 += kCen) {
+  for (int k0 = 0; k0 < K; k0 += CCH) {
     __syncthreads();
-    for (int i = tid; i < kCen * D; i += 256) {
-      int k = i / D, c = i % D;
-      Ct[c][k] = (k0 + k < K) ? Ch[(size_t)(k0 + k) * D + c] : 0.0f;
+    // stage chat rows [k0, k0+64) as bf16 (exact: chat holds bf16 values)
+    for (int i = tid; i < CCH * (D / 8); i += 256) {
+      const int k = i / (D / 8), c8 = (i % (D / 8)) * 8;
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (k0 + k < K) {
+        const float4* src = reinterpret_cast<const float4*>(Ch + (size_t)(k0 + k) * D + c8);
+        float4 x = src[0], y = src[1];
+        w.x = (__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xffff0000u);
+        w.y = (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xffff0000u);
+        w.z = (__float_as_uint(y.x) >> 16) | (__float_as_uint(y.y) & 0xffff0000u);
+        w.w = (__float_as_uint(y.z) >> 16) | (__float_as_uint(y.w) & 0xffff0000u);
+      }
+      *reinterpret_cast<uint4*>(Cs + k * ROWB + 2 * c8) = w;
     }
-    if (tid < kCen) cn[tid] = (k0 + tid < K) ? Nh[k0 + tid] : 0.0f;
+    if (tid < CCH) {
+      const bool ok = k0 + tid < K;
+      const float cnk = ok ? Nh[k0 + tid] : 0.0f;
+      cn_s[tid] = ok ? cnk : __builtin_inff();
+      ca_s[tid] = sqrtf(cnk) * 1.0001f;
+    }
     __syncthreads();
-    float dot[4][4];
-    for (int i = 0; i < 4; i++)
-      for (int k = 0; k < 4; k++) dot[i][k] = 0.0f;
-    for (int c = 0; c < D; c++) {
-      const float4 v4 = *reinterpret_cast<const float4*>(&Vt[c][ty * 4]);
-      const float4 c4 = *reinterpret_cast<const float4*>(&Ct[c][tx * 4]);
-      const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
-      const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-      for (int i = 0; i < 4; i++)
-        for (int k = 0; k < 4; k++) dot[i][k] = __builtin_fmaf(vv[i], cc[k], dot[i][k]);
-    }
-    for (int k = 0; k < 4; k++) {
-      const int kk = k0 + tx * 4 + k;
-      if (kk >= K) continue;
-      const float cnk = cn[tx * 4 + k];
-      const float cabs = sqrtf(cnk) * 1.0001f;
+    for (int cb = 0; cb < CCH / 16; cb++) {
+      v4f acc[2] = {zero4, zero4};
+      for (int ks = 0; ks < KS; ks++) {
+        bf16x8 a;
+        memcpy(&a, Cs + (16 * cb + r16) * ROWB + 2 * (32 * ks + 8 * lg), 16);
+        for (int g = 0; g < 2; g++) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[g][ks], acc[g], 0, 0, 0);
+      }
       for (int i = 0; i < 4; i++) {
-        const float dd = cnk - 2.0f * dot[i][k];
-        const float e = 2.0f * (2.0f * gam * vnorm[ty * 4 + i] * cabs + u * (cnk + fabsf(dd))) + 1e-30f;
-        cand_push(cand[i], dd, e, kk);
+        const int kl = 16 * cb + 4 * lg + i;
+        const float cnk = cn_s[kl];
+        if (!(cnk < __builtin_inff())) continue;  // padding past K
+        const float cabs = ca_s[kl];
+        for (int g = 0; g < 2; g++) {
+          const float dd = cnk - 2.0f * acc[g][i];
+          const float e = 2.0f * (2.0f * gam * vn[g] * cabs + u * (cnk + fabsf(dd))) + 1e-30f;
+          cand_push(cand[g], dd, e, k0 + kl);
+        }
       }
     }
   }
-  // merge the 16 partial records of each token
-  for (int i = 0; i < 4; i++) rec[ty * 4 + i][tx] = cand[i];
+  // merge the four lane groups of each token through LDS
   if (tid == 0) n_unsure = 0;
+  for (int g = 0; g < 2; g++) rec[wave * 32 + g * 16 + r16][lg] = cand[g];
   __syncthreads();
-  if (tid < kTok && tid < ntok) {
+  if (tid < 128) {
     Cand a = rec[tid][0];
-    for (int x = 1; x < 16; x++) cand_merge(a, rec[tid][x]);
+    for (int x = 1; x < 4; x++) cand_merge(a, rec[tid][x]);
     if (a.lb > a.d + a.e) {
       labels[(size_t)bh * N + t0 + tid] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
     } else {
-      int slot = atomicAdd(&n_unsure, 1);
-      unsure[slot] = tid;
+      unsure[atomicAdd(&n_unsure, 1)] = tid;
     }
   }
   __syncthreads();
   // exact re-rank (binary64) of the uncertain tokens, the whole group per token
   const int nu = n_unsure;
   for (int ui = 0; ui < nu; ui++) {
-    const int t = unsure[ui];
+    const int t = t0 + unsure[ui];
+    const uint16_t* vt = Vh + (size_t)t * D;
     double best = __builtin_inf();
     int bk = 0x7fffffff;
     for (int k = tid; k < K; k += 256) {
       const float* ck = Ch + (size_t)k * D;
       double s = 0.0;
       for (int c = 0; c < D; c++) {
-        double df = (double)Vt[c][t] - (double)ck[c];
+        double df = (double)bf16_to_f32(vt[c]) - (double)ck[c];
         s = fma(df, df, s);
       }
-      if (s < best) { best = s; bk = k; }  // k ascending per thread: ties keep the lower
+      if (s < best) { best = s; bk = k; }
     }
     red_d[tid] = best;
     red_k[tid] = bk;
@@ -181,7 +216,7 @@ __global__ __launch_bounds__(256) void cl_assign(const uint16_t* __restrict__ V,
       }
       __syncthreads();
     }
-    if (tid == 0) labels[(size_t)bh * N + t0 + t] = ((unsigned)red_k[0] < (unsigned)K) ? red_k[0] : 0;
+    if (tid == 0) labels[(size_t)bh * N + t] = ((unsigned)red_k[0] < (unsigned)K) ? red_k[0] : 0;
     __syncthreads();
   }
 }
@@ -290,11 +325,11 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
   int32_t* cstart = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
   int32_t* csize = (int32_t*)w;
   if (cold) cl_cold<<<dim3(K, BH), d, 0, st>>>(V, C, N, K, d);
-  const dim3 gtok((N + kTok - 1) / kTok, BH), gch(nch, BH), gk(K, BH);
+  const dim3 gmf(N / 128, BH), gch(nch, BH), gk(K, BH);
   for (int it = 0; it < iters; it++) {
     cl_prep<<<gk, d, 0, st>>>(C, chat, cnorm, K, d);
-    if (d == 128) cl_assign<128><<<gtok, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
-    else cl_assign<64><<<gtok, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
+    if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
+    else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
     cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
     cl_scan<<<BH, 1024, 0, st>>>(counts, K, nch, offs, cstart, csize);
     cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, perm);
