@@ -8,7 +8,7 @@ built, importing the functions raises.
 
 Entry points (same names as the C ABI):
   vc_cluster, vc_quantize, vc_attention, vc_attention_dump, vc_debug_expcast,
-  vc_cluster_workspace_bytes, vc_quantize_workspace_bytes, vc_status_string.
+  vc_cluster_workspace_bytes, vc_quantize_workspace_bytes, vc_mu_pack_size, vc_status_string.
 """
 from __future__ import annotations
 
@@ -57,7 +57,9 @@ def lib() -> ctypes.CDLL:
         L.vc_quantize_workspace_bytes.restype = S
         L.vc_quantize_workspace_bytes.argtypes = [I, I, I, I, I]
         L.vc_quantize.restype = I
-        L.vc_quantize.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, S, P]
+        L.vc_quantize.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.vc_mu_pack_size.restype = S
+        L.vc_mu_pack_size.argtypes = [I, I, I, I]
         L.vc_attention.restype = I
         L.vc_attention.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, U, P, P]
         L.vc_attention_dump.restype = I
@@ -112,6 +114,10 @@ def vc_cluster_workspace_bytes(B, H, N, d, K) -> int:
     return int(lib().vc_cluster_workspace_bytes(B, H, N, d, K))
 
 
+def vc_mu_pack_size(B, H, N, d) -> int:
+    return int(lib().vc_mu_pack_size(B, H, N, d))
+
+
 def vc_quantize_workspace_bytes(B, H, N, d, block=BLOCK) -> int:
     return int(lib().vc_quantize_workspace_bytes(B, H, N, d, block))
 
@@ -145,6 +151,7 @@ def quantize_outputs(B, H, N, d, device="cuda"):
         Vq=torch.empty((B, H, nb, d, BLOCK), dtype=torch.uint8, **kw), sV=torch.empty((B, H, d), dtype=torch.float32, **kw),
         mu=torch.empty((B, H, nb, d), dtype=torch.bfloat16, **kw),
         mu_scaled=torch.empty((B, H, nb, d), dtype=torch.float32, **kw),
+        mu_pack=torch.empty((B, H, (nb + 7) // 8, d // 16, 64, 8), dtype=torch.bfloat16, **kw),
     )
 
 
@@ -160,7 +167,8 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK):
         ws = workspace(need, Q.device)
     st = lib().vc_quantize(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, int(block), int(flags),
                            _ptr(out["Qq"]), _ptr(out["sQ"]), _ptr(out["Kq"]), _ptr(out["sK"]), _ptr(out["Vq"]),
-                           _ptr(out["sV"]), _ptr(out.get("mu")), _ptr(out.get("mu_scaled")), _ptr(ws), ws.numel(),
+                           _ptr(out["sV"]), _ptr(out.get("mu")), _ptr(out.get("mu_scaled")), _ptr(out.get("mu_pack")),
+                           _ptr(ws), ws.numel(),
                            _stream(stream))
     _check(st)
     return out
@@ -169,7 +177,7 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK):
 def vc_attention(q, O, beta=-0.35, flags=VC_F_EXPCAST, restore_mean=True, stream=None, block=BLOCK):
     """Attention over the quantised tensors `q` (dict from vc_quantize); O bf16 [B,H,N,d]."""
     B, H, N, d = _dims(O)
-    mu = q["mu_scaled"] if restore_mean else None
+    mu = q["mu_pack"] if restore_mean else None
     st = lib().vc_attention(_ptr(q["Qq"]), _ptr(q["sQ"]), _ptr(q["Kq"]), _ptr(q["sK"]), _ptr(q["Vq"]), _ptr(q["sV"]),
                             _ptr(mu), B, H, N, d, int(block), float(beta), int(flags), _ptr(O), _stream(stream))
     _check(st)
@@ -180,7 +188,7 @@ def vc_attention_dump(q, O, dump_block, codes, beta=-0.35, flags=VC_F_EXPCAST, r
                       block=BLOCK):
     B, H, N, d = _dims(O)
     _need(codes, torch.uint8, (B, H, N, BLOCK), "codes")
-    mu = q["mu_scaled"] if restore_mean else None
+    mu = q["mu_pack"] if restore_mean else None
     st = lib().vc_attention_dump(_ptr(q["Qq"]), _ptr(q["sQ"]), _ptr(q["Kq"]), _ptr(q["sK"]), _ptr(q["Vq"]),
                                  _ptr(q["sV"]), _ptr(mu), B, H, N, d, int(block), float(beta), int(flags), _ptr(O),
                                  int(dump_block), _ptr(codes), _stream(stream))

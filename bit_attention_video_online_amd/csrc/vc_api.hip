@@ -10,10 +10,11 @@
 
 extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
                                   int d, uint32_t flags, float cL, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* ws, hipStream_t st);
+                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* ws,
+                                  hipStream_t st);
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                                   const uint8_t* Vq, const float* sV, const float* mu, int B, int H, int N, int d,
+                                   const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
                                    float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
 extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
                                  hipStream_t st);
@@ -37,6 +38,10 @@ bool shape_ok(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (N % 128) != 0 || (d != 64 && d != 128)) return false;
   const long long el = (long long)B * H * N * d;
   return el < (1LL << 31);
+}
+size_t vc_mu_pack_bytes(int B, int H, int N, int d) {
+  const size_t nc = ((size_t)N / 128 + 7) / 8;
+  return (size_t)B * H * nc * (d / 16) * 64 * 8 * 2;
 }
 bool aligned16(const void* p) { return p == nullptr || (((uintptr_t)p) & 15u) == 0; }
 
@@ -92,6 +97,11 @@ extern "C" vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K
   return VC_OK;
 }
 
+extern "C" size_t vc_mu_pack_size(int B, int H, int N, int d) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  return vc_mu_pack_bytes(B, H, N, d);
+}
+
 extern "C" size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int block) {
   if (!shape_ok(B, H, N, d) || block != 128) return 0;
   return vc_quantize_ws_bytes(B, H, N, d);
@@ -99,13 +109,13 @@ extern "C" size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int bl
 
 extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
                                  int d, int block, uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                 uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* workspace,
+                                 uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || !workspace) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
   if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST)) return VC_E_PARAM;
   if (workspace_bytes < vc_quantize_ws_bytes(B, H, N, d)) return VC_E_WORKSPACE;
-  const void* ptrs[] = {Q, K, V, perm, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, workspace};
+  const void* ptrs[] = {Q, K, V, perm, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, mu_pack, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return VC_E_UNSUPPORTED;
   const size_t el = (size_t)B * H * N * d, nbk = (size_t)B * H * (N / 128);
@@ -113,54 +123,55 @@ extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, co
                        {(const char*)perm, (size_t)B * H * N * 4}};
   const Range outs[] = {{(const char*)Qq, el}, {(const char*)sQ, nbk * 4}, {(const char*)Kq, el},
                         {(const char*)sK, nbk * 4}, {(const char*)Vq, el}, {(const char*)sV, (size_t)B * H * d * 4},
-                        {(const char*)mu, nbk * d * 2}, {(const char*)mu_scaled, nbk * d * 4}};
+                        {(const char*)mu, nbk * d * 2}, {(const char*)mu_scaled, nbk * d * 4},
+                        {(const char*)mu_pack, vc_mu_pack_bytes(B, H, N, d)}};
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (vc_launch_quantize(Q, K, V, perm, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled,
-                         workspace, (hipStream_t)stream) != 0)
+                         mu_pack, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
 }
 
 static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                                  const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N, int d,
+                                  const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
                                   int block, float beta, uint32_t flags, void* O, int dump_block, uint8_t* codes,
                                   void* stream) {
   if (!Qq || !sQ || !Kq || !sK || !Vq || !sV || !O) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
   if (!isfinite(beta) || (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST))) return VC_E_PARAM;
-  const void* ptrs[] = {Qq, sQ, Kq, sK, Vq, sV, mu_scaled, O, codes};
+  const void* ptrs[] = {Qq, sQ, Kq, sK, Vq, sV, mu_pack, O, codes};
   for (const void* p : ptrs)
     if (!aligned16(p)) return VC_E_UNSUPPORTED;
   const size_t el = (size_t)B * H * N * d, nbk = (size_t)B * H * (N / 128);
   const Range ins[] = {{(const char*)Qq, el}, {(const char*)sQ, nbk * 4}, {(const char*)Kq, el},
                        {(const char*)sK, nbk * 4}, {(const char*)Vq, el}, {(const char*)sV, (size_t)B * H * d * 4},
-                       {(const char*)mu_scaled, nbk * d * 4}};
+                       {(const char*)mu_pack, vc_mu_pack_bytes(B, H, N, d)}};
   const Range outs[] = {{(const char*)O, el * 2}, {(const char*)codes, (size_t)B * H * N * 128}};
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
-  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, beta, (flags & VC_F_EXPCAST) ? 1 : 0,
+  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, (flags & VC_F_EXPCAST) ? 1 : 0,
                           (uint16_t*)O, dump_block, codes, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
 }
 
 extern "C" vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                                  const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N, int d,
+                                  const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
                                   int block, float beta, uint32_t flags, void* O, void* stream) {
-  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, block, beta, flags, O, -1, nullptr, stream);
+  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, block, beta, flags, O, -1, nullptr, stream);
 }
 
 extern "C" vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                                       const uint8_t* Vq, const float* sV, const float* mu_scaled, int B, int H, int N,
+                                       const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N,
                                        int d, int block, float beta, uint32_t flags, void* O, int dump_block,
                                        uint8_t* codes, void* stream) {
   if (!codes) return VC_E_NULLPTR;
   if (N >= 128 && (dump_block < 0 || dump_block >= N / 128)) return VC_E_PARAM;
-  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_scaled, B, H, N, d, block, beta, flags, O, dump_block, codes,
+  return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, block, beta, flags, O, dump_block, codes,
                           stream);
 }
 

@@ -21,7 +21,8 @@
 //   bytes: one more MFMA with an all-ones A operand (every output row is the sum).
 //   O^T (d x queries) += V_j^T P^T with the same instruction (K = 128 keys); V
 //   codes arrive block-transposed ([d][128]) so the A operand is contiguous.
-//   Mean restoration: O^T[c][q] += r_q * mu_scaled_j[c] (one FMA per accumulator).
+//   Mean restoration: O^T[c][q] += r_q * mu~_j[c], accumulated on the matrix core once
+//   per 8 key blocks (bf16 hi/lo split, see flush below).
 // K and V tiles are copied global -> LDS directly (global_load_lds_dwordx4) into a
 // two-stage buffer with a 16-byte XOR swizzle that keeps the ds_read_b128 operand
 // fetches free of bank conflicts; tile j+1 lands while tile j is consumed, with one
@@ -71,6 +72,7 @@ __device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // 16-byte global -> LDS copy (global_load_lds_dwordx4): lane L of the wave writes
 // LDS[base + 16 L]. The builtin exists only for the device pass; seen by the host pass
@@ -85,7 +87,7 @@ template <int D, bool EXPCAST, bool RESTORE, bool DUMP>
 __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
                                                          const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
                                                          const uint8_t* __restrict__ Vq, const float* __restrict__ sV,
-                                                         const float* __restrict__ mu_scaled, int N, int total,
+                                                         const uint16_t* __restrict__ mu_pack, int N, int total,
                                                          float C0, uint16_t* __restrict__ O, int dump_block,
                                                          uint8_t* __restrict__ dump) {
   constexpr int TILE = kBlock * D;              // bytes per K (or V) tile
@@ -93,8 +95,11 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   constexpr int PW = NCH / kAThreads;           // chunks per thread per tile (4 or 2)
   constexpr int DB = D / 16;                    // 16-row d blocks
   constexpr int CPR = D / 16;                   // 16-byte chunks per K row
-  constexpr int BUF = 2 * TILE + 4 * D;         // one stage: K tile | V tile | mu row
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+  constexpr int BUF = 2 * TILE;                 // one stage: K tile | V tile
+  constexpr int PACK = DB * 64 * 16;            // mean operand of one chunk of 8 key blocks
+  constexpr int RLOG = 4 * 2 * 16 * 8 * 8;      // per wave, group, query, slot: (r, m') floats
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF + (RESTORE ? PACK + RLOG : 16)];
+  uint8_t* const packs = smem + 2 * BUF;
 
   const int nb = N / kBlock;
   const int logical = xcd_remap(blockIdx.x, total);
@@ -104,7 +109,8 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
 
   const uint8_t* Kh = Kq + (size_t)bh * N * D;
   const uint8_t* Vh = Vq + (size_t)bh * N * D;
-  const float* muh = mu_scaled + (size_t)bh * nb * D;
+  const int nchunk = (nb + 7) / 8;
+  const uint16_t* packh = RESTORE ? mu_pack + (size_t)bh * nchunk * DB * 64 * 8 : nullptr;
   const float sq = sQ[(size_t)bh * nb + qb];
 
   // ---- Q fragments (B operand of S^T): query row, bytes [32*lg, 32*lg+32)
@@ -141,8 +147,12 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
       g2lds16(kt + ksrc[i], (lds_void*)(sb + (wave * 64 + kAThreads * i) * 16));
       g2lds16(vt + vsrc[i], (lds_void*)(sb + TILE + (wave * 64 + kAThreads * i) * 16));
     }
-    if (RESTORE && wave == 0 && lane < D / 4)
-      g2lds16(muh + (size_t)j * D + lane * 4, (lds_void*)(sb + 2 * TILE));
+  };
+  // mean operand of chunk c (8 key blocks): DB d-blocks x 64 lanes x 16 bytes, one
+  // d-block per wave per round
+  auto issue_pack = [&](int c) {
+    for (int db = wave; db < DB; db += 4)
+      g2lds16(packh + (((size_t)c * DB + db) * 64 + lane) * 8, (lds_void*)(packs + db * 1024));
   };
 
   // fixed per-lane fragment offsets (bytes, within a stage)
@@ -157,13 +167,45 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     for (int g = 0; g < 2; g++) oacc[db][g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Mean restoration on the matrix core: each key block's row sum r_j is logged with the
+  // running max m'_j it is scaled to; once per 8 key blocks the logged sums are brought
+  // to the current max, w = r_j 2^(m'_j - m'), and folded in with one
+  // v_mfma_f32_16x16x32_bf16 per d-block: O^T[c][q] += sum_s mu~_s[c] w_s[q], with mu~
+  // and w split into bf16 hi + lo (mu_hi w_hi + mu_hi w_lo + mu_lo w_hi).
+  // Log layout [wave][g][query r16][slot]: one lane's eight slots are 64 contiguous bytes.
+  float2* const rlog = reinterpret_cast<float2*>(packs + PACK) + wave * 2 * 16 * 8;
+  auto flush = [&](int nvalid) {
+    bf16x8 wb[2];
+    for (int g = 0; g < 2; g++) {
+      const float4* src = reinterpret_cast<const float4*>(rlog + (g * 16 + r16) * 8);
+      float rv[8], mv[8];
+      for (int k = 0; k < 4; k++) {
+        const float4 t = src[k];
+        rv[2 * k] = t.x; mv[2 * k] = t.y; rv[2 * k + 1] = t.z; mv[2 * k + 1] = t.w;
+      }
+      for (int k = 0; k < 8; k++) {
+        const float w = k < nvalid ? rv[k] * __builtin_amdgcn_exp2f(mv[k] - m[g]) : 0.0f;
+        const __bf16 hi = (__bf16)w;
+        const __bf16 lo = (__bf16)(w - (float)hi);
+        wb[g][k] = lg == 1 ? lo : (lg == 3 ? (__bf16)0.0f : hi);
+      }
+    }
+    for (int db = 0; db < DB; db++) {
+      bf16x8 a;
+      __builtin_memcpy(&a, packs + db * 1024 + lane * 16, 16);
+      for (int g = 0; g < 2; g++) oacc[db][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[g], oacc[db][g], 0, 0, 0);
+    }
+  };
+
   issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int j = 0; j < nb; j++) {
     const uint8_t* sb = smem + (j & 1) * BUF;
+    if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
     if (j + 1 < nb) issue(j + 1, (j + 1) & 1);
+    if (RESTORE && (((j + 1) & 7) == 0 || j + 1 == nb)) issue_pack(j >> 3);
 
     // ---- S^T = K_j Q^T  (MFMA kb covers key rows krow0 + 4*kb)
     v4f sacc[8][2];
@@ -231,9 +273,9 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
       }
       rsum[g] = r;
       lsum[g] = __builtin_fmaf(alpha, lsum[g], r);
-      if (__ballot(alpha != 1.0f)) {
+      if (__ballot(alpha != 1.0f))
         for (int db = 0; db < DB; db++) oacc[db][g] *= alpha;
-      }
+      if (RESTORE && lg == 0) rlog[(g * 16 + r16) * 8 + (j & 7)] = make_float2(r, mp);
       m[g] = mp;
       if (DUMP && j == dump_block) {
         const int q = qb * kBlock + wave * 32 + g * 16 + r16;
@@ -249,23 +291,13 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
       for (int g = 0; g < 2; g++)
         oacc[db][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf[g], oacc[db][g], 0, 0, 0, 0, 0, 0);
     }
-    if (RESTORE) {
-      const float* mus = reinterpret_cast<const float*>(sb + 2 * TILE);
-      for (int db = 0; db < DB; db++) {
-        const float4 mu4 = *reinterpret_cast<const float4*>(mus + 16 * db + 4 * lg);
-        for (int g = 0; g < 2; g++) {
-          oacc[db][g][0] = __builtin_fmaf(rsum[g], mu4.x, oacc[db][g][0]);
-          oacc[db][g][1] = __builtin_fmaf(rsum[g], mu4.y, oacc[db][g][1]);
-          oacc[db][g][2] = __builtin_fmaf(rsum[g], mu4.z, oacc[db][g][2]);
-          oacc[db][g][3] = __builtin_fmaf(rsum[g], mu4.w, oacc[db][g][3]);
-        }
-      }
-    }
     // next stage landed (its loads were issued at the top of this iteration) and every
     // wave is done with this stage before it is refilled
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+
+  if (RESTORE) flush(nb - ((nb - 1) & ~7));  // last chunk: slots past the final key block are zero
 
   // ---- epilogue: O = bf16(sV * A / l), rows in original order
   for (int g = 0; g < 2; g++) {
@@ -290,7 +322,7 @@ __global__ void expcast_kernel(const float* __restrict__ acc, const float* __res
 
 template <int D, bool E, bool R, bool DU>
 static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
-                        const float* sV, const float* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
+                        const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                         uint8_t* dump, hipStream_t st) {
   const int total = BH * (N / kBlock);
   attn_fwd<D, E, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
@@ -298,7 +330,7 @@ static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, c
 
 template <int D, bool E, bool R>
 static void launch_attn_d(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
-                          const float* sV, const float* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
+                          const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                           uint8_t* dump, hipStream_t st) {
   if (dump) launch_attn<D, E, R, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
   else launch_attn<D, E, R, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
@@ -309,8 +341,9 @@ static void launch_attn_d(const uint8_t* Qq, const float* sQ, const uint8_t* Kq,
 using namespace vc;
 
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                                   const uint8_t* Vq, const float* sV, const float* mu, int B, int H, int N, int d,
+                                   const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
                                    float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
+  const uint16_t* mu = (const uint16_t*)mu_pack;
   const int BH = B * H;
   const float C0 = 120.0f + beta;  // fl32(120 + beta)
   const bool R = mu != nullptr;

@@ -171,7 +171,8 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
                                                          const float* __restrict__ kbar, const float* __restrict__ sV,
                                                          const float* __restrict__ vinv, const uint16_t* __restrict__ mu,
                                                          uint8_t* __restrict__ Kq, float* __restrict__ sK,
-                                                         uint8_t* __restrict__ Vq, float* __restrict__ mu_scaled) {
+                                                         uint8_t* __restrict__ Vq, float* __restrict__ mu_scaled,
+                                                         uint16_t* __restrict__ mu_pack) {
   __shared__ float tile[kBlock * D];
   __shared__ float red[4];
   __shared__ uint8_t codes[D * kBlock];
@@ -206,7 +207,26 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
     float rr = tile[r * D + c] - m;
     codes[c * kBlock + r] = (uint8_t)e4m3_from_f32(rr * inv);
   }
-  if (g == 0 && mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
+  const float ms = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
+  if (g == 0 && mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = ms;
+  if (g == 0 && mu_pack) {
+    // mean-restoration operand, laid out as the A operand of v_mfma_f32_16x16x32_bf16:
+    // [chunk of 8 key blocks][d-block][lane][8]: lanes 0-31 hold bf16(ms), lanes 32-47
+    // bf16(ms - bf16(ms)), lanes 48-63 zero; element s belongs to key block 8*chunk + s.
+    const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 16, r = c % 16;
+    const uint16_t hi = f32_to_bf16(ms);
+    const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
+    uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 16) + db) * 64) * 8;
+    base[(r) * 8 + s8] = hi;
+    base[(16 + r) * 8 + s8] = hi;
+    base[(32 + r) * 8 + s8] = lo;
+    base[(48 + r) * 8 + s8] = 0;
+    if (j == nb - 1) {  // key blocks past the end of the last chunk contribute nothing
+      for (int t = s8 + 1; t < 8; t++) {
+        base[(r) * 8 + t] = 0; base[(16 + r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(48 + r) * 8 + t] = 0;
+      }
+    }
+  }
   __syncthreads();
   // contiguous copy-out of the D x 128 byte tile
   uint4* dst = reinterpret_cast<uint4*>(Vq + head + jrow);
@@ -220,7 +240,8 @@ using namespace vc;
 
 extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
                                   int d, uint32_t flags, float cL, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* ws, hipStream_t st) {
+                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* ws,
+                                  hipStream_t st) {
   const int nb = N / kBlock, BH = B * H;
   // workspace: ksum double [BH,nb,d] | vamax float [BH,nb,d] | kbar float [BH,d] | vinv float [BH,d] | mu (if caller's NULL)
   char* w = (char*)ws;
@@ -236,13 +257,13 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
                                                 Qq, sQ, mup, ksum, vamax);
     quant_reduce<128><<<BH, 128, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
     quant_apply<128><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
-                                                Kq, sK, Vq, mu_scaled);
+                                                Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
   } else {
     quant_stats<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, N, flags, cL,
                                                Qq, sQ, mup, ksum, vamax);
     quant_reduce<64><<<BH, 64, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
     quant_apply<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
-                                               Kq, sK, Vq, mu_scaled);
+                                               Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

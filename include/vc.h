@@ -62,7 +62,7 @@ const char* vc_status_string(vc_status s);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int vc_abi_version(void);
-#define VC_ABI_VERSION 1
+#define VC_ABI_VERSION 2
 
 /* ------------------------------------------------------------------------
  * vc_cluster -- online k-means on value tokens (paper page, method step (1)):
@@ -82,11 +82,12 @@ int vc_abi_version(void);
  *   perm       int32 [B,H,N]    out: stable argsort of labels (ties by token index)
  *   workspace  >= vc_cluster_workspace_bytes(B,H,N,d,K) bytes of device memory
  *
- * Scores: the assignment kernel ranks clusters in binary32 with a rigorous error
- * bound and re-ranks every token whose best two candidates are within that bound
- * in binary64, so labels equal the exact argmin whenever the binary64 squared
- * distances are themselves exact (always, for values whose per-token exponent
- * span is below 2^18).
+ * Scores: the assignment kernel ranks clusters from bf16 matrix-core dot products
+ * (exact products; accumulation error measured far inside the binary32 bound the
+ * test uses), keeps a rigorous per-distance error bound, and re-ranks in binary64
+ * every token whose best candidate is not separated from the rest by the bounds, so
+ * labels equal the exact argmin whenever the binary64 squared distances are exact
+ * (always, for values whose per-token exponent span is below 2^18).
  * ------------------------------------------------------------------------ */
 size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K);
 vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
@@ -109,18 +110,25 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
  *                                  Vq[b,h,j,c,t] = code of R[128j+t, c], R = V[perm] - mu
  *   sV   float [B,H,d]             per-channel residual scale (over all N tokens)
  *   mu   bf16 [B,H,N/128,d]        block means of V' (zero when !VC_F_VSMOOTH); may be NULL
- *   mu_scaled float [B,H,N/128,d]  fl32(mu / sV), consumed by vc_attention
+ *   mu_scaled float [B,H,N/128,d]  fl32(mu / sV); may be NULL
+ *   mu_pack  bf16, vc_mu_pack_size(B,H,N,d) bytes: mu_scaled in the operand layout that
+ *            vc_attention consumes, [B,H,ceil(N/1024),d/16,64,8]: for chunk c of 8 key
+ *            blocks, 16-channel group b, lane l and element s (key block 8c+s): lanes
+ *            0..31 hold bf16(mu_scaled), lanes 32..47 bf16(mu_scaled - bf16(mu_scaled)),
+ *            lanes 48..63 zero, always of channel 16b + (l mod 16); key blocks past
+ *            N/128 are zero. May be NULL.
  * Arithmetic: block and channel scales are fl32(amax/448) with codes
  * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
  * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).
  * workspace >= vc_quantize_workspace_bytes(B,H,N,d,block).
  * ------------------------------------------------------------------------ */
 size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int block);
+size_t vc_mu_pack_size(int B, int H, int N, int d); /* bytes of mu_pack (0 if the shape is invalid) */
 vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm,
                       int B, int H, int N, int d, int block, uint32_t flags,
                       uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
-                      void* mu, float* mu_scaled, void* workspace, size_t workspace_bytes,
-                      void* stream);
+                      void* mu, float* mu_scaled, void* mu_pack, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * vc_attention -- non-causal attention over the quantised tensors (paper page,
@@ -132,15 +140,17 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
  *   VC_F_EXPCAST: c = clamp(rne(fma(S, 8 sigma, fl32(fl32(120 + beta) - 8 m'))), 0, 120)
  *   otherwise:    c = e4m3(256 * exp2(fl32(sigma S) - m')),
  *   r = row sum of the probabilities, l = 2^(m - m') l + r,
- *   A = 2^(m - m') A + c . Vq_j + r * mu_scaled_j   (mu term only if mu_scaled != NULL),
- * and finally O_i = bf16(sV * A / l), rows in original token order.
+ *   A = 2^(m - m') A + c . Vq_j + r * mu_scaled_j   (mu term only if mu_pack != NULL),
+ * and finally O_i = bf16(sV * A / l), rows in original token order. The r * mu term is
+ * accumulated once per 8 key blocks from the bf16 hi/lo mu_pack operand (relative
+ * error ~2^-16 of that term).
  *
  *   O      bf16 [B,H,N,d] output; must not overlap any input
  *   beta   finite; the pages use -0.35
  *   flags  VC_F_EXPCAST selects ExpCast; other bits ignored
  * ------------------------------------------------------------------------ */
 vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                       const uint8_t* Vq, const float* sV, const float* mu_scaled,
+                       const uint8_t* Vq, const float* sV, const void* mu_pack,
                        int B, int H, int N, int d, int block, float beta, uint32_t flags,
                        void* O, void* stream);
 
@@ -148,7 +158,7 @@ vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
  * `dump_block` received from every query: codes uint8 [B,H,N,128] (key order of
  * the block). Test support for in-kernel byte parity. */
 vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
-                            const uint8_t* Vq, const float* sV, const float* mu_scaled,
+                            const uint8_t* Vq, const float* sV, const void* mu_pack,
                             int B, int H, int N, int d, int block, float beta, uint32_t flags,
                             void* O, int dump_block, uint8_t* codes, void* stream);
 

@@ -33,6 +33,27 @@ def vq_rowmajor(Vq: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(Vq.transpose(0, 1, 2, 4, 3).reshape(B, H, nb * T, d))
 
 
+def mu_pack_expected(mu_scaled: np.ndarray) -> np.ndarray:
+    """Layout of vc_quantize's mu_pack output derived from [nb, d] float32 scaled means:
+    [ceil(nb/8), d/16, 64, 8] bf16 bits (lanes 0-31 hi, 32-47 lo, 48-63 zero)."""
+    import synth
+    nb, d = mu_scaled.shape
+    nc = (nb + 7) // 8
+    ms = np.zeros((nc * 8, d), np.float32)
+    ms[:nb] = mu_scaled
+    hi = synth.bf16_bits(ms)
+    lo = synth.bf16_bits((ms - synth.bf16_to_f32(hi)).astype(np.float32))
+    out = np.zeros((nc, d // 16, 64, 8), np.uint16)
+    for c in range(nc):
+        for b in range(d // 16):
+            for r in range(16):
+                ch = 16 * b + r
+                out[c, b, r] = hi[8 * c:8 * c + 8, ch]
+                out[c, b, 16 + r] = hi[8 * c:8 * c + 8, ch]
+                out[c, b, 32 + r] = lo[8 * c:8 * c + 8, ch]
+    return out
+
+
 def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings_and_version(L):
-    assert L.vc_abi_version() == 1
+    assert L.vc_abi_version() == 2
     for s in range(8):
         assert vc.vc_status_string(s).startswith(("VC_OK", "VC_E_"))
     assert vc.vc_status_string(99) == "unknown vc_status"
@@ -46,11 +46,13 @@ def _quant(L, **kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, perm=None, B=1, H=1, N=256, d=128, block=128, flags=3,
              Qq=ctypes.c_void_p(1 << 20), sQ=ctypes.c_void_p(2 << 20), Kq=ctypes.c_void_p(3 << 20),
              sK=ctypes.c_void_p(4 << 20), Vq=ctypes.c_void_p(5 << 20), sV=ctypes.c_void_p(6 << 20),
-             mu=ctypes.c_void_p(7 << 20), mus=ctypes.c_void_p(8 << 20), ws=ctypes.c_void_p(9 << 20),
+             mu=ctypes.c_void_p(7 << 20), mus=ctypes.c_void_p(8 << 20), mup=ctypes.c_void_p(10 << 20),
+             ws=ctypes.c_void_p(9 << 20),
              wsb=1 << 30, st=None)
     a.update(kw)
     return L.vc_quantize(a["Q"], a["K"], a["V"], a["perm"], a["B"], a["H"], a["N"], a["d"], a["block"], a["flags"],
-                         a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"], a["mus"], a["ws"], a["wsb"],
+                         a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"], a["mus"], a["mup"], a["ws"],
+                         a["wsb"],
                          a["st"])
 
 

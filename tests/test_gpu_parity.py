@@ -18,7 +18,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 vc = pytest.importorskip("bit_attention_video_online_amd")
-from tests.gpu_util import bf16_bits, gpu_quantize, rel_l2, to_dev, to_dev_bf16, vq_rowmajor  # noqa: E402
+from tests.gpu_util import bf16_bits, gpu_quantize, mu_pack_expected, rel_l2, to_dev, to_dev_bf16, vq_rowmajor  # noqa: E402
 
 BETA = -0.35
 FLAGS_ALL = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
@@ -66,6 +66,7 @@ def _compare_quant(out, q_or, b, h, vsmooth):
     assert np.array_equal(g["mu_scaled"][b, h], q_or["mu_scaled"])
     if vsmooth:
         assert np.array_equal(bf16_bits(out["mu"])[b, h], q_or["mu"])
+    assert np.array_equal(g["mu_pack"][b, h], mu_pack_expected(q_or["mu_scaled"]))
 
 
 @pytest.mark.parametrize("flags", [FLAGS_ALL, vc.VC_F_KSMOOTH, vc.VC_F_VSMOOTH, 0])

@@ -19,7 +19,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 vc = pytest.importorskip("bit_attention_video_online_amd")
-from tests.gpu_util import bf16_bits, rel_l2, to_dev_bf16, vq_rowmajor  # noqa: E402
+from tests.gpu_util import bf16_bits, mu_pack_expected, rel_l2, to_dev_bf16, vq_rowmajor  # noqa: E402
 
 HEADS = (0, 23)
 KC = 550
@@ -106,6 +106,7 @@ def test_wan_quantize_bitexact_sampled_heads(run, oracle_heads):
         assert np.array_equal(g["sV"][0, h], o["sV"])
         assert np.array_equal(g["mu"][0, h], o["mu"])
         assert np.array_equal(g["mu_scaled"][0, h], o["mu_scaled"])
+        assert np.array_equal(g["mu_pack"][0, h], mu_pack_expected(o["mu_scaled"]))
 
 
 def test_wan_attention_sampled_rows(run, oracle_heads):
