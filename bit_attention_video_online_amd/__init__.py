@@ -151,7 +151,7 @@ def quantize_outputs(B, H, N, d, device="cuda"):
         Vq=torch.empty((B, H, nb, d, BLOCK), dtype=torch.uint8, **kw), sV=torch.empty((B, H, d), dtype=torch.float32, **kw),
         mu=torch.empty((B, H, nb, d), dtype=torch.bfloat16, **kw),
         mu_scaled=torch.empty((B, H, nb, d), dtype=torch.float32, **kw),
-        mu_pack=torch.empty((B, H, (nb + 7) // 8, d // 16, 64, 8), dtype=torch.bfloat16, **kw),
+        mu_pack=torch.empty((B, H, (nb + 7) // 8, d // 32, 2, 64, 8), dtype=torch.bfloat16, **kw),
     )
 
 

@@ -3,64 +3,51 @@
 // Paper page (paper.rainbus.top), method steps (3) and (4); study notes 2-3, 2-4;
 // online-softmax prerequisite. Non-causal; every query sees all keys.
 //
-// Work decomposition: one work-group = 4 waves = 128 query rows of one (b,h);
-// each wave owns 32 rows as two 16-row groups. The key loop walks the 128-key
-// blocks in ascending order (ExpCast bytes depend on the running maximum, so the
-// loop is never split or reordered).
-//
-// Per key block, per wave:
-//   S^T (keys x queries) = K_j Q^T with v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3,
-//   binary32 accumulate, one instruction covers d = 128). MFMA kb (0..7) takes the
-//   key rows kappa(kb, r) = 32*(r/4) + 4*kb + (r%4), so lane group g = lane/16 holds
-//   keys 32*g + 4*kb + i (i = 0..3) of its query: exactly the 32 K-slots that the
-//   PV MFMA's B operand expects from that lane in natural key order. The
-//   probability bytes therefore never leave the lane: the four accumulators of
-//   MFMA kb become dword kb of the B operand.
-//   Row max over a query's 128 keys: 32 values in-lane, then the four lane groups are
-//   combined with v_permlane16_swap and v_permlane32_swap. Row sum of the ExpCast
-//   bytes: one more MFMA with an all-ones A operand (every output row is the sum).
-//   O^T (d x queries) += V_j^T P^T with the same instruction (K = 128 keys); V
-//   codes arrive block-transposed ([d][128]) so the A operand is contiguous.
-//   Mean restoration: O^T[c][q] += r_q * mu~_j[c], accumulated on the matrix core once
-//   per 8 key blocks (bf16 hi/lo split, see flush below).
-// K and V tiles are copied global -> LDS directly (global_load_lds_dwordx4) into a
-// two-stage buffer with a 16-byte XOR swizzle that keeps the ds_read_b128 operand
-// fetches free of bank conflicts; tile j+1 lands while tile j is consumed, with one
-// barrier per tile.
+// Work decomposition: one work-group = 4 waves = 128 query rows of one (b,h), 32 rows
+// per wave, two work-groups per CU (the kernel below documents the per-block steps).
+// Design notes for gfx950, all measured on the device:
+//   - a wave issues at most one VALU instruction every ~9 cycles, two waves on a SIMD
+//     reach ~4 cycles, so every SIMD keeps two waves that both carry softmax work;
+//   - an FP8 MFMA blocks the SIMD's VALU issue for most of its duration; the 32x32x64
+//     shape does twice the work of 16x16x128 for ~1.4x the blocking, so it is used for
+//     S, PV and the row sums;
+//   - K and V tiles are copied global -> LDS with buffer_load ... lds (scalar-addressed,
+//     no per-lane address arithmetic) into a two-stage buffer; tile j+1 lands while
+//     tile j is consumed, with one barrier per tile.
 #include "vc_device.h"
 
 namespace vc {
 
-constexpr int kAThreads = 256;
+constexpr int kAThreads = 256;  // 4 waves; two work-groups per CU
 
-__device__ __forceinline__ float lane_max4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+// lanes l and l^32 hold the same query: combine them with one v_permlane32_swap
+__device__ __forceinline__ float lane_max2(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float lane_sum4(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+__device__ __forceinline__ float lane_sum2(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// LDS swizzles (16-byte chunk index XOR). K tile rows are D bytes; the XOR pattern
-// uses only row bits that the per-MFMA key offset (+4*kb rows) leaves untouched, so a
-// lane's eight K fragments sit at one base plus immediates. V tile rows are 128 bytes;
-// the pattern uses row bits 1..3, untouched by the +16*db row offset.
+// LDS swizzles (16-byte chunk index XOR). gfx950 serves a wave's ds_read_b128 in four
+// passes of 16 lanes, pass = (lane/16) xor parity(lane bits 2, 3), i.e. four interleaved
+// lane quads; a pass is conflict-free when its 16 lanes hit distinct 16-byte slots modulo
+// 256 bytes (64 banks). The XOR patterns below satisfy that for every fragment read.
+// K tile rows are D bytes; the pattern uses row bits 1..3 (d = 128) or 2..3 (d = 64),
+// which the per-MFMA key offsets (+16, +64, +80 rows) leave untouched, so a lane's K
+// fragments sit at one base plus immediates. V tile rows are 128 bytes; the pattern uses
+// row bits 1..3, untouched by the +32*db row offset.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (((row >> 1) & 1) | (((row >> 5) & 1) << 1)) : ((row >> 5) & 1);
+  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int k_off(int row, int chunk) {
   return row * D + ((chunk ^ k_swz<D>(row)) << 4);
 }
-__device__ __forceinline__ int v_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
+__device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int v_off(int row, int chunk) { return row * 128 + ((chunk ^ v_swz(row)) << 4); }
 
 __device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
   uint4 a = *reinterpret_cast<const uint4*>(p0);
@@ -83,6 +70,58 @@ __device__ __forceinline__ void g2lds16(const void* src, lds_void* dst_wave_base
 #endif
 }
 
+// Buffer resource for a wave-uniform base pointer (forced into SGPRs with readfirstlane,
+// so copies need no per-lane descriptor) and a record limit in bytes: an offset past the
+// limit reads zeros instead of faulting. The host pass only sees a placeholder type.
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#else
+struct rsrc_t { int w[4]; };
+#endif
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, nbytes, 0x00020000);
+#else
+  (void)base; (void)nbytes;
+  return rsrc_t{};
+#endif
+}
+// 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane L of the wave writes
+// LDS[base + 16 L] from the resource at voff + soff. Device pass only (see g2lds16).
+__device__ __forceinline__ void buf2lds16(rsrc_t r, int voff, int soff, lds_void* dst_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst_wave_base, 16, voff, soff, 0, 0);
+#else
+  (void)r; (void)voff; (void)soff; (void)dst_wave_base;
+#endif
+}
+
+// Work-group barrier without a memory fence: LDS tiles are only written by the
+// asynchronous copies, whose completion the loop waits for explicitly, and every wave
+// has consumed the fragments it read before it arrives (the MFMAs that use them are
+// issued first). The clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One work-group = 4 waves = 128 query rows of one (b,h), 32 rows per wave; two
+// work-groups per CU, so every SIMD runs two waves whose vector-ALU work interleaves with
+// the other's matrix-core work. The key loop walks the 128-key blocks in ascending order
+// (ExpCast bytes depend on the running maximum, so the loop is never split or reordered).
+//
+// Per key block, per wave (32 queries = one 32x32 MFMA column block):
+//   S^T (keys x queries) = K_j Q^T with v_mfma_f32_32x32x64_f8f6f4: MFMA kb (0..3) per
+//   64-wide d half takes the key rows kappa(kb, r) = 64(kb>>1) + 32((r>>2)&1) + 16(kb&1)
+//   + 4(r>>3) + (r&3), so accumulator element i of lane l holds key 64(kb>>1) + 32(l/32)
+//   + 16(kb&1) + i of query l%32: exactly byte 16(kb&1)+i of the PV B operand that lane
+//   supplies for the 64-key half kb>>1. The probability bytes never leave the lane.
+//   Row max: 64 values in-lane, then lanes l and l^32 combine (v_permlane32_swap).
+//   Row sum of the ExpCast bytes: two MFMAs with an all-ones A operand.
+//   O^T (d x queries) += V_j^T P^T with the same instruction (K = 64 keys per half).
+//   Mean restoration: O^T[c][q] += r_q mu~_j[c], accumulated on the matrix core once
+//   per 8 key blocks (bf16 hi/lo split, v_mfma_f32_32x32x16_bf16).
 template <int D, bool EXPCAST, bool RESTORE, bool DUMP>
 __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
                                                          const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
@@ -93,225 +132,251 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   constexpr int TILE = kBlock * D;              // bytes per K (or V) tile
   constexpr int NCH = TILE / 16;                // 16-byte chunks per tile
   constexpr int PW = NCH / kAThreads;           // chunks per thread per tile (4 or 2)
-  constexpr int DB = D / 16;                    // 16-row d blocks
+  constexpr int NDB = D / 32;                   // 32-channel blocks of O
+  constexpr int NDH = D / 64;                   // 64-wide d halves of the S contraction
   constexpr int CPR = D / 16;                   // 16-byte chunks per K row
-  constexpr int BUF = 2 * TILE;                 // one stage: K tile | V tile
-  constexpr int PACK = DB * 64 * 16;            // mean operand of one chunk of 8 key blocks
-  constexpr int RLOG = 4 * 2 * 16 * 8 * 8;      // per wave, group, query, slot: (r, m') floats
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF + (RESTORE ? PACK + RLOG : 16)];
-  uint8_t* const packs = smem + 2 * BUF;
+  constexpr int PACK = NDB * 2 * 64 * 16;       // mean operand of one chunk of 8 key blocks
+  constexpr int RLOG = 4 * 8 * 32 * 8;          // waves x slots x queries x (r, m')
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE + (RESTORE ? PACK + RLOG : 16)];
+  uint8_t* const kbuf = smem;                   // [2][TILE], K_j in stage j & 1
+  uint8_t* const vbuf = smem + 2 * TILE;        // [2][TILE], V_j in stage j & 1
+  uint8_t* const packs = smem + 4 * TILE;       // [PACK], mean operand of the current chunk
 
   const int nb = N / kBlock;
   const int logical = xcd_remap(blockIdx.x, total);
   const int bh = logical / nb, qb = logical % nb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int q = qb * kBlock + wave * 32 + r32;  // this lane's query row
 
   const uint8_t* Kh = Kq + (size_t)bh * N * D;
   const uint8_t* Vh = Vq + (size_t)bh * N * D;
   const int nchunk = (nb + 7) / 8;
-  const uint16_t* packh = RESTORE ? mu_pack + (size_t)bh * nchunk * DB * 64 * 8 : nullptr;
   const float sq = sQ[(size_t)bh * nb + qb];
+  const float* sKh = sK + (size_t)bh * nb;
 
-  // ---- Q fragments (B operand of S^T): query row, bytes [32*lg, 32*lg+32)
-  v8i qf[2];
-  for (int g = 0; g < 2; g++) {
-    const int q = qb * kBlock + wave * 32 + g * 16 + r16;
-    if (D == 128 || lg < 2) {
-      const uint4* src = reinterpret_cast<const uint4*>(Qq + ((size_t)bh * N + q) * D + 32 * lg);
-      uint4 a = src[0], b = src[1];
-      qf[g][0] = a.x; qf[g][1] = a.y; qf[g][2] = a.z; qf[g][3] = a.w;
-      qf[g][4] = b.x; qf[g][5] = b.y; qf[g][6] = b.z; qf[g][7] = b.w;
-    } else {
-      for (int k = 0; k < 8; k++) qf[g][k] = 0;
-    }
+  // ---- Q fragments (B operand of S^T): query row, bytes [64 dh + 32 h, +32)
+  v8i qf[NDH];
+  for (int dh = 0; dh < NDH; dh++) {
+    const uint4* src = reinterpret_cast<const uint4*>(Qq + ((size_t)bh * N + q) * D + 64 * dh + 32 * h);
+    uint4 a = src[0], b = src[1];
+    qf[dh][0] = a.x; qf[dh][1] = a.y; qf[dh][2] = a.z; qf[dh][3] = a.w;
+    qf[dh][4] = b.x; qf[dh][5] = b.y; qf[dh][6] = b.z; qf[dh][7] = b.w;
   }
-  v8i ones;  // all-ones E4M3 (0x38 = 1.0): one MFMA turns the probability bytes into row sums
+  v8i ones;  // all-ones E4M3 (0x38 = 1.0): MFMAs with it turn probability bytes into row sums
   for (int k = 0; k < 8; k++) ones[k] = 0x38383838;
 
-  // ---- tile staging: global -> LDS directly (lane L of a wave fills LDS chunk base+L);
-  // the source of each chunk is chosen so that LDS ends up in the swizzled layout.
-  int ksrc[PW], vsrc[PW];
-  for (int i = 0; i < PW; i++) {
-    const int P = wave * 64 + lane + kAThreads * i;
+  // ---- tile copies (buffer -> LDS, lane L of a wave fills LDS chunk base+L). The source of
+  // each chunk is chosen so that LDS ends up in the swizzled layout; a thread's chunks i > 0
+  // sit 32 K rows (64 for d = 64) further on, which the swizzles ignore, so one per-lane
+  // offset serves all of them and the rest goes into the scalar offset.
+  const rsrc_t krs = make_rsrc(Kh, N * D), vrs = make_rsrc(Vh, N * D);
+  int ksrc, vsrc;
+  {
+    const int P = wave * 64 + lane;
     const int row = P / CPR, phys = P % CPR;
-    ksrc[i] = row * D + 16 * (phys ^ k_swz<D>(row));
+    ksrc = row * D + 16 * (phys ^ k_swz<D>(row));
     const int vrow = P >> 3, vphys = P & 7;
-    vsrc[i] = vrow * 128 + 16 * (vphys ^ ((vrow >> 1) & 7));
+    vsrc = vrow * 128 + 16 * (vphys ^ v_swz(vrow));
   }
-  auto issue = [&](int j, int stage) {
-    const uint8_t* kt = Kh + (size_t)j * TILE;
-    const uint8_t* vt = Vh + (size_t)j * TILE;
-    uint8_t* sb = smem + stage * BUF;
+  auto issue = [&](int j) {
+    uint8_t* kd = kbuf + (j & 1) * TILE;
+    uint8_t* vd = vbuf + (j & 1) * TILE;
     for (int i = 0; i < PW; i++) {
-      g2lds16(kt + ksrc[i], (lds_void*)(sb + (wave * 64 + kAThreads * i) * 16));
-      g2lds16(vt + vsrc[i], (lds_void*)(sb + TILE + (wave * 64 + kAThreads * i) * 16));
+      buf2lds16(krs, ksrc, j * TILE + i * kAThreads * 16, (lds_void*)(kd + (wave * 64 + kAThreads * i) * 16));
+      buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
     }
   };
-  // mean operand of chunk c (8 key blocks): DB d-blocks x 64 lanes x 16 bytes, one
-  // d-block per wave per round
+  // mean operand of chunk c: NDB x 2 MFMAs x 64 lanes x 16 bytes, one 1 KB piece per wave
   auto issue_pack = [&](int c) {
-    for (int db = wave; db < DB; db += 4)
-      g2lds16(packh + (((size_t)c * DB + db) * 64 + lane) * 8, (lds_void*)(packs + db * 1024));
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(mu_pack) + ((size_t)bh * nchunk + c) * PACK;
+    const rsrc_t r = make_rsrc(src, PACK);
+    for (int piece = wave; piece < PACK / 1024; piece += 4)
+      buf2lds16(r, lane * 16, piece * 1024, (lds_void*)(packs + piece * 1024));
   };
 
   // fixed per-lane fragment offsets (bytes, within a stage)
-  const int krow0 = 32 * (r16 >> 2) + (r16 & 3);
-  const int kA = k_off<D>(krow0, 2 * lg), kB = k_off<D>(krow0, 2 * lg + 1);
-  const int vA = v_off(r16, 2 * lg), vB = v_off(r16, 2 * lg + 1);
+  const int krow0 = 32 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
+  int kA[NDH], kB[NDH];
+  for (int dh = 0; dh < NDH; dh++) {
+    kA[dh] = k_off<D>(krow0, 4 * dh + 2 * h);
+    kB[dh] = k_off<D>(krow0, 4 * dh + 2 * h + 1);
+  }
+  const int vA0 = v_off(r32, 2 * h), vB0 = v_off(r32, 2 * h + 1);
+  const int vA1 = v_off(r32, 4 + 2 * h), vB1 = v_off(r32, 4 + 2 * h + 1);
 
-  float m[2] = {-__builtin_inff(), -__builtin_inff()};
-  float lsum[2] = {0.0f, 0.0f};
-  v4f oacc[DB][2];
-  for (int db = 0; db < DB; db++)
-    for (int g = 0; g < 2; g++) oacc[db][g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -__builtin_inff(), lsum = 0.0f;
+  v16f oacc[NDB];
+  for (int db = 0; db < NDB; db++)
+    for (int i = 0; i < 16; i++) oacc[db][i] = 0.0f;
+  v16f zero16;
+  for (int i = 0; i < 16; i++) zero16[i] = 0.0f;
 
   // Mean restoration on the matrix core: each key block's row sum r_j is logged with the
-  // running max m'_j it is scaled to; once per 8 key blocks the logged sums are brought
-  // to the current max, w = r_j 2^(m'_j - m'), and folded in with one
-  // v_mfma_f32_16x16x32_bf16 per d-block: O^T[c][q] += sum_s mu~_s[c] w_s[q], with mu~
-  // and w split into bf16 hi + lo (mu_hi w_hi + mu_hi w_lo + mu_lo w_hi).
-  // Log layout [wave][g][query r16][slot]: one lane's eight slots are 64 contiguous bytes.
-  float2* const rlog = reinterpret_cast<float2*>(packs + PACK) + wave * 2 * 16 * 8;
+  // running max m'_j it is scaled to; once per 8 key blocks the logged sums are brought to
+  // the current max, w = r_j 2^(m'_j - m'), split into bf16 hi + lo, and folded in with two
+  // v_mfma_f32_32x32x16_bf16 per 32-channel block: K slots 0..7 (lanes 0-31) take
+  // mu_hi x w_hi, slots 8..15 (lanes 32-63) mu_hi x w_lo, and the second MFMA mu_lo x w_hi.
+  // Log layout per wave [slot][query]: 32 lanes touch 256 contiguous bytes.
+  float2* const rlog = reinterpret_cast<float2*>(packs + PACK) + wave * (8 * 32);
   auto flush = [&](int nvalid) {
-    bf16x8 wb[2];
-    for (int g = 0; g < 2; g++) {
-      const float4* src = reinterpret_cast<const float4*>(rlog + (g * 16 + r16) * 8);
-      float rv[8], mv[8];
-      for (int k = 0; k < 4; k++) {
-        const float4 t = src[k];
-        rv[2 * k] = t.x; mv[2 * k] = t.y; rv[2 * k + 1] = t.z; mv[2 * k + 1] = t.w;
-      }
-      for (int k = 0; k < 8; k++) {
-        const float w = k < nvalid ? rv[k] * __builtin_amdgcn_exp2f(mv[k] - m[g]) : 0.0f;
-        const __bf16 hi = (__bf16)w;
-        const __bf16 lo = (__bf16)(w - (float)hi);
-        wb[g][k] = lg == 1 ? lo : (lg == 3 ? (__bf16)0.0f : hi);
-      }
+    float2 t[8];
+    for (int k = 0; k < 8; k++) t[k] = rlog[k * 32 + r32];
+    bf16x8 w0, w1;
+    for (int k = 0; k < 8; k++) {
+      const float w = k < nvalid ? t[k].x * __builtin_amdgcn_exp2f(t[k].y - m) : 0.0f;
+      const __bf16 hi = (__bf16)w;
+      const __bf16 lo = (__bf16)(w - (float)hi);
+      w0[k] = h ? lo : hi;
+      w1[k] = h ? (__bf16)0.0f : hi;
     }
-    for (int db = 0; db < DB; db++) {
-      bf16x8 a;
-      __builtin_memcpy(&a, packs + db * 1024 + lane * 16, 16);
-      for (int g = 0; g < 2; g++) oacc[db][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[g], oacc[db][g], 0, 0, 0);
+    for (int db = 0; db < NDB; db++) {
+      bf16x8 a0, a1;
+      __builtin_memcpy(&a0, packs + (db * 2 + 0) * 1024 + lane * 16, 16);
+      __builtin_memcpy(&a1, packs + (db * 2 + 1) * 1024 + lane * 16, 16);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, w0, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, w1, oacc[db], 0, 0, 0);
     }
   };
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  issue(0);
+  if (RESTORE) issue_pack(0);
+  wait_copies();
   __syncthreads();
 
   for (int j = 0; j < nb; j++) {
-    const uint8_t* sb = smem + (j & 1) * BUF;
+    const uint8_t* kt = kbuf + (j & 1) * TILE;
+    const uint8_t* vt = vbuf + (j & 1) * TILE;
     if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
-    if (j + 1 < nb) issue(j + 1, (j + 1) & 1);
-    if (RESTORE && (((j + 1) & 7) == 0 || j + 1 == nb)) issue_pack(j >> 3);
+    if (j + 1 < nb) issue(j + 1);
+    // chunk c = j/8 replaces chunk c-1, which every wave flushed before the last barrier
+    if (RESTORE && j > 1 && (j & 7) == 1) issue_pack(j >> 3);
 
-    // ---- S^T = K_j Q^T  (MFMA kb covers key rows krow0 + 4*kb)
-    v4f sacc[8][2];
-    for (int kb = 0; kb < 8; kb++) {
-      v8i a;
-      if (D == 128 || lg < 2) {
-        a = ld_frag(sb + kA + 4 * kb * D, sb + kB + 4 * kb * D);
-      } else {
-        for (int k = 0; k < 8; k++) a[k] = 0;
+    // ---- S^T = K_j Q^T
+    v16f sacc[4];
+    for (int kb = 0; kb < 4; kb++) {
+      const int ko = (64 * (kb >> 1) + 16 * (kb & 1)) * D;
+      for (int dh = 0; dh < NDH; dh++) {
+        const v8i a = ld_frag(kt + kA[dh] + ko, kt + kB[dh] + ko);
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[dh], dh == 0 ? zero16 : sacc[kb], 0, 0, 0, 0, 0, 0);
       }
-      for (int g = 0; g < 2; g++)
-        sacc[kb][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qf[g], zero4, 0, 0, 0, 0, 0, 0);
     }
-    const float sigma = sq * sK[(size_t)bh * nb + j];
+    const float sigma = sq * sKh[j];
 
     // ---- online softmax, probability bytes, row sums
+    float mx;
+    {
+      float v[64];
+      for (int kb = 0; kb < 4; kb++)
+        for (int i = 0; i < 16; i++) v[16 * kb + i] = sacc[kb][i];
+      float w[22];
+      for (int i = 0; i < 21; i++) w[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+      w[21] = v[63];
+      float x[8];
+      for (int i = 0; i < 7; i++) x[i] = fmaxf(fmaxf(w[3 * i], w[3 * i + 1]), w[3 * i + 2]);
+      x[7] = w[21];
+      const float y0 = fmaxf(fmaxf(x[0], x[1]), x[2]), y1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+      mx = lane_max2(fmaxf(fmaxf(y0, y1), fmaxf(x[6], x[7])));
+    }
+    const float mnew = sigma * mx;
+    const float mp = fmaxf(m, mnew);
+    const float alpha = __builtin_amdgcn_exp2f(m - mp);
     v8i pf[2];
-    float rsum[2];
-    for (int g = 0; g < 2; g++) {
-      float mx = fmaxf(sacc[0][g][0], sacc[0][g][1]);
-      mx = fmaxf(mx, fmaxf(sacc[0][g][2], sacc[0][g][3]));
-      for (int kb = 1; kb < 8; kb++)
-        mx = fmaxf(fmaxf(mx, fmaxf(sacc[kb][g][0], sacc[kb][g][1])), fmaxf(sacc[kb][g][2], sacc[kb][g][3]));
-      mx = lane_max4(mx);
-      const float mnew = sigma * mx;
-      const float mp = fmaxf(m[g], mnew);
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - mp);
-      float r = 0.0f;
-      if (EXPCAST) {
-        const float bias = C0 - 8.0f * mp;
-        const float s8 = 8.0f * sigma;
-        if (!__ballot(fabsf(mp) >= 65536.0f)) {
-          // |m'| < 2^16 bounds t = fma(S, 8 sigma, bias) below 120.5, so the upper clamp
-          // is idle; cvt_pk_u8_f32 rounds half-even and saturates negatives (and NaN) to 0.
-          for (int kb = 0; kb < 8; kb++) {
+    float r;
+    if (EXPCAST) {
+      const float bias = C0 - 8.0f * mp;
+      const float s8 = 8.0f * sigma;
+      if (!__ballot(fabsf(mp) >= 65536.0f)) {
+        // |m'| < 2^16 bounds t = fma(S, 8 sigma, bias) below 120.5, so the upper clamp is
+        // idle; cvt_pk_u8_f32 rounds half-even and saturates negatives (and NaN) to 0.
+        for (int kb = 0; kb < 4; kb++)
+          for (int qd = 0; qd < 4; qd++) {
             uint32_t w = 0;
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][g][0], s8, bias), 0, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][g][1], s8, bias), 1, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][g][2], s8, bias), 2, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][g][3], s8, bias), 3, w);
-            pf[g][kb] = (int)w;
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 0], s8, bias), 0, w);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 1], s8, bias), 1, w);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 2], s8, bias), 2, w);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 3], s8, bias), 3, w);
+            pf[kb >> 1][4 * (kb & 1) + qd] = (int)w;
           }
-        } else {
-          for (int kb = 0; kb < 8; kb++) {
-            uint32_t w = 0;
-            w = expcast_byte(sacc[kb][g][0], s8, bias, w, 0);
-            w = expcast_byte(sacc[kb][g][1], s8, bias, w, 1);
-            w = expcast_byte(sacc[kb][g][2], s8, bias, w, 2);
-            w = expcast_byte(sacc[kb][g][3], s8, bias, w, 3);
-            pf[g][kb] = (int)w;
-          }
-        }
-        // row sum of the decoded bytes on the matrix core: every row of the result is r
-        r = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pf[g], zero4, 0, 0, 0, 0, 0, 0)[0];
       } else {
-        for (int kb = 0; kb < 8; kb++) {
-          float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][0] - mp);
-          float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][1] - mp);
-          float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][2] - mp);
-          float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][g][3] - mp);
-          pf[g][kb] = (int)e4m3x4_from_f32(p0, p1, p2, p3);
+        for (int kb = 0; kb < 4; kb++)
+          for (int qd = 0; qd < 4; qd++) {
+            uint32_t w = 0;
+            w = expcast_byte(sacc[kb][4 * qd + 0], s8, bias, w, 0);
+            w = expcast_byte(sacc[kb][4 * qd + 1], s8, bias, w, 1);
+            w = expcast_byte(sacc[kb][4 * qd + 2], s8, bias, w, 2);
+            w = expcast_byte(sacc[kb][4 * qd + 3], s8, bias, w, 3);
+            pf[kb >> 1][4 * (kb & 1) + qd] = (int)w;
+          }
+      }
+      // row sum of the decoded bytes on the matrix core: every row of the result is r
+      v16f rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[0], zero16, 0, 0, 0, 0, 0, 0);
+      rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[1], rs, 0, 0, 0, 0, 0, 0);
+      r = rs[0];
+    } else {
+      r = 0.0f;
+      for (int kb = 0; kb < 4; kb++) {
+        __builtin_amdgcn_sched_barrier(0);
+        for (int qd = 0; qd < 4; qd++) {
+          const float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 0] - mp);
+          const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
+          const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
+          const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
+          pf[kb >> 1][4 * (kb & 1) + qd] = (int)e4m3x4_from_f32(p0, p1, p2, p3);
           r += (p0 + p1) + (p2 + p3);
         }
-        r = lane_sum4(r);
       }
-      rsum[g] = r;
-      lsum[g] = __builtin_fmaf(alpha, lsum[g], r);
-      if (__ballot(alpha != 1.0f))
-        for (int db = 0; db < DB; db++) oacc[db][g] *= alpha;
-      if (RESTORE && lg == 0) rlog[(g * 16 + r16) * 8 + (j & 7)] = make_float2(r, mp);
-      m[g] = mp;
-      if (DUMP && j == dump_block) {
-        const int q = qb * kBlock + wave * 32 + g * 16 + r16;
-        uint4* dst = reinterpret_cast<uint4*>(dump + ((size_t)bh * N + q) * kBlock + 32 * lg);
-        dst[0] = make_uint4(pf[g][0], pf[g][1], pf[g][2], pf[g][3]);
-        dst[1] = make_uint4(pf[g][4], pf[g][5], pf[g][6], pf[g][7]);
-      }
+      r = lane_sum2(r);
+    }
+    lsum = __builtin_fmaf(alpha, lsum, r);
+    if (__ballot(alpha != 1.0f))
+      for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
+    if (RESTORE && h == 0) rlog[(j & 7) * 32 + r32] = make_float2(r, mp);
+    m = mp;
+    if (DUMP && j == dump_block) {
+      uint4* dst = reinterpret_cast<uint4*>(dump + ((size_t)bh * N + q) * kBlock + 32 * h);
+      dst[0] = make_uint4(pf[0][0], pf[0][1], pf[0][2], pf[0][3]);
+      dst[1] = make_uint4(pf[0][4], pf[0][5], pf[0][6], pf[0][7]);
+      dst[4] = make_uint4(pf[1][0], pf[1][1], pf[1][2], pf[1][3]);
+      dst[5] = make_uint4(pf[1][4], pf[1][5], pf[1][6], pf[1][7]);
     }
 
-    // ---- O^T += V_j^T P^T  (+ r * mu_j)
-    for (int db = 0; db < DB; db++) {
-      v8i a = ld_frag(sb + TILE + vA + 16 * db * 128, sb + TILE + vB + 16 * db * 128);
-      for (int g = 0; g < 2; g++)
-        oacc[db][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, pf[g], oacc[db][g], 0, 0, 0, 0, 0, 0);
+    // ---- O^T += V_j^T P^T  (32-channel block db, 64-key half kh)
+    for (int db = 0; db < NDB; db++) {
+      const int vo = 32 * db * 128;
+      const v8i a0 = ld_frag(vt + vA0 + vo, vt + vB0 + vo);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, pf[0], oacc[db], 0, 0, 0, 0, 0, 0);
+      const v8i a1 = ld_frag(vt + vA1 + vo, vt + vB1 + vo);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, pf[1], oacc[db], 0, 0, 0, 0, 0, 0);
     }
-    // next stage landed (its loads were issued at the top of this iteration) and every
+    // next stage landed (its copies were issued at the top of this iteration) and every
     // wave is done with this stage before it is refilled
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    wait_copies();
+    wg_barrier();
   }
 
-  if (RESTORE) flush(nb - ((nb - 1) & ~7));  // last chunk: slots past the final key block are zero
+  if (RESTORE) {
+    const int clast = (nb - 1) >> 3;
+    if (clast > 0 && 8 * clast + 1 >= nb) {  // a one-block last chunk was not copied in the loop
+      issue_pack(clast);
+      wait_copies();
+      wg_barrier();
+    }
+    flush(nb - 8 * clast);
+  }
 
-  // ---- epilogue: O = bf16(sV * A / l), rows in original order
-  for (int g = 0; g < 2; g++) {
-    const int q = qb * kBlock + wave * 32 + g * 16 + r16;
-    const float il = 1.0f / lsum[g];
-    uint16_t* orow = O + ((size_t)bh * N + q) * D;
-    for (int db = 0; db < DB; db++) {
-      const int c = 16 * db + 4 * lg;
+  // ---- epilogue: O = bf16(sV * A / l); element i of block db is channel 32 db + 8(i/4) + 4h + i%4
+  const float il = 1.0f / lsum;
+  uint16_t* orow = O + ((size_t)bh * N + q) * D;
+  for (int db = 0; db < NDB; db++)
+    for (int g = 0; g < 4; g++) {
+      const int c = 32 * db + 8 * g + 4 * h;
       const float4 s4 = *reinterpret_cast<const float4*>(sV + (size_t)bh * D + c);
-      uint32_t w0 = (uint32_t)f32_to_bf16(s4.x * oacc[db][g][0] * il) | ((uint32_t)f32_to_bf16(s4.y * oacc[db][g][1] * il) << 16);
-      uint32_t w1 = (uint32_t)f32_to_bf16(s4.z * oacc[db][g][2] * il) | ((uint32_t)f32_to_bf16(s4.w * oacc[db][g][3] * il) << 16);
+      uint32_t w0 = (uint32_t)f32_to_bf16(s4.x * oacc[db][4 * g + 0] * il) | ((uint32_t)f32_to_bf16(s4.y * oacc[db][4 * g + 1] * il) << 16);
+      uint32_t w1 = (uint32_t)f32_to_bf16(s4.z * oacc[db][4 * g + 2] * il) | ((uint32_t)f32_to_bf16(s4.w * oacc[db][4 * g + 3] * il) << 16);
       *reinterpret_cast<uint2*>(orow + c) = make_uint2(w0, w1);
     }
-  }
 }
 
 __global__ void expcast_kernel(const float* __restrict__ acc, const float* __restrict__ s8, const float* __restrict__ bias,

@@ -8,6 +8,7 @@ namespace vc {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 128;  // quantisation block and key tile: 128 tokens
@@ -74,8 +75,12 @@ __device__ __forceinline__ uint32_t e4m3x4_from_f32(float a, float b, float c, f
 // FMA, then round half to even and clamp to [0, 120]. med3 clamps in the float
 // domain (clamping to integer bounds commutes with rounding) and cvt_pk_u8_f32
 // rounds to nearest even; the byte lands in position `sel` of `old`.
+// The FMA is written as the instruction itself: the attention kernel also evaluates the
+// same FMA on its unclamped fast path, and an opaque instruction keeps the compiler from
+// hoisting both into one shared set of 32 live temporaries.
 __device__ __forceinline__ uint32_t expcast_byte(float acc, float scale8, float bias, uint32_t old, int sel) {
-  float t = __builtin_fmaf(acc, scale8, bias);
+  float t;
+  asm("v_fma_f32 %0, %1, %2, %3" : "=v"(t) : "v"(acc), "v"(scale8), "v"(bias));
   t = __builtin_amdgcn_fmed3f(t, 0.0f, 120.0f);
   switch (sel) {
     case 0: return __builtin_amdgcn_cvt_pk_u8_f32(t, 0, old);

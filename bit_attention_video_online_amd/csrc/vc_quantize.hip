@@ -210,20 +210,21 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
   const float ms = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
   if (g == 0 && mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = ms;
   if (g == 0 && mu_pack) {
-    // mean-restoration operand, laid out as the A operand of v_mfma_f32_16x16x32_bf16:
-    // [chunk of 8 key blocks][d-block][lane][8]: lanes 0-31 hold bf16(ms), lanes 32-47
-    // bf16(ms - bf16(ms)), lanes 48-63 zero; element s belongs to key block 8*chunk + s.
-    const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 16, r = c % 16;
+    // mean-restoration operand, laid out as the A operands of two v_mfma_f32_32x32x16_bf16
+    // per 32-channel block: [chunk of 8 key blocks][d-block][MFMA t][lane][8]. MFMA 0:
+    // lanes 0-31 and 32-63 hold bf16(ms); MFMA 1: lanes 0-31 bf16(ms - bf16(ms)), lanes
+    // 32-63 zero; lane l carries channel 32*d-block + l%32, element s key block 8*chunk + s.
+    const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 32, r = c % 32;
     const uint16_t hi = f32_to_bf16(ms);
     const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
-    uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 16) + db) * 64) * 8;
+    uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 32) + db) * 2 * 64) * 8;
     base[(r) * 8 + s8] = hi;
-    base[(16 + r) * 8 + s8] = hi;
-    base[(32 + r) * 8 + s8] = lo;
-    base[(48 + r) * 8 + s8] = 0;
+    base[(32 + r) * 8 + s8] = hi;
+    base[(64 + r) * 8 + s8] = lo;
+    base[(96 + r) * 8 + s8] = 0;
     if (j == nb - 1) {  // key blocks past the end of the last chunk contribute nothing
       for (int t = s8 + 1; t < 8; t++) {
-        base[(r) * 8 + t] = 0; base[(16 + r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(48 + r) * 8 + t] = 0;
+        base[(r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(64 + r) * 8 + t] = 0; base[(96 + r) * 8 + t] = 0;
       }
     }
   }

@@ -112,11 +112,11 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
  *   mu   bf16 [B,H,N/128,d]        block means of V' (zero when !VC_F_VSMOOTH); may be NULL
  *   mu_scaled float [B,H,N/128,d]  fl32(mu / sV); may be NULL
  *   mu_pack  bf16, vc_mu_pack_size(B,H,N,d) bytes: mu_scaled in the operand layout that
- *            vc_attention consumes, [B,H,ceil(N/1024),d/16,64,8]: for chunk c of 8 key
- *            blocks, 16-channel group b, lane l and element s (key block 8c+s): lanes
- *            0..31 hold bf16(mu_scaled), lanes 32..47 bf16(mu_scaled - bf16(mu_scaled)),
- *            lanes 48..63 zero, always of channel 16b + (l mod 16); key blocks past
- *            N/128 are zero. May be NULL.
+ *            vc_attention consumes, [B,H,ceil(N/1024),d/32,2,64,8]: for chunk c of 8 key
+ *            blocks, 32-channel block b, operand t, lane l and element s (key block 8c+s),
+ *            always of channel 32b + (l mod 32): t = 0 holds bf16(mu_scaled) in all lanes;
+ *            t = 1 holds bf16(mu_scaled - bf16(mu_scaled)) in lanes 0..31 and zero in
+ *            lanes 32..63; key blocks past N/128 are zero. May be NULL.
  * Arithmetic: block and channel scales are fl32(amax/448) with codes
  * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
  * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).

@@ -35,7 +35,8 @@ def vq_rowmajor(Vq: np.ndarray) -> np.ndarray:
 
 def mu_pack_expected(mu_scaled: np.ndarray) -> np.ndarray:
     """Layout of vc_quantize's mu_pack output derived from [nb, d] float32 scaled means:
-    [ceil(nb/8), d/16, 64, 8] bf16 bits (lanes 0-31 hi, 32-47 lo, 48-63 zero)."""
+    [ceil(nb/8), d/32, 2, 64, 8] bf16 bits (MFMA 0: hi in both lane halves; MFMA 1: lo in
+    lanes 0-31, zero in lanes 32-63; lane l carries channel 32*block + l%32)."""
     import synth
     nb, d = mu_scaled.shape
     nc = (nb + 7) // 8
@@ -43,14 +44,14 @@ def mu_pack_expected(mu_scaled: np.ndarray) -> np.ndarray:
     ms[:nb] = mu_scaled
     hi = synth.bf16_bits(ms)
     lo = synth.bf16_bits((ms - synth.bf16_to_f32(hi)).astype(np.float32))
-    out = np.zeros((nc, d // 16, 64, 8), np.uint16)
+    out = np.zeros((nc, d // 32, 2, 64, 8), np.uint16)
     for c in range(nc):
-        for b in range(d // 16):
-            for r in range(16):
-                ch = 16 * b + r
-                out[c, b, r] = hi[8 * c:8 * c + 8, ch]
-                out[c, b, 16 + r] = hi[8 * c:8 * c + 8, ch]
-                out[c, b, 32 + r] = lo[8 * c:8 * c + 8, ch]
+        for b in range(d // 32):
+            for r in range(32):
+                ch = 32 * b + r
+                out[c, b, 0, r] = hi[8 * c:8 * c + 8, ch]
+                out[c, b, 0, 32 + r] = hi[8 * c:8 * c + 8, ch]
+                out[c, b, 1, r] = lo[8 * c:8 * c + 8, ch]
     return out
 
 
