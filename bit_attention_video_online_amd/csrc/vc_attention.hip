@@ -20,6 +20,14 @@ namespace vc {
 
 constexpr int kAThreads = 256;  // 4 waves; two work-groups per CU
 
+// per-byte min(b, 120) of a packed dword (two bytes per 16-bit half at a time)
+__device__ __forceinline__ uint32_t bytes_min120(uint32_t w) {
+  uint32_t lo = w & 0x00ff00ffu, hi = (w >> 8) & 0x00ff00ffu;
+  lo = min(lo & 0xffffu, 120u) | (min(lo >> 16, 120u) << 16);
+  hi = min(hi & 0xffffu, 120u) | (min(hi >> 16, 120u) << 16);
+  return lo | (hi << 8);
+}
+
 // lanes l and l^32 hold the same query: combine them with one v_permlane32_swap
 __device__ __forceinline__ float lane_max2(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -164,8 +172,17 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     qf[dh][0] = a.x; qf[dh][1] = a.y; qf[dh][2] = a.z; qf[dh][3] = a.w;
     qf[dh][4] = b.x; qf[dh][5] = b.y; qf[dh][6] = b.z; qf[dh][7] = b.w;
   }
-  v8i ones;  // all-ones E4M3 (0x38 = 1.0): MFMAs with it turn probability bytes into row sums
-  for (int k = 0; k < 8; k++) ones[k] = 0x38383838;
+  // Row sums on the matrix core: read as the B operand of v_mfma_f32_16x16x128_f8f6f4, a
+  // PV operand pf[kh] gives column c = l%16 the key bytes of query c (lane groups 0, 2)
+  // and of query c+16 (lane groups 1, 3). The A operand row m selects one of the two:
+  // it is E4M3 1.0 (0x38) where ((m>>2)&1) equals the lane group's query half and zero
+  // elsewhere, so output rows 4(l/16)..+3, which lane l receives, all hold the row sum of
+  // query l%32.
+  v8i sel;
+  {
+    const int on = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x38383838 : 0;
+    for (int k = 0; k < 8; k++) sel[k] = on;
+  }
 
   // ---- tile copies (buffer -> LDS, lane L of a wave fills LDS chunk base+L). The source of
   // each chunk is chosen so that LDS ends up in the swizzled layout; a thread's chunks i > 0
@@ -180,13 +197,15 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     const int vrow = P >> 3, vphys = P & 7;
     vsrc = vrow * 128 + 16 * (vphys ^ v_swz(vrow));
   }
-  auto issue = [&](int j) {
+  auto issue_k = [&](int j) {
     uint8_t* kd = kbuf + (j & 1) * TILE;
-    uint8_t* vd = vbuf + (j & 1) * TILE;
-    for (int i = 0; i < PW; i++) {
+    for (int i = 0; i < PW; i++)
       buf2lds16(krs, ksrc, j * TILE + i * kAThreads * 16, (lds_void*)(kd + (wave * 64 + kAThreads * i) * 16));
+  };
+  auto issue_v = [&](int j) {
+    uint8_t* vd = vbuf + (j & 1) * TILE;
+    for (int i = 0; i < PW; i++)
       buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
-    }
   };
   // mean operand of chunk c: NDB x 2 MFMAs x 64 lanes x 16 bytes, one 1 KB piece per wave
   auto issue_pack = [&](int c) {
@@ -212,6 +231,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     for (int i = 0; i < 16; i++) oacc[db][i] = 0.0f;
   v16f zero16;
   for (int i = 0; i < 16; i++) zero16[i] = 0.0f;
+  const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   // Mean restoration on the matrix core: each key block's row sum r_j is logged with the
   // running max m'_j it is scaled to; once per 8 key blocks the logged sums are brought to
@@ -240,31 +260,50 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     }
   };
 
-  issue(0);
-  if (RESTORE) issue_pack(0);
-  wait_copies();
-  __syncthreads();
-
-  for (int j = 0; j < nb; j++) {
-    const uint8_t* kt = kbuf + (j & 1) * TILE;
-    const uint8_t* vt = vbuf + (j & 1) * TILE;
-    if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
-    if (j + 1 < nb) issue(j + 1);
-    // chunk c = j/8 replaces chunk c-1, which every wave flushed before the last barrier
-    if (RESTORE && j > 1 && (j & 7) == 1) issue_pack(j >> 3);
-
-    // ---- S^T = K_j Q^T
-    v16f sacc[4];
-    for (int kb = 0; kb < 4; kb++) {
+  // S for key groups kb0, kb0+1 of the tile in stage `stage` (d halves accumulated)
+  v16f sacc[4];
+  auto s_part = [&](int stage, int kb0) {
+    const uint8_t* kt = kbuf + stage * TILE;
+    for (int kb = kb0; kb < kb0 + 2; kb++) {
       const int ko = (64 * (kb >> 1) + 16 * (kb & 1)) * D;
       for (int dh = 0; dh < NDH; dh++) {
         const v8i a = ld_frag(kt + kA[dh] + ko, kt + kB[dh] + ko);
         sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[dh], dh == 0 ? zero16 : sacc[kb], 0, 0, 0, 0, 0, 0);
       }
     }
+  };
+  // O^T += V_j^T P^T for the 64-key half kh
+  auto pv_part = [&](const uint8_t* vt, int kh, const v8i& p) {
+    const int A0 = kh ? vA1 : vA0, B0 = kh ? vB1 : vB0;
+    for (int db = 0; db < NDB; db++) {
+      const int vo = 32 * db * 128;
+      const v8i a = ld_frag(vt + A0 + vo, vt + B0 + vo);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, oacc[db], 0, 0, 0, 0, 0, 0);
+    }
+  };
+
+  // Pipeline: K runs one tile ahead of V. Iteration j holds K_{j+1} and V_j in LDS while
+  // K_{j+2} and V_{j+1} land in the other stages; S_j was computed in iteration j-1.
+  issue_k(0);
+  if (nb > 1) issue_k(1);
+  issue_v(0);
+  if (RESTORE) issue_pack(0);
+  wait_copies();
+  __syncthreads();
+  s_part(0, 0);
+  s_part(0, 2);
+
+  for (int j = 0; j < nb; j++) {
+    const uint8_t* vt = vbuf + (j & 1) * TILE;
+    const int nst = (j + 1) & 1;  // stage of K_{j+1} (stale, and unused, after the last tile)
+    if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
+    if (j + 2 < nb) issue_k(j + 2);                    // replaces K_j, consumed in iteration j-1
+    if (j + 1 < nb) issue_v(j + 1);                    // replaces V_{j-1}
+    // chunk c = j/8 replaces chunk c-1, which every wave flushed before the last barrier
+    if (RESTORE && j > 1 && (j & 7) == 1) issue_pack(j >> 3);
     const float sigma = sq * sKh[j];
 
-    // ---- online softmax, probability bytes, row sums
+    // ---- running max over S_j
     float mx;
     {
       float v[64];
@@ -282,56 +321,57 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     const float mnew = sigma * mx;
     const float mp = fmaxf(m, mnew);
     const float alpha = __builtin_amdgcn_exp2f(m - mp);
+    if (__ballot(alpha != 1.0f))
+      for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
+
+    // ---- probability bytes per 64-key half; the PV MFMAs of a half and the next tile's
+    // S MFMAs for the freed accumulators are issued as soon as the half is done, so the
+    // matrix core works while the vector ALU converts the other half.
     v8i pf[2];
-    float r;
-    if (EXPCAST) {
-      const float bias = C0 - 8.0f * mp;
-      const float s8 = 8.0f * sigma;
-      if (!__ballot(fabsf(mp) >= 65536.0f)) {
-        // |m'| < 2^16 bounds t = fma(S, 8 sigma, bias) below 120.5, so the upper clamp is
-        // idle; cvt_pk_u8_f32 rounds half-even and saturates negatives (and NaN) to 0.
-        for (int kb = 0; kb < 4; kb++)
-          for (int qd = 0; qd < 4; qd++) {
-            uint32_t w = 0;
+    float r = 0.0f;
+    v4f rs;
+    // ExpCast bytes: cvt_pk_u8_f32 rounds half-even and saturates to [0, 255] (NaN -> 0), so
+    // clamp(rne(t), 0, 120) = min(cvt(t), 120). For |m'| < 2^16 every t = fma(S, 8 sigma, bias)
+    // stays below 120.5 and the min is idle; otherwise (uniform per wave, rare) a packed
+    // per-byte min fixes the operand before its MFMAs read it.
+    const bool fix = EXPCAST && __ballot(fabsf(mp) >= 65536.0f);
+    auto bytes_half = [&](int kh) {
+      for (int kb = 2 * kh; kb < 2 * kh + 2; kb++)
+        for (int qd = 0; qd < 4; qd++) {
+          uint32_t w = 0;
+          if (EXPCAST) {
+            const float bias = C0 - 8.0f * mp;
+            const float s8 = 8.0f * sigma;
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 0], s8, bias), 0, w);
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 1], s8, bias), 1, w);
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 2], s8, bias), 2, w);
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 3], s8, bias), 3, w);
-            pf[kb >> 1][4 * (kb & 1) + qd] = (int)w;
+          } else {
+            const float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 0] - mp);
+            const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
+            const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
+            const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
+            w = e4m3x4_from_f32(p0, p1, p2, p3);
+            r += (p0 + p1) + (p2 + p3);
           }
-      } else {
-        for (int kb = 0; kb < 4; kb++)
-          for (int qd = 0; qd < 4; qd++) {
-            uint32_t w = 0;
-            w = expcast_byte(sacc[kb][4 * qd + 0], s8, bias, w, 0);
-            w = expcast_byte(sacc[kb][4 * qd + 1], s8, bias, w, 1);
-            w = expcast_byte(sacc[kb][4 * qd + 2], s8, bias, w, 2);
-            w = expcast_byte(sacc[kb][4 * qd + 3], s8, bias, w, 3);
-            pf[kb >> 1][4 * (kb & 1) + qd] = (int)w;
-          }
-      }
-      // row sum of the decoded bytes on the matrix core: every row of the result is r
-      v16f rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[0], zero16, 0, 0, 0, 0, 0, 0);
-      rs = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf[1], rs, 0, 0, 0, 0, 0, 0);
-      r = rs[0];
-    } else {
-      r = 0.0f;
-      for (int kb = 0; kb < 4; kb++) {
-        __builtin_amdgcn_sched_barrier(0);
-        for (int qd = 0; qd < 4; qd++) {
-          const float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 0] - mp);
-          const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
-          const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
-          const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
-          pf[kb >> 1][4 * (kb & 1) + qd] = (int)e4m3x4_from_f32(p0, p1, p2, p3);
-          r += (p0 + p1) + (p2 + p3);
+          pf[kh][4 * (kb & 1) + qd] = (int)w;
         }
-      }
-      r = lane_sum2(r);
+      if (fix)
+        for (int k = 0; k < 8; k++) pf[kh][k] = (int)bytes_min120((uint32_t)pf[kh][k]);
+    };
+    bytes_half(0);
+    pv_part(vt, 0, pf[0]);
+    s_part(nst, 0);
+    bytes_half(1);
+    if (EXPCAST) {  // row sum of the decoded bytes on the matrix core
+      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[0], zero4, 0, 0, 0, 0, 0, 0);
+      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[1], rs, 0, 0, 0, 0, 0, 0);
     }
+    pv_part(vt, 1, pf[1]);
+    s_part(nst, 2);
+    r = EXPCAST ? rs[0] : lane_sum2(r);
+
     lsum = __builtin_fmaf(alpha, lsum, r);
-    if (__ballot(alpha != 1.0f))
-      for (int db = 0; db < NDB; db++) oacc[db] *= alpha;
     if (RESTORE && h == 0) rlog[(j & 7) * 32 + r32] = make_float2(r, mp);
     m = mp;
     if (DUMP && j == dump_block) {
@@ -341,17 +381,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
       dst[4] = make_uint4(pf[1][0], pf[1][1], pf[1][2], pf[1][3]);
       dst[5] = make_uint4(pf[1][4], pf[1][5], pf[1][6], pf[1][7]);
     }
-
-    // ---- O^T += V_j^T P^T  (32-channel block db, 64-key half kh)
-    for (int db = 0; db < NDB; db++) {
-      const int vo = 32 * db * 128;
-      const v8i a0 = ld_frag(vt + vA0 + vo, vt + vB0 + vo);
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, pf[0], oacc[db], 0, 0, 0, 0, 0, 0);
-      const v8i a1 = ld_frag(vt + vA1 + vo, vt + vB1 + vo);
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, pf[1], oacc[db], 0, 0, 0, 0, 0, 0);
-    }
-    // next stage landed (its copies were issued at the top of this iteration) and every
-    // wave is done with this stage before it is refilled
+    // copies of this iteration landed, and every wave is done with the stages they replace
     wait_copies();
     wg_barrier();
   }
