@@ -14,6 +14,8 @@
 //   - K and V tiles are copied global -> LDS with buffer_load ... lds (scalar-addressed,
 //     no per-lane address arithmetic) into a two-stage buffer; tile j+1 lands while
 //     tile j is consumed, with one barrier per tile.
+#include <type_traits>
+
 #include "vc_device.h"
 
 namespace vc {
@@ -97,6 +99,13 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int nbytes) {
   return rsrc_t{};
 #endif
 }
+// Read-only data with a wave-uniform address, through the constant address space: the
+// load becomes a scalar s_load, which never waits behind the tile copies the way a
+// vector load's vmcnt would.
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+__device__ __forceinline__ float uniform_load(const float* p, int i) {
+  return ((const_f32_ptr)p)[i];
+}
 // 16-byte buffer -> LDS copy (buffer_load_dwordx4 ... lds): lane L of the wave writes
 // LDS[base + 16 L] from the resource at voff + soff. Device pass only (see g2lds16).
 __device__ __forceinline__ void buf2lds16(rsrc_t r, int voff, int soff, lds_void* dst_wave_base) {
@@ -112,7 +121,9 @@ __device__ __forceinline__ void buf2lds16(rsrc_t r, int voff, int soff, lds_void
 // has consumed the fragments it read before it arrives (the MFMAs that use them are
 // issued first). The clobber keeps the compiler from moving memory accesses across.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) only (expcnt 7, lgkmcnt 15 left open), through the builtin so that the compiler's
+// own wait tracking knows the copies are complete
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // One work-group = 4 waves = 128 query rows of one (b,h), 32 rows per wave; two
 // work-groups per CU, so every SIMD runs two waves whose vector-ALU work interleaves with
@@ -145,13 +156,19 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   constexpr int CPR = D / 16;                   // 16-byte chunks per K row
   constexpr int PACK = NDB * 2 * 64 * 16;       // mean operand of one chunk of 8 key blocks
   constexpr int RLOG = 4 * 8 * 32 * 8;          // waves x slots x queries x (r, m')
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * TILE + (RESTORE ? PACK + RLOG : 16)];
-  uint8_t* const kbuf = smem;                   // [2][TILE], K_j in stage j & 1
-  uint8_t* const vbuf = smem + 2 * TILE;        // [2][TILE], V_j in stage j & 1
-  uint8_t* const packs = smem + 4 * TILE;       // [PACK], mean operand of the current chunk
+  // Two stages each of K and V as separate arrays, always indexed by compile-time stage
+  // numbers (the loop below is unrolled by two): the compiler can then prove that fragment
+  // reads of one stage never alias the asynchronous copies into the other, and inserts no
+  // wait for those copies before the reads.
+  __shared__ __attribute__((aligned(16))) uint8_t kst0[TILE], kst1[TILE], vst0[TILE], vst1[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t packs[RESTORE ? PACK + RLOG : 16];
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   const int nb = N / kBlock;
-  const int logical = xcd_remap(blockIdx.x, total);
+  // work-group indices are uniform; readfirstlane makes that visible to the compiler so
+  // address arithmetic on them stays scalar
+  const int logical = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, total));
   const int bh = logical / nb, qb = logical % nb;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   const uint8_t* Vh = Vq + (size_t)bh * N * D;
   const int nchunk = (nb + 7) / 8;
   const float sq = sQ[(size_t)bh * nb + qb];
-  const float* sKh = sK + (size_t)bh * nb;
+  const float* sKh = sK + (size_t)bh * nb;  // per-tile scales, read with scalar loads
 
   // ---- Q fragments (B operand of S^T): query row, bytes [64 dh + 32 h, +32)
   v8i qf[NDH];
@@ -197,13 +214,13 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     const int vrow = P >> 3, vphys = P & 7;
     vsrc = vrow * 128 + 16 * (vphys ^ v_swz(vrow));
   }
-  auto issue_k = [&](int j) {
-    uint8_t* kd = kbuf + (j & 1) * TILE;
+  auto issue_k = [&](int j, auto st) {  // K_j into stage st (= j & 1)
+    uint8_t* kd = decltype(st)::value ? kst1 : kst0;
     for (int i = 0; i < PW; i++)
       buf2lds16(krs, ksrc, j * TILE + i * kAThreads * 16, (lds_void*)(kd + (wave * 64 + kAThreads * i) * 16));
   };
-  auto issue_v = [&](int j) {
-    uint8_t* vd = vbuf + (j & 1) * TILE;
+  auto issue_v = [&](int j, auto st) {  // V_j into stage st (= j & 1)
+    uint8_t* vd = decltype(st)::value ? vst1 : vst0;
     for (int i = 0; i < PW; i++)
       buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
   };
@@ -262,8 +279,8 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
 
   // S for key groups kb0, kb0+1 of the tile in stage `stage` (d halves accumulated)
   v16f sacc[4];
-  auto s_part = [&](int stage, int kb0) {
-    const uint8_t* kt = kbuf + stage * TILE;
+  auto s_part = [&](auto st, int kb0) {
+    const uint8_t* kt = decltype(st)::value ? kst1 : kst0;
     for (int kb = kb0; kb < kb0 + 2; kb++) {
       const int ko = (64 * (kb >> 1) + 16 * (kb & 1)) * D;
       for (int dh = 0; dh < NDH; dh++) {
@@ -284,24 +301,26 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
 
   // Pipeline: K runs one tile ahead of V. Iteration j holds K_{j+1} and V_j in LDS while
   // K_{j+2} and V_{j+1} land in the other stages; S_j was computed in iteration j-1.
-  issue_k(0);
-  if (nb > 1) issue_k(1);
-  issue_v(0);
+  issue_k(0, S0{});
+  if (nb > 1) issue_k(1, S1{});
+  issue_v(0, S0{});
   if (RESTORE) issue_pack(0);
   wait_copies();
   __syncthreads();
-  s_part(0, 0);
-  s_part(0, 2);
+  s_part(S0{}, 0);
+  s_part(S0{}, 2);
 
-  for (int j = 0; j < nb; j++) {
-    const uint8_t* vt = vbuf + (j & 1) * TILE;
-    const int nst = (j + 1) & 1;  // stage of K_{j+1} (stale, and unused, after the last tile)
+  // iteration j; P = j & 1 is a compile-time stage number
+  auto iteration = [&](int j, auto P) {
+    constexpr int p = decltype(P)::value;
+    using Other = std::integral_constant<int, 1 - p>;
+    const uint8_t* vt = p ? vst1 : vst0;  // V_j
+    const float sigma = sq * uniform_load(sKh, j);
     if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
-    if (j + 2 < nb) issue_k(j + 2);                    // replaces K_j, consumed in iteration j-1
-    if (j + 1 < nb) issue_v(j + 1);                    // replaces V_{j-1}
+    if (j + 2 < nb) issue_k(j + 2, P);                 // replaces K_j, consumed in iteration j-1
+    if (j + 1 < nb) issue_v(j + 1, Other{});           // replaces V_{j-1}
     // chunk c = j/8 replaces chunk c-1, which every wave flushed before the last barrier
     if (RESTORE && j > 1 && (j & 7) == 1) issue_pack(j >> 3);
-    const float sigma = sq * sKh[j];
 
     // ---- running max over S_j
     float mx;
@@ -361,14 +380,14 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     };
     bytes_half(0);
     pv_part(vt, 0, pf[0]);
-    s_part(nst, 0);
+    s_part(Other{}, 0);  // K_{j+1} (stale, and unused, after the last tile)
     bytes_half(1);
     if (EXPCAST) {  // row sum of the decoded bytes on the matrix core
       rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[0], zero4, 0, 0, 0, 0, 0, 0);
       rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[1], rs, 0, 0, 0, 0, 0, 0);
     }
     pv_part(vt, 1, pf[1]);
-    s_part(nst, 2);
+    s_part(Other{}, 2);
     r = EXPCAST ? rs[0] : lane_sum2(r);
 
     lsum = __builtin_fmaf(alpha, lsum, r);
@@ -384,6 +403,10 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     // copies of this iteration landed, and every wave is done with the stages they replace
     wait_copies();
     wg_barrier();
+  };
+  for (int j = 0; j < nb; j += 2) {
+    iteration(j, S0{});
+    if (j + 1 < nb) iteration(j + 1, S1{});
   }
 
   if (RESTORE) {
