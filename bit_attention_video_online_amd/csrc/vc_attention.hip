@@ -20,7 +20,9 @@
 
 namespace vc {
 
-constexpr int kAThreads = 256;  // 4 waves; two work-groups per CU
+constexpr int kWaves = 4;                 // waves per work-group (32 query rows each); two per CU
+constexpr int kAThreads = 64 * kWaves;
+constexpr int kQB = kWaves / 4;           // 128-row query blocks per work-group
 
 // per-byte min(b, 120) of a packed dword (two bytes per 16-bit half at a time)
 __device__ __forceinline__ uint32_t bytes_min120(uint32_t w) {
@@ -142,7 +144,7 @@ __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f7
 //   Mean restoration: O^T[c][q] += r_q mu~_j[c], accumulated on the matrix core once
 //   per 8 key blocks (bf16 hi/lo split, v_mfma_f32_32x32x16_bf16).
 template <int D, bool EXPCAST, bool RESTORE, bool DUMP>
-__global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
+__global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
                                                          const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
                                                          const uint8_t* __restrict__ Vq, const float* __restrict__ sV,
                                                          const uint16_t* __restrict__ mu_pack, int N, int total,
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   constexpr int NDH = D / 64;                   // 64-wide d halves of the S contraction
   constexpr int CPR = D / 16;                   // 16-byte chunks per K row
   constexpr int PACK = NDB * 2 * 64 * 16;       // mean operand of one chunk of 8 key blocks
-  constexpr int RLOG = 4 * 8 * 32 * 8;          // waves x slots x queries x (r, m')
+  constexpr int RLOG = kWaves * 8 * 32 * 8;     // waves x slots x queries x (r, m')
   // Two stages each of K and V as separate arrays, always indexed by compile-time stage
   // numbers (the loop below is unrolled by two): the compiler can then prove that fragment
   // reads of one stage never alias the asynchronous copies into the other, and inserts no
@@ -168,12 +170,18 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   const int nb = N / kBlock;
   // work-group indices are uniform; readfirstlane makes that visible to the compiler so
   // address arithmetic on them stays scalar
+  const int nwg = (nb + kQB - 1) / kQB;         // work-groups per (b,h)
   const int logical = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, total));
-  const int bh = logical / nb, qb = logical % nb;
+  const int bh = logical / nwg, wgq = logical % nwg;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, h = lane >> 5;
-  const int q = qb * kBlock + wave * 32 + r32;  // this lane's query row
+  // query block of this wave; a missing last block (N/128 not a multiple of the blocks per
+  // work-group) is computed on the last real block and not stored
+  const int qb_raw = kQB * wgq + wave / 4;
+  const bool store = qb_raw < nb;
+  const int qb = min(qb_raw, nb - 1);
+  const int q = qb * kBlock + (wave & 3) * 32 + r32;  // this lane's query row
 
   const uint8_t* Kh = Kq + (size_t)bh * N * D;
   const uint8_t* Vh = Vq + (size_t)bh * N * D;
@@ -228,7 +236,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   auto issue_pack = [&](int c) {
     const uint8_t* src = reinterpret_cast<const uint8_t*>(mu_pack) + ((size_t)bh * nchunk + c) * PACK;
     const rsrc_t r = make_rsrc(src, PACK);
-    for (int piece = wave; piece < PACK / 1024; piece += 4)
+    for (int piece = wave; piece < PACK / 1024; piece += kWaves)
       buf2lds16(r, lane * 16, piece * 1024, (lds_void*)(packs + piece * 1024));
   };
 
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
     lsum = __builtin_fmaf(alpha, lsum, r);
     if (RESTORE && h == 0) rlog[(j & 7) * 32 + r32] = make_float2(r, mp);
     m = mp;
-    if (DUMP && j == dump_block) {
+    if (DUMP && j == dump_block && store) {
       uint4* dst = reinterpret_cast<uint4*>(dump + ((size_t)bh * N + q) * kBlock + 32 * h);
       dst[0] = make_uint4(pf[0][0], pf[0][1], pf[0][2], pf[0][3]);
       dst[1] = make_uint4(pf[0][4], pf[0][5], pf[0][6], pf[0][7]);
@@ -420,6 +428,7 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_fwd(const uint8_t* __restri
   }
 
   // ---- epilogue: O = bf16(sV * A / l); element i of block db is channel 32 db + 8(i/4) + 4h + i%4
+  if (!store) return;
   const float il = 1.0f / lsum;
   uint16_t* orow = O + ((size_t)bh * N + q) * D;
   for (int db = 0; db < NDB; db++)
@@ -442,7 +451,7 @@ template <int D, bool E, bool R, bool DU>
 static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
                         const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                         uint8_t* dump, hipStream_t st) {
-  const int total = BH * (N / kBlock);
+  const int total = BH * ((N / kBlock + kQB - 1) / kQB);
   attn_fwd<D, E, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
 }
 
