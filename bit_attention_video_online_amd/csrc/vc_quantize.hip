@@ -12,66 +12,106 @@
 //   quant_reduce : per (b,h): kbar = fl32(exact mean), sV = fl32(amax/448), 448/amax.
 //   quant_apply  : per (b,h,block): K~' codes + scale; residual codes (block-transposed
 //                  layout) and mu / sV.
-// All loads are 16-byte vectors of one token row; rows of V' and K' are gathered
-// through pi. Exact sums use binary64, which is exact for these 128-term (or N-term)
-// sums of bfloat16 values whenever their exponent span is moderate.
+// Tiles stay in registers (no LDS staging): every load is a 16-byte vector of one token
+// row (rows of V' and K' gathered through pi) and per-channel reductions use lane
+// shuffles plus a small LDS step. Exact sums use binary64, which is exact for these
+// 128-term (or N-term) sums of bfloat16 values whenever their exponent span is moderate.
 #include "vc_device.h"
 
 namespace vc {
 
 constexpr int kQThreads = 256;
 
-// Block reduction of a float max over 256 threads (4 waves).
-__device__ __forceinline__ float block_max_256(float v, float* red) {
+// Thread layout of a 128 x D tile: 16-byte vectors (8 bf16). Thread t owns column chunk
+// t % CH (channels 8*chunk .. +7) of the RPT consecutive rows RPT*(t / CH) .. +RPT-1, so a
+// wave-wide load or store instruction covers whole rows (coalesced), and per-channel
+// reductions run over the threads that share a chunk: lanes xor multiples of CH inside a
+// wave, then the four waves through LDS.
+template <int D>
+struct Lay {
+  static constexpr int CH = D / 8;                   // chunks per row
+  static constexpr int RG = kQThreads / CH;          // row groups
+  static constexpr int RPT = kBlock / RG;            // rows per thread (8 or 4)
+};
+
+__device__ __forceinline__ void unpack8(uint4 raw, float* x) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int k = 0; k < 4; k++) {
+    x[2 * k] = __uint_as_float(w[k] << 16);
+    x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+
+// rows of a tile, gathered through `perm_blk` (or contiguous when NULL); an out-of-range
+// permutation entry reads row 0 instead of out of bounds
+template <int D>
+__device__ __forceinline__ void load_tile(const uint16_t* base, const int32_t* perm_blk, int nrows, float (&x)[Lay<D>::RPT][8]) {
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
+  const int chunk = threadIdx.x % CH, rg = threadIdx.x / CH;
+  for (int i = 0; i < RPT; i++) {
+    const int r = RPT * rg + i;
+    int src = perm_blk ? perm_blk[r] : r;
+    src = ((unsigned)src < (unsigned)nrows) ? src : 0;
+    unpack8(*reinterpret_cast<const uint4*>(base + (size_t)src * D + 8 * chunk), x[i]);
+  }
+}
+
+// reductions over the threads that share a chunk (lane bits >= log2(CH), then waves)
+template <int D>
+__device__ __forceinline__ double chunk_sum_wave(double v) {
+  for (int o = Lay<D>::CH; o < 64; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+template <int D>
+__device__ __forceinline__ float chunk_max_wave(float v) {
+  for (int o = Lay<D>::CH; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+// whole-block max over 256 threads
+__device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  int w = threadIdx.x >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Quantise a [128 x D] tile held as rows of bf16 in `tile` (LDS, floats) with one
-// scale; writes codes row-major to dst (global) and returns the scale.
+// one scale for the tile: s = fl32(amax/448), codes e4m3(fl32(x * fl32(448/amax)));
+// amax = 0 gives scale 1 and zero codes. Codes row-major, 8 bytes per row and thread.
 template <int D>
-__device__ __forceinline__ float quant_tile_rowmajor(const float* tile, uint8_t* dst, float* red) {
-  constexpr int EL = kBlock * D;
-  constexpr int STEPS = EL / (4 * kQThreads);  // float4 steps per thread: 16 (D=128) or 8 (D=64)
-  const float4* t4 = reinterpret_cast<const float4*>(tile);
+__device__ __forceinline__ float quant_rows(float (&x)[Lay<D>::RPT][8], uint8_t* dst, float* red) {
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
+  const int chunk = threadIdx.x % CH, rg = threadIdx.x / CH;
   float a = 0.0f;
-  for (int i = 0; i < STEPS; i++) {
-    float4 v = t4[i * kQThreads + threadIdx.x];
-    a = fmaxf(fmaxf(fmaxf(a, fabsf(v.x)), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  }
-  a = block_max_256(a, red);
+  for (int i = 0; i < RPT; i++)
+    for (int e = 0; e < 8; e++) a = fmaxf(a, fabsf(x[i][e]));
+  a = block_max(a, red);
   float s, inv;
   if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
-  uint32_t* o = reinterpret_cast<uint32_t*>(dst);
-  for (int i = 0; i < STEPS; i++) {
-    float4 v = t4[i * kQThreads + threadIdx.x];
-    o[i * kQThreads + threadIdx.x] = e4m3x4_from_f32(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+  for (int i = 0; i < RPT; i++) {
+    const uint32_t lo = e4m3x4_from_f32(x[i][0] * inv, x[i][1] * inv, x[i][2] * inv, x[i][3] * inv);
+    const uint32_t hi = e4m3x4_from_f32(x[i][4] * inv, x[i][5] * inv, x[i][6] * inv, x[i][7] * inv);
+    *reinterpret_cast<uint2*>(dst + (size_t)(RPT * rg + i) * D + 8 * chunk) = make_uint2(lo, hi);
   }
   return s;
 }
 
-// Load a 128-row tile of bf16 rows (rows gathered through `rows_of`, or contiguous)
-// into LDS as floats. Thread layout: 16-byte vectors (8 bf16), D/8 vectors per row.
+// per-channel exact column sums of the tile (binary64; every partial sum of these bf16
+// values is exact for moderate exponent spans, so the summation order is immaterial);
+// result for channel c in colsum[c] (LDS), valid after the call
 template <int D>
-__device__ __forceinline__ void load_rows(const uint16_t* base, const int32_t* perm_blk, float* tile, int nrows) {
-  constexpr int VPR = D / 8;                 // vectors per row
-  constexpr int NV = kBlock * VPR;           // vectors per tile
-  for (int v = threadIdx.x; v < NV; v += kQThreads) {
-    int r = v / VPR, c = (v % VPR) * 8;
-    int src = perm_blk ? perm_blk[r] : r;
-    src = ((unsigned)src < (unsigned)nrows) ? src : 0;  // a malformed permutation must not read out of bounds
-    uint4 raw = *reinterpret_cast<const uint4*>(base + (size_t)src * D + c);
-    float* t = tile + r * D + c;
-    uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    for (int k = 0; k < 4; k++) {
-      t[2 * k] = __uint_as_float(w[k] << 16);
-      t[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-    }
+__device__ __forceinline__ void column_sums(const float (&x)[Lay<D>::RPT][8], double* part, double* colsum) {
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
+  const int chunk = threadIdx.x % CH, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = 0; e < 8; e++) {
+    double acc = 0.0;
+    for (int i = 0; i < RPT; i++) acc += (double)x[i][e];
+    acc = chunk_sum_wave<D>(acc);
+    if (lane < CH) part[w * D + 8 * chunk + e] = acc;
   }
+  __syncthreads();
+  if (threadIdx.x < D) colsum[threadIdx.x] = (part[threadIdx.x] + part[D + threadIdx.x]) + (part[2 * D + threadIdx.x] + part[3 * D + threadIdx.x]);
+  __syncthreads();
 }
 
 template <int D>
@@ -81,88 +121,93 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
                                                          uint8_t* __restrict__ Qq, float* __restrict__ sQ,
                                                          uint16_t* __restrict__ mu, double* __restrict__ ksum,
                                                          float* __restrict__ vamax) {
-  __shared__ float tile[kBlock * D];
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
   __shared__ float red[4];
-  __shared__ double part[kQThreads];
+  __shared__ double part[4 * D];
+  __shared__ double colsum[D];
+  __shared__ float pmax[4 * D];
   const int nb = N / kBlock;
   const int j = blockIdx.x, bh = blockIdx.y;
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D, jrow = (size_t)j * kBlock * D;
   const int32_t* pblk = perm ? perm + (size_t)bh * N + (size_t)j * kBlock : nullptr;
+  const int chunk = threadIdx.x % CH, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float x[RPT][8];
 
-  // ---- Q block (original order)
-  load_rows<D>(Q + head + (size_t)j * kBlock * D, nullptr, tile, kBlock);
-  __syncthreads();
-  float s = quant_tile_rowmajor<D>(tile, Qq + head + (size_t)j * kBlock * D, red);
+  // ---- Q block (original order): codes and scale
+  load_tile<D>(Q + head + jrow, nullptr, kBlock, x);
+  const float s = quant_rows<D>(x, Qq + head + jrow, red);
   if (threadIdx.x == 0) sQ[(size_t)bh * nb + j] = s * cL;
-  __syncthreads();
 
   // ---- key channel partial sums (token order is irrelevant for a sum)
-  constexpr int G = kQThreads / D;  // row groups: 2 (D=128) or 4 (D=64)
-  const int c = threadIdx.x % D, g = threadIdx.x / D;
   if (flags & 1u) {
-    load_rows<D>(K + head + (size_t)j * kBlock * D, nullptr, tile, kBlock);
-    __syncthreads();
-    double acc = 0.0;
-    for (int r = g; r < kBlock; r += G) acc += (double)tile[r * D + c];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-    if (g == 0) {
-      double t = 0.0;
-      for (int k = 0; k < G; k++) t += part[k * D + c];
-      ksum[((size_t)bh * nb + j) * D + c] = t;
-    }
-    __syncthreads();
+    load_tile<D>(K + head + jrow, nullptr, kBlock, x);
+    column_sums<D>(x, part, colsum);
+    if (threadIdx.x < D) ksum[((size_t)bh * nb + j) * D + threadIdx.x] = colsum[threadIdx.x];
   }
 
-  // ---- V' block: mean (bf16) and residual channel maximum
-  if (pblk) load_rows<D>(V + head, pblk, tile, N);
-  else load_rows<D>(V + head + (size_t)j * kBlock * D, nullptr, tile, kBlock);
-  __syncthreads();
-  float m = 0.0f;
+  // ---- V' block: mean mu = bf16(exact mean) and the residual channel maximum
+  if (pblk) load_tile<D>(V + head, pblk, N, x);
+  else load_tile<D>(V + head + jrow, nullptr, kBlock, x);
+  float m[8];
   if (flags & 2u) {
-    double acc = 0.0;
-    for (int r = g; r < kBlock; r += G) acc += (double)tile[r * D + c];
-    part[threadIdx.x] = acc;
-    __syncthreads();
-    double t = 0.0;
-    for (int k = 0; k < G; k++) t += part[k * D + c];
-    uint16_t h = f64_to_bf16(t * (1.0 / kBlock));
-    m = bf16_to_f32(h);
-    if (g == 0) mu[((size_t)bh * nb + j) * D + c] = h;
-  } else if (mu != nullptr && g == 0) {
-    mu[((size_t)bh * nb + j) * D + c] = 0;
+    column_sums<D>(x, part, colsum);
+    for (int e = 0; e < 8; e++) m[e] = bf16_to_f32(f64_to_bf16(colsum[8 * chunk + e] * (1.0 / kBlock)));
+    if (threadIdx.x < D) mu[((size_t)bh * nb + j) * D + threadIdx.x] = f64_to_bf16(colsum[threadIdx.x] * (1.0 / kBlock));
+  } else {
+    for (int e = 0; e < 8; e++) m[e] = 0.0f;
+    if (mu != nullptr && threadIdx.x < D) mu[((size_t)bh * nb + j) * D + threadIdx.x] = 0;
   }
-  float a = 0.0f;
-  for (int r = g; r < kBlock; r += G) a = fmaxf(a, fabsf(tile[r * D + c] - m));
-  __syncthreads();
-  tile[threadIdx.x] = a;  // reuse: G partial maxima per channel
-  __syncthreads();
-  if (g == 0) {
-    float t = 0.0f;
-    for (int k = 0; k < G; k++) t = fmaxf(t, tile[k * D + c]);
-    vamax[((size_t)bh * nb + j) * D + c] = t;
+  for (int e = 0; e < 8; e++) {
+    float a = 0.0f;
+    for (int i = 0; i < RPT; i++) a = fmaxf(a, fabsf(x[i][e] - m[e]));
+    a = chunk_max_wave<D>(a);
+    if (lane < CH) pmax[w * D + 8 * chunk + e] = a;
   }
+  __syncthreads();
+  if (threadIdx.x < D)
+    vamax[((size_t)bh * nb + j) * D + threadIdx.x] =
+        fmaxf(fmaxf(pmax[threadIdx.x], pmax[D + threadIdx.x]), fmaxf(pmax[2 * D + threadIdx.x], pmax[3 * D + threadIdx.x]));
 }
 
+// Per (b,h): kbar = fl32(exact mean) of the keys, residual scale sV = fl32(amax/448) and
+// 448/amax. kQThreads threads: channel c = t % D, group t / D takes every G-th block.
 template <int D>
-__global__ __launch_bounds__(D) void quant_reduce(int N, uint32_t flags, const double* __restrict__ ksum,
-                                                  const float* __restrict__ vamax, float* __restrict__ kbar,
-                                                  float* __restrict__ sV, float* __restrict__ vinv) {
+__global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags, const double* __restrict__ ksum,
+                                                          const float* __restrict__ vamax, float* __restrict__ kbar,
+                                                          float* __restrict__ sV, float* __restrict__ vinv) {
+  constexpr int G = kQThreads / D;
+  __shared__ double ps[kQThreads];
+  __shared__ float pm[kQThreads];
   const int nb = N / kBlock;
-  const int bh = blockIdx.x, c = threadIdx.x;
-  float kb = 0.0f;
-  if (flags & 1u) {
-    double t = 0.0;
-    for (int j = 0; j < nb; j++) t += ksum[((size_t)bh * nb + j) * D + c];
-    kb = div_to_f32(t, (double)N);
+  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  double t0 = 0.0, t1 = 0.0;
+  float a0 = 0.0f, a1 = 0.0f;
+  int jb = g;
+  for (; jb + G < nb; jb += 2 * G) {  // two independent chains per thread
+    if (flags & 1u) {
+      t0 += ksum[((size_t)bh * nb + jb) * D + c];
+      t1 += ksum[((size_t)bh * nb + jb + G) * D + c];
+    }
+    a0 = fmaxf(a0, vamax[((size_t)bh * nb + jb) * D + c]);
+    a1 = fmaxf(a1, vamax[((size_t)bh * nb + jb + G) * D + c]);
   }
-  kbar[(size_t)bh * D + c] = kb;
-  float a = 0.0f;
-  for (int j = 0; j < nb; j++) a = fmaxf(a, vamax[((size_t)bh * nb + j) * D + c]);
-  float s, inv;
-  if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
-  sV[(size_t)bh * D + c] = s;
-  vinv[(size_t)bh * D + c] = inv;
+  if (jb < nb) {
+    if (flags & 1u) t0 += ksum[((size_t)bh * nb + jb) * D + c];
+    a0 = fmaxf(a0, vamax[((size_t)bh * nb + jb) * D + c]);
+  }
+  ps[threadIdx.x] = t0 + t1;
+  pm[threadIdx.x] = fmaxf(a0, a1);
+  __syncthreads();
+  if (g == 0) {
+    double t = 0.0;
+    float a = 0.0f;
+    for (int k = 0; k < G; k++) { t += ps[k * D + c]; a = fmaxf(a, pm[k * D + c]); }
+    kbar[(size_t)bh * D + c] = (flags & 1u) ? div_to_f32(t, (double)N) : 0.0f;
+    float s, inv;
+    if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
+    sV[(size_t)bh * D + c] = s;
+    vinv[(size_t)bh * D + c] = inv;
+  }
 }
 
 template <int D>
@@ -173,66 +218,77 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
                                                          uint8_t* __restrict__ Kq, float* __restrict__ sK,
                                                          uint8_t* __restrict__ Vq, float* __restrict__ mu_scaled,
                                                          uint16_t* __restrict__ mu_pack) {
-  __shared__ float tile[kBlock * D];
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
   __shared__ float red[4];
-  __shared__ uint8_t codes[D * kBlock];
   const int nb = N / kBlock;
   const int j = blockIdx.x, bh = blockIdx.y;
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D, jrow = (size_t)j * kBlock * D;
   const int32_t* pblk = perm ? perm + (size_t)bh * N + (size_t)j * kBlock : nullptr;
-  const size_t jrow = (size_t)j * kBlock * D;
+  const int chunk = threadIdx.x % CH, rg = threadIdx.x / CH;
+  float x[RPT][8];
 
   // ---- K~' = fl32(K[pi] - kbar), one scale per block, row-major codes
-  if (pblk) load_rows<D>(K + head, pblk, tile, N);
-  else load_rows<D>(K + head + jrow, nullptr, tile, kBlock);
-  __syncthreads();
   {
-    constexpr int EL = kBlock * D;
-    for (int i = threadIdx.x; i < EL; i += kQThreads) tile[i] = tile[i] - kbar[(size_t)bh * D + (i % D)];
+    const float4 k0 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + 8 * chunk);
+    const float4 k1 = *reinterpret_cast<const float4*>(kbar + (size_t)bh * D + 8 * chunk + 4);
+    const float kb[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+    if (pblk) load_tile<D>(K + head, pblk, N, x);
+    else load_tile<D>(K + head + jrow, nullptr, kBlock, x);
+    for (int i = 0; i < RPT; i++)
+      for (int e = 0; e < 8; e++) x[i][e] = x[i][e] - kb[e];
+    const float s = quant_rows<D>(x, Kq + head + jrow, red);
+    if (threadIdx.x == 0) sK[(size_t)bh * nb + j] = s;
   }
-  __syncthreads();
-  float s = quant_tile_rowmajor<D>(tile, Kq + head + jrow, red);
-  if (threadIdx.x == 0) sK[(size_t)bh * nb + j] = s;
-  __syncthreads();
 
-  // ---- residual codes of V'[block j], stored transposed: Vq[c][t]
-  if (pblk) load_rows<D>(V + head, pblk, tile, N);
-  else load_rows<D>(V + head + jrow, nullptr, tile, kBlock);
-  __syncthreads();
-  constexpr int G = kQThreads / D;
-  const int c = threadIdx.x % D, g = threadIdx.x / D;
-  const float m = (flags & 2u) ? bf16_to_f32(mu[((size_t)bh * nb + j) * D + c]) : 0.0f;
-  const float inv = vinv[(size_t)bh * D + c];
-  for (int r = g; r < kBlock; r += G) {
-    float rr = tile[r * D + c] - m;
-    codes[c * kBlock + r] = (uint8_t)e4m3_from_f32(rr * inv);
+  // ---- residual codes of V'[block j], block-transposed: Vq[c][t]; each thread stores the
+  // RPT consecutive tokens of its 8 channels
+  {
+    const float4 v0 = *reinterpret_cast<const float4*>(vinv + (size_t)bh * D + 8 * chunk);
+    const float4 v1 = *reinterpret_cast<const float4*>(vinv + (size_t)bh * D + 8 * chunk + 4);
+    const float inv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float m[8];
+    if (flags & 2u) unpack8(*reinterpret_cast<const uint4*>(mu + ((size_t)bh * nb + j) * D + 8 * chunk), m);
+    else for (int e = 0; e < 8; e++) m[e] = 0.0f;
+    if (pblk) load_tile<D>(V + head, pblk, N, x);
+    else load_tile<D>(V + head + jrow, nullptr, kBlock, x);
+    uint8_t* vb = Vq + head + jrow;
+    for (int e = 0; e < 8; e++) {
+      uint32_t wds[RPT / 4];
+      for (int k = 0; k < RPT / 4; k++)
+        wds[k] = e4m3x4_from_f32((x[4 * k + 0][e] - m[e]) * inv[e], (x[4 * k + 1][e] - m[e]) * inv[e],
+                                 (x[4 * k + 2][e] - m[e]) * inv[e], (x[4 * k + 3][e] - m[e]) * inv[e]);
+      uint8_t* dst = vb + (size_t)(8 * chunk + e) * kBlock + RPT * rg;
+      if (RPT == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(wds[0], wds[RPT / 4 - 1]);
+      else *reinterpret_cast<uint32_t*>(dst) = wds[0];
+    }
   }
-  const float ms = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
-  if (g == 0 && mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = ms;
-  if (g == 0 && mu_pack) {
-    // mean-restoration operand, laid out as the A operands of two v_mfma_f32_32x32x16_bf16
-    // per 32-channel block: [chunk of 8 key blocks][d-block][MFMA t][lane][8]. MFMA 0:
-    // lanes 0-31 and 32-63 hold bf16(ms); MFMA 1: lanes 0-31 bf16(ms - bf16(ms)), lanes
-    // 32-63 zero; lane l carries channel 32*d-block + l%32, element s key block 8*chunk + s.
-    const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 32, r = c % 32;
-    const uint16_t hi = f32_to_bf16(ms);
-    const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
-    uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 32) + db) * 2 * 64) * 8;
-    base[(r) * 8 + s8] = hi;
-    base[(32 + r) * 8 + s8] = hi;
-    base[(64 + r) * 8 + s8] = lo;
-    base[(96 + r) * 8 + s8] = 0;
-    if (j == nb - 1) {  // key blocks past the end of the last chunk contribute nothing
-      for (int t = s8 + 1; t < 8; t++) {
-        base[(r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(64 + r) * 8 + t] = 0; base[(96 + r) * 8 + t] = 0;
+
+  // ---- mu / sV, and the packed mean operand of the attention kernel
+  if (threadIdx.x < D) {
+    const int c = threadIdx.x;
+    const float m = (flags & 2u) ? bf16_to_f32(mu[((size_t)bh * nb + j) * D + c]) : 0.0f;
+    const float ms = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
+    if (mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = ms;
+    if (mu_pack) {
+      // mean-restoration operand, laid out as the A operands of two v_mfma_f32_32x32x16_bf16
+      // per 32-channel block: [chunk of 8 key blocks][d-block][MFMA t][lane][8]. MFMA 0:
+      // lanes 0-31 and 32-63 hold bf16(ms); MFMA 1: lanes 0-31 bf16(ms - bf16(ms)), lanes
+      // 32-63 zero; lane l carries channel 32*d-block + l%32, element s key block 8*chunk + s.
+      const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 32, r = c % 32;
+      const uint16_t hi = f32_to_bf16(ms);
+      const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
+      uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 32) + db) * 2 * 64) * 8;
+      base[(r) * 8 + s8] = hi;
+      base[(32 + r) * 8 + s8] = hi;
+      base[(64 + r) * 8 + s8] = lo;
+      base[(96 + r) * 8 + s8] = 0;
+      if (j == nb - 1) {  // key blocks past the end of the last chunk contribute nothing
+        for (int t = s8 + 1; t < 8; t++) {
+          base[(r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(64 + r) * 8 + t] = 0; base[(96 + r) * 8 + t] = 0;
+        }
       }
     }
   }
-  __syncthreads();
-  // contiguous copy-out of the D x 128 byte tile
-  uint4* dst = reinterpret_cast<uint4*>(Vq + head + jrow);
-  const uint4* srcv = reinterpret_cast<const uint4*>(codes);
-  for (int i = threadIdx.x; i < D * kBlock / 16; i += kQThreads) dst[i] = srcv[i];
 }
 
 }  // namespace vc
@@ -256,13 +312,13 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
   if (d == 128) {
     quant_stats<128><<<grid, kQThreads, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, N, flags, cL,
                                                 Qq, sQ, mup, ksum, vamax);
-    quant_reduce<128><<<BH, 128, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
+    quant_reduce<128><<<BH, kQThreads, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
     quant_apply<128><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
                                                 Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
   } else {
     quant_stats<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, N, flags, cL,
                                                Qq, sQ, mup, ksum, vamax);
-    quant_reduce<64><<<BH, 64, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
+    quant_reduce<64><<<BH, kQThreads, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
     quant_apply<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
                                                Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
   }
