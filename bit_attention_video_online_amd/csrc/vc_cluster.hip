@@ -13,7 +13,7 @@
 //              rigorous per-distance error bound, and a binary64 re-rank of every token
 //              whose best candidate is not separated from the rest by the bounds (exact
 //              for bf16 data of moderate dynamic range).
-//   cl_hist / cl_scan / cl_scatter   stable counting sort of the labels (pi)
+//   cl_hist / cl_scan_k / cl_scan_c / cl_scatter   stable counting sort of the labels (pi)
 //   cl_update  C_k = fl32(sum of members / count), binary64 sums in pi order
 // No atomics on floating-point data: every result is run-to-run deterministic.
 #include "vc_device.h"
@@ -237,43 +237,61 @@ __global__ __launch_bounds__(256) void cl_hist(const int32_t* __restrict__ label
   for (int k = threadIdx.x; k < K; k += 256) counts[((size_t)bh * K + k) * nch + ch] = hist[k];
 }
 
-// exclusive scan of counts in (k, chunk) order per head; cluster starts and sizes
-__global__ __launch_bounds__(1024) void cl_scan(const int32_t* __restrict__ counts, int K, int nch,
-                                                int32_t* __restrict__ offsets, int32_t* __restrict__ cstart,
-                                                int32_t* __restrict__ csize) {
+// Stable counting sort, scan part 1: one wave per cluster k scans the per-chunk counts of
+// k (chunk order) into offsets relative to the start of cluster k and writes the total.
+__global__ __launch_bounds__(256) void cl_scan_k(const int32_t* __restrict__ counts, int K, int nch,
+                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (k >= K) return;
+  const int32_t* cnt = counts + ((size_t)bh * K + k) * nch;
+  int32_t* off = offsets + ((size_t)bh * K + k) * nch;
+  const int per = (nch + 63) / 64;
+  const int a = min(nch, lane * per), b = min(nch, a + per);
+  int s = 0;
+  for (int i = a; i < b; i++) s += cnt[i];
+  int inc = s;  // inclusive wave scan of the per-lane sums
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o);
+    if (lane >= o) inc += v;
+  }
+  int run = inc - s;
+  for (int i = a; i < b; i++) {
+    off[i] = run;
+    run += cnt[i];
+  }
+  if (lane == 63) total[(size_t)bh * K + k] = inc;
+}
+
+// Scan part 2: cluster starts = exclusive scan of the totals (k order), sizes = totals.
+__global__ __launch_bounds__(1024) void cl_scan_c(const int32_t* __restrict__ total, int K, int32_t* __restrict__ cstart,
+                                                  int32_t* __restrict__ csize) {
   __shared__ int part[1024];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const size_t total = (size_t)K * nch;
-  const size_t per = (total + 1023) / 1024;
-  const size_t a = tid * per, b = min(total, a + per);
-  const int32_t* cnt = counts + (size_t)bh * total;
-  int32_t* off = offsets + (size_t)bh * total;
+  const int per = (K + 1023) / 1024;
+  const int a = min(K, tid * per), b = min(K, a + per);
+  const int32_t* tt = total + (size_t)bh * K;
   int s = 0;
-  for (size_t i = a; i < b; i++) s += cnt[i];
+  for (int i = a; i < b; i++) s += tt[i];
   part[tid] = s;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
-    int v = (tid >= o) ? part[tid - o] : 0;
+    const int v = (tid >= o) ? part[tid - o] : 0;
     __syncthreads();
     part[tid] += v;
     __syncthreads();
   }
-  int run = part[tid] - s;  // exclusive prefix of this thread's range
-  for (size_t i = a; i < b; i++) {
-    off[i] = run;
-    run += cnt[i];
-  }
-  __syncthreads();
-  for (int k = tid; k < K; k += 1024) {
-    cstart[(size_t)bh * K + k] = off[(size_t)k * nch];
-    int z = 0;
-    for (int c = 0; c < nch; c++) z += cnt[(size_t)k * nch + c];
-    csize[(size_t)bh * K + k] = z;
+  int run = part[tid] - s;
+  for (int i = a; i < b; i++) {
+    cstart[(size_t)bh * K + i] = run;
+    csize[(size_t)bh * K + i] = tt[i];
+    run += tt[i];
   }
 }
 
 __global__ __launch_bounds__(256) void cl_scatter(const int32_t* __restrict__ labels, int N, int K, int nch,
-                                                  const int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+                                                  const int32_t* __restrict__ offsets, const int32_t* __restrict__ cstart,
+                                                  int32_t* __restrict__ perm) {
   __shared__ int lab[kChunk];
   const int ch = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int t = ch * kChunk + tid;
@@ -285,22 +303,44 @@ __global__ __launch_bounds__(256) void cl_scatter(const int32_t* __restrict__ la
     const int z = lab[tid];
     int rank = 0;
     for (int i = 0; i < tid; i++) rank += (lab[i] == z);
-    perm[(size_t)bh * N + offsets[((size_t)bh * K + z) * nch + ch] + rank] = t;
+    perm[(size_t)bh * N + cstart[(size_t)bh * K + z] + offsets[((size_t)bh * K + z) * nch + ch] + rank] = t;
   }
 }
 
-__global__ void cl_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                          const int32_t* __restrict__ cstart, const int32_t* __restrict__ csize, int N, int K, int D,
-                          float* __restrict__ C) {
-  const int k = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
+// C_k = fl32(exact mean of the member rows). 128 threads: the D channels in 16-byte
+// chunks (D/8 threads per row) times 128*8/D row groups that take every G-th member;
+// exact binary64 partial sums are combined in LDS (order-independent).
+template <int D>
+__global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 const int32_t* __restrict__ cstart, const int32_t* __restrict__ csize,
+                                                 int N, int K, float* __restrict__ C) {
+  constexpr int CH = D / 8, G = 128 / CH;
+  __shared__ double part[G][D];
+  const int k = blockIdx.x, bh = blockIdx.y;
   const int n = csize[(size_t)bh * K + k];
   if (n == 0) return;  // empty cluster keeps its centroid
   const int s0 = cstart[(size_t)bh * K + k];
   const uint16_t* Vh = V + (size_t)bh * N * D;
-  const int32_t* ph = perm + (size_t)bh * N;
-  double s = 0.0;
-  for (int i = 0; i < n; i++) s += (double)bf16_to_f32(Vh[(size_t)ph[s0 + i] * D + c]);
-  C[((size_t)bh * K + k) * D + c] = div_to_f32(s, (double)n);
+  const int32_t* ph = perm + (size_t)bh * N + s0;
+  const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int i = g; i < n; i += G) {
+    int row = ph[i];
+    row = ((unsigned)row < (unsigned)N) ? row : 0;
+    const uint4 raw = *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int e = 0; e < 4; e++) {
+      acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+      acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+  for (int e = 0; e < 8; e++) part[g][8 * chunk + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += 128) {
+    double s = 0.0;
+    for (int q = 0; q < G; q++) s += part[q][c];
+    C[((size_t)bh * K + k) * D + c] = div_to_f32(s, (double)n);
+  }
 }
 
 }  // namespace vc
@@ -310,7 +350,7 @@ using namespace vc;
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K) {
   const size_t BH = (size_t)B * H, nch = ((size_t)N + kChunk - 1) / kChunk;
   return BH * K * d * sizeof(float) + BH * K * sizeof(float) + 2 * BH * K * nch * sizeof(int32_t) +
-         2 * BH * K * sizeof(int32_t) + 1024;
+         3 * BH * K * sizeof(int32_t) + 1024;
 }
 
 extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int K, int iters, int cold, float* C,
@@ -323,7 +363,8 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
   int32_t* counts = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
   int32_t* offs = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
   int32_t* cstart = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
-  int32_t* csize = (int32_t*)w;
+  int32_t* csize = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
+  int32_t* ctotal = (int32_t*)w;
   if (cold) cl_cold<<<dim3(K, BH), d, 0, st>>>(V, C, N, K, d);
   const dim3 gmf(N / 128, BH), gch(nch, BH), gk(K, BH);
   for (int it = 0; it < iters; it++) {
@@ -331,9 +372,11 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
     if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
     else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
     cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
-    cl_scan<<<BH, 1024, 0, st>>>(counts, K, nch, offs, cstart, csize);
-    cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, perm);
-    cl_update<<<gk, d, 0, st>>>(V, perm, cstart, csize, N, K, d, C);
+    cl_scan_k<<<dim3((K + 3) / 4, BH), 256, 0, st>>>(counts, K, nch, offs, ctotal);
+    cl_scan_c<<<BH, 1024, 0, st>>>(ctotal, K, cstart, csize);
+    cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, cstart, perm);
+    if (d == 128) cl_update<128><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
+    else cl_update<64><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
