@@ -44,30 +44,12 @@ __global__ void cl_prep(const float* __restrict__ C, float* __restrict__ chat, f
   }
 }
 
-// record for the per-token best / bound tracking
-struct Cand {
-  float d;   // best distance' (|c|^2 - 2 v.c)
-  float e;   // its error bound
-  float lb;  // min over the other clusters of (distance' - bound)
+// per-token record of one lane group: best distance' d1, its bounds lo1 = d1 - e1 and
+// hi1 = d1 + e1, L = min over the group's other centroids of d_k - e_k, and the index
+struct Best {
+  float d1, lo1, hi1, L;
   int k;
 };
-
-__device__ __forceinline__ void cand_push(Cand& c, float d, float e, int k) {
-  if (d < c.d || (d == c.d && k < c.k)) {
-    c.lb = fminf(c.lb, c.d - c.e);
-    c.d = d; c.e = e; c.k = k;
-  } else {
-    c.lb = fminf(c.lb, d - e);
-  }
-}
-__device__ __forceinline__ void cand_merge(Cand& a, const Cand& b) {
-  if (b.d < a.d || (b.d == a.d && b.k < a.k)) {
-    float lb = fminf(fminf(a.lb, b.lb), a.d - a.e);
-    a.d = b.d; a.e = b.e; a.k = b.k; a.lb = lb;
-  } else {
-    a.lb = fminf(fminf(a.lb, b.lb), b.d - b.e);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Assignment on the matrix cores. S^T = chat V^T with v_mfma_f32_16x16x32_bf16: the
@@ -89,8 +71,8 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   constexpr int ROWB = 2 * D + 16;      // padded LDS row stride (bytes)
   constexpr int CCH = 64;               // centroids per chunk
   __shared__ __attribute__((aligned(16))) uint8_t Cs[CCH * ROWB];
-  __shared__ float cn_s[CCH], ca_s[CCH];
-  __shared__ Cand rec[128][4];
+  __shared__ float cn_s[CCH], ea_s[CCH], eb_s[CCH];
+  __shared__ Best rec[128][4];
   __shared__ int unsure[128];
   __shared__ int n_unsure;
   __shared__ double red_d[256];
@@ -128,8 +110,19 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   }
   const float u = 5.9604645e-8f;  // 2^-24
   const float gam = (float)D * u / (1.0f - (float)D * u);
-  Cand cand[2];
-  for (int g = 0; g < 2; g++) cand[g] = Cand{__builtin_inff(), 0.0f, __builtin_inff(), 0x7fffffff};
+  // Every computed distance' d_k is within e_k = 2(2 gamma |v||c_k| + u(|c_k|^2 + |d_k|))
+  // of its exact value (bf16 products are exact; the accumulation error is inside the
+  // binary32 bound). Per token and lane group the loop tracks, branch-free, the best d1 with
+  // its index, lo1 = d1 - e1 and hi1 = d1 + e1, and L = min over the other centroids of
+  // d_k - e_k; L > hi1 proves the best index exact. A lane group meets its centroids in
+  // increasing index order, so only a strictly smaller distance replaces the best.
+  float d1[2], lo1[2], hi1[2], L[2];
+  int kbest[2];
+  for (int g = 0; g < 2; g++) {
+    d1[g] = __builtin_inff(); lo1[g] = __builtin_inff(); hi1[g] = __builtin_inff(); L[g] = __builtin_inff();
+    kbest[g] = 0x7fffffff;
+  }
+  const float twou = 2.0f * u;
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int k0 = 0; k0 < K; k0 += CCH) {
@@ -148,11 +141,14 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
       }
       *reinterpret_cast<uint4*>(Cs + k * ROWB + 2 * c8) = w;
     }
+    // per-centroid bound terms e_k = A_k |v| + B_k + 2u |d_k|; padding past K gets zero rows
+    // and a huge finite norm, so its distance never wins and no bound overflows
     if (tid < CCH) {
       const bool ok = k0 + tid < K;
-      const float cnk = ok ? Nh[k0 + tid] : 0.0f;
-      cn_s[tid] = ok ? cnk : __builtin_inff();
-      ca_s[tid] = sqrtf(cnk) * 1.0001f;
+      const float cnk = ok ? Nh[k0 + tid] : 3.0e38f;
+      cn_s[tid] = cnk;
+      ea_s[tid] = ok ? 4.0f * gam * (sqrtf(cnk) * 1.0001f) : 0.0f;
+      eb_s[tid] = twou * cnk + 1e-30f;
     }
     __syncthreads();
     for (int cb = 0; cb < CCH / 16; cb++) {
@@ -164,25 +160,37 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
       }
       for (int i = 0; i < 4; i++) {
         const int kl = 16 * cb + 4 * lg + i;
-        const float cnk = cn_s[kl];
-        if (!(cnk < __builtin_inff())) continue;  // padding past K
-        const float cabs = ca_s[kl];
+        const float cnk = cn_s[kl], ea = ea_s[kl], eb = eb_s[kl];
         for (int g = 0; g < 2; g++) {
-          const float dd = cnk - 2.0f * acc[g][i];
-          const float e = 2.0f * (2.0f * gam * vn[g] * cabs + u * (cnk + fabsf(dd))) + 1e-30f;
-          cand_push(cand[g], dd, e, k0 + kl);
+          const float dd = __builtin_fmaf(-2.0f, acc[g][i], cnk);  // exact scaling, one rounding
+          const float e = __builtin_fmaf(twou, fabsf(dd), __builtin_fmaf(ea, vn[g], eb));
+          const float lo = dd - e;
+          const bool better = dd < d1[g];
+          L[g] = fminf(L[g], better ? lo1[g] : lo);
+          lo1[g] = better ? lo : lo1[g];
+          hi1[g] = better ? dd + e : hi1[g];
+          d1[g] = better ? dd : d1[g];
+          kbest[g] = better ? k0 + kl : kbest[g];
         }
       }
     }
   }
   // merge the four lane groups of each token through LDS
   if (tid == 0) n_unsure = 0;
-  for (int g = 0; g < 2; g++) rec[wave * 32 + g * 16 + r16][lg] = cand[g];
+  for (int g = 0; g < 2; g++) rec[wave * 32 + g * 16 + r16][lg] = Best{d1[g], lo1[g], hi1[g], L[g], kbest[g]};
   __syncthreads();
   if (tid < 128) {
-    Cand a = rec[tid][0];
-    for (int x = 1; x < 4; x++) cand_merge(a, rec[tid][x]);
-    if (a.lb > a.d + a.e) {
+    Best a = rec[tid][0];
+    for (int x = 1; x < 4; x++) {
+      const Best& o = rec[tid][x];
+      if (o.d1 < a.d1 || (o.d1 == a.d1 && o.k < a.k)) {
+        a.L = fminf(fminf(a.L, o.L), a.lo1);
+        a.d1 = o.d1; a.lo1 = o.lo1; a.hi1 = o.hi1; a.k = o.k;
+      } else {
+        a.L = fminf(fminf(a.L, o.L), o.lo1);
+      }
+    }
+    if (a.L > a.hi1) {
       labels[(size_t)bh * N + t0 + tid] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
     } else {
       unsure[atomicAdd(&n_unsure, 1)] = tid;
