@@ -7,7 +7,7 @@ resident in HBM before the timed region. `value` is attention-equivalent TFLOPS 
 whole step, 4*B*H*N^2*d / t_step; the per-stage times and the attention kernel's own
 TFLOPS (from HIP events on the launch stream) are reported beside it.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -85,6 +85,76 @@ def cpu_baseline(host, K_clusters, sample_rows, threads):
                 seconds_measured=round(t4 - t1, 2), warm_start_seconds=round(t1 - t0, 2))
 
 
+def run_schedule(args):
+    """The 20-step amortised schedule on Wan-shaped inputs (seed 3): Q and K fixed, V drifts
+    each step as V_s = bf16(V_{s-1} + xi * |V_{s-1}|), xi ~ N(0, 0.05^2) drawn with a seeded
+    CUDA generator (stream state per step). Clustering runs at steps 0-4 (step 0 cold with 4
+    iterations, steps 1-4 warm with 2) and steps 5-19 reuse step 4's permutation; every step
+    quantises and runs attention. Reports per-step stage times, the clustering share
+    sum t(cluster) / sum [t(quantize) + t(attention)], and the error against binary64 exact
+    attention (oracle) on sampled rows of head 0."""
+    import numpy as np
+    import torch
+    import synth
+    import oracle
+    import bit_attention_video_online_amd as vc
+
+    w = synth.WORKLOADS["schedule"]
+    B, H, N, d, Kc, seed, S = 1, w["H"], w["N"], w["d"], w["clusters"], w["seed"], w["steps"]
+    torch.cuda.set_device(0)
+    dev, host = make_inputs("schedule", B, H, N, d, seed)
+    Qd, Kd, V = dev["Q"], dev["K"], dev["V"].clone()
+    C = torch.zeros((B, H, Kc, d), dtype=torch.float32, device="cuda")
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    ws_c = vc.workspace(vc.vc_cluster_workspace_bytes(B, H, N, d, Kc))
+    q = vc.quantize_outputs(B, H, N, d)
+    ws_q = vc.workspace(vc.vc_quantize_workspace_bytes(B, H, N, d))
+    O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    flags_q = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
+    rows = np.linspace(0, N - 1, args.schedule_rows).astype(np.int32)
+    Qh, Kh = host["Q"][0, 0], host["K"][0, 0]
+    gen = torch.Generator(device="cuda")
+    steps = []
+    for s in range(S):
+        if s > 0:
+            gen.manual_seed(seed * 1000 + s)
+            xi = torch.randn(V.shape, generator=gen, device="cuda", dtype=torch.float32) * 0.05
+            Vf = V.float()
+            V = (Vf + xi * Vf.abs()).to(torch.bfloat16)
+            del xi, Vf
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record()
+        if s == 0:
+            vc.vc_cluster(V, Kc, 4, True, C, lab, perm, ws=ws_c)
+        elif s <= 4:
+            vc.vc_cluster(V, Kc, 2, False, C, lab, perm, ws=ws_c)
+        ev[1].record()
+        vc.vc_quantize(Qd, Kd, V, perm, flags_q, q, ws=ws_q)
+        ev[2].record()
+        vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+        ev[3].record()
+        torch.cuda.synchronize()
+        tc, tq, ta = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
+        Vh = V[0, 0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        O_ex = oracle.attention_exact(Qh, Kh, Vh, rows)
+        Og = O[0, 0][torch.from_numpy(rows).long().cuda()].float().cpu().numpy().astype(np.float64)
+        rmse = float(np.linalg.norm(Og - O_ex) / np.linalg.norm(O_ex))
+        steps.append(dict(step=s, cluster_ms=round(tc, 3), quantize_ms=round(tq, 3), attention_ms=round(ta, 3),
+                          rmse=round(rmse, 6)))
+        log("[schedule] step %2d: cluster %.3f ms, quantize %.3f ms, attention %.3f ms, rMSE %.4f%%"
+            % (s, tc, tq, ta, 100 * rmse))
+    t_c = sum(x["cluster_ms"] for x in steps)
+    t_qa = sum(x["quantize_ms"] + x["attention_ms"] for x in steps)
+    res = {"workload": "20-step amortised schedule, B=%d H=%d N=%d d=%d, %d clusters; cluster at steps 0-4 "
+                       "(cold x4, then warm x2), permutation of step 4 reused for steps 5-19" % (B, H, N, d, Kc),
+           "clustering_share": round(t_c / t_qa, 5), "cluster_ms_total": round(t_c, 3),
+           "quantize_attention_ms_total": round(t_qa, 3),
+           "rmse_rows": "head 0, %d rows evenly spaced, vs binary64 exact attention (oracle)" % rows.size,
+           "steps": steps}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +164,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
+    ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -110,6 +181,10 @@ def main():
         print("bench.py: this build runs on exactly one GPU; the path shards by (batch, head) with no exchange, "
               "but multi-GPU runs are not part of it (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "schedule":
+        run_schedule(args)
+        return
 
     import torch
     import bit_attention_video_online_amd as vc
