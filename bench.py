@@ -7,7 +7,8 @@ resident in HBM before the timed region. `value` is attention-equivalent TFLOPS 
 whole step, 4*B*H*N^2*d / t_step; the per-stage times and the attention kernel's own
 TFLOPS (from HIP events on the launch stream) are reported beside it.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule] [--no-cpu-baseline]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule|oracle]
+                       [--no-cpu-baseline] [--attention-only [--attn-mode vc|expcast|exp]]
 """
 from __future__ import annotations
 
@@ -22,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "FP8 VC-attention TFLOPS & % FP8 MFMA peak at N=70,400,H=40,d=128"
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (published)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA (published)
 HBM_PEAK_GBS = 8000.0
 BETA = -0.35
 
@@ -85,6 +87,132 @@ def cpu_baseline(host, K_clusters, sample_rows, threads):
                 seconds_measured=round(t4 - t1, 2), warm_start_seconds=round(t1 - t0, 2))
 
 
+def exact_attention_rows(Qr, K, V):
+    """softmax(Q K^T / sqrt(d)) V in binary64 for a few query rows (torch, on the device)."""
+    import torch
+    s = torch.mm(Qr, K.t().contiguous()) / (Qr.shape[1] ** 0.5)
+    p = torch.softmax(s, dim=1)
+    return p @ V
+
+
+def device_info():
+    """Name, compute units and the maximum shader clock the runtime reports for device 0."""
+    import ctypes
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    info = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None), "compute_units": prop.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:  # hipDeviceAttributeClockRate (kHz)
+            info["max_clock_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    return info
+
+
+def stage_rates(B, H, N, d, Kc, iters, avg):
+    """Algorithmic bytes (and k-means FLOPs) per stage launch and the rates they give.
+
+    quantiser, single-pass minimum: read Q, K, V (bf16) and the permutation; write the three
+    code tensors, the Q/K block scales, the channel scales, mu (bf16), mu / s_V (fp32) and
+    the matrix-core mean operand (bf16 hi/lo). The two-pass design re-reads K and V.
+    k-means, per iteration: V read by the assignment and again by the centroid update,
+    labels and permutation written once and read once, centroids read and written;
+    assignment FLOPs 2 N K d per head (bf16 matrix core)."""
+    nb = N // 128
+    e = B * H * N * d
+    quant = 3 * e * 2 + B * H * N * 4 + 3 * e + 2 * B * H * nb * 4 + B * H * d * 4 + B * H * nb * d * (2 + 4) \
+        + B * H * ((nb + 7) // 8) * d * 2 * 2 * 2 * 8
+    quant_two_pass = quant + 2 * e * 2
+    clus = iters * (2 * e * 2 + 2 * 2 * B * H * N * 4 + 2 * B * H * Kc * d * 4)
+    clus_flops = iters * 2.0 * B * H * N * Kc * d
+    out = {}
+    if avg.get("quantize"):
+        t = avg["quantize"] / 1e3
+        out["quantize"] = {"algorithmic_bytes": quant, "gbps": round(quant / t / 1e9, 1),
+                           "two_pass_bytes": quant_two_pass, "two_pass_gbps": round(quant_two_pass / t / 1e9, 1),
+                           "frac_hbm_peak": round(quant / t / 1e9 / HBM_PEAK_GBS, 4)}
+    if avg.get("cluster"):
+        t = avg["cluster"] / 1e3
+        out["cluster"] = {"algorithmic_bytes": clus, "gbps": round(clus / t / 1e9, 1),
+                          "frac_hbm_peak": round(clus / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "assign_flops": clus_flops, "assign_tflops": round(clus_flops / t / 1e12, 2),
+                          "frac_bf16_peak": round(clus_flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def _oracle_c0():
+    """The tiny configuration through the oracle in full: k-means (8 clusters, 4 cold
+    iterations), quantiser, ExpCast attention emulation on all 1024 rows. Seconds per stage."""
+    import numpy as np
+    import synth
+    import oracle
+    w = synth.gen("tiny")
+    Q, K, V = (w[k][0, 0] for k in ("Q", "K", "V"))
+    t0 = time.perf_counter()
+    _, perm, _ = oracle.kmeans(V, 8, 4, cold=True)
+    t1 = time.perf_counter()
+    q = oracle.quantize(Q, K, V, perm, oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
+    t2 = time.perf_counter()
+    oracle.attention_emul(q, np.arange(Q.shape[0], dtype=np.int32), beta=BETA, mode=oracle.MODE_EXPCAST)
+    t3 = time.perf_counter()
+    return {"kmeans_s": round(t1 - t0, 4), "quantize_s": round(t2 - t1, 4), "attention_s": round(t3 - t2, 4),
+            "total_s": round(t3 - t0, 4), "threads": oracle.num_threads()}
+
+
+def run_oracle_timing(args):
+    """Oracle (CPU, not tuned) timings on the small configurations in full: tiny (B=1 H=1
+    N=1024 d=128, whole VC path) with all host threads and with one thread, and the
+    ExpCast-only configuration (B=1 H=8 N=8192 d=128: K smoothing, no V-Smooth, identity
+    permutation) with all host threads. A reported baseline, not a target."""
+    import subprocess
+    import numpy as np
+    import synth
+    import oracle
+    if args.workload == "oracle-c0":
+        print(json.dumps(_oracle_c0()), flush=True)
+        return
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    res = {"workload": "oracle timing on the tiny and ExpCast-only configurations in full", "cpu": cpu,
+           "nproc": os.cpu_count(), "omp_threads": oracle.num_threads()}
+    c0 = _oracle_c0()
+    c0["tflops_equiv"] = round(4.0 * 1024 * 1024 * 128 / c0["total_s"] / 1e12, 6)
+    res["tiny_all_threads"] = c0
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    out = subprocess.run([sys.executable, os.path.abspath(__file__), "--workload", "oracle-c0"], env=env,
+                         capture_output=True, text=True, check=True)
+    c0s = json.loads(out.stdout.strip().splitlines()[-1])
+    c0s["tflops_equiv"] = round(4.0 * 1024 * 1024 * 128 / c0s["total_s"] / 1e12, 6)
+    res["tiny_one_thread"] = c0s
+    w = synth.WORKLOADS["expcast"]
+    H, N, d = w["H"], w["N"], w["d"]
+    tq = ta = 0.0
+    for h in range(H):
+        g = synth.gen("expcast", heads=[h])
+        Q, K, V = (g[k][0, 0] for k in ("Q", "K", "V"))
+        t0 = time.perf_counter()
+        q = oracle.quantize(Q, K, V, None, oracle.FLAG_KSMOOTH)
+        t1 = time.perf_counter()
+        oracle.attention_emul(q, np.arange(N, dtype=np.int32), beta=BETA, mode=oracle.MODE_EXPCAST)
+        t2 = time.perf_counter()
+        tq += t1 - t0
+        ta += t2 - t1
+        log("[oracle] expcast head %d: quantise %.2f s, attention %.2f s" % (h, t1 - t0, t2 - t1))
+    res["expcast_all_threads"] = {"quantize_s": round(tq, 3), "attention_s": round(ta, 3),
+                                  "total_s": round(tq + ta, 3),
+                                  "tflops_equiv": round(4.0 * H * N * N * d / (tq + ta) / 1e12, 6),
+                                  "threads": oracle.num_threads()}
+    print(json.dumps(res), flush=True)
+
+
 def run_schedule(args):
     """The 20-step amortised schedule on Wan-shaped inputs (seed 3): Q and K fixed, V drifts
     each step as V_s = bf16(V_{s-1} + xi * |V_{s-1}|), xi ~ N(0, 0.05^2) drawn with a seeded
@@ -92,11 +220,10 @@ def run_schedule(args):
     iterations, steps 1-4 warm with 2) and steps 5-19 reuse step 4's permutation; every step
     quantises and runs attention. Reports per-step stage times, the clustering share
     sum t(cluster) / sum [t(quantize) + t(attention)], and the error against binary64 exact
-    attention (oracle) on sampled rows of head 0."""
+    attention (computed with torch on the device) on sampled rows of head 0."""
     import numpy as np
     import torch
     import synth
-    import oracle
     import bit_attention_video_online_amd as vc
 
     w = synth.WORKLOADS["schedule"]
@@ -113,7 +240,9 @@ def run_schedule(args):
     O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
     flags_q = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
     rows = np.linspace(0, N - 1, args.schedule_rows).astype(np.int32)
-    Qh, Kh = host["Q"][0, 0], host["K"][0, 0]
+    rows_t = torch.from_numpy(rows).long().cuda()
+    Qr = Qd[0, 0][rows_t].double()
+    Kh = Kd[0, 0].double()
     gen = torch.Generator(device="cuda")
     steps = []
     for s in range(S):
@@ -136,10 +265,8 @@ def run_schedule(args):
         ev[3].record()
         torch.cuda.synchronize()
         tc, tq, ta = (ev[i].elapsed_time(ev[i + 1]) for i in range(3))
-        Vh = V[0, 0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        O_ex = oracle.attention_exact(Qh, Kh, Vh, rows)
-        Og = O[0, 0][torch.from_numpy(rows).long().cuda()].float().cpu().numpy().astype(np.float64)
-        rmse = float(np.linalg.norm(Og - O_ex) / np.linalg.norm(O_ex))
+        O_ex = exact_attention_rows(Qr, Kh, V[0, 0].double())
+        rmse = float(torch.linalg.norm(O[0, 0][rows_t].double() - O_ex) / torch.linalg.norm(O_ex))
         steps.append(dict(step=s, cluster_ms=round(tc, 3), quantize_ms=round(tq, 3), attention_ms=round(ta, 3),
                           rmse=round(rmse, 6)))
         log("[schedule] step %2d: cluster %.3f ms, quantize %.3f ms, attention %.3f ms, rMSE %.4f%%"
@@ -150,7 +277,8 @@ def run_schedule(args):
                        "(cold x4, then warm x2), permutation of step 4 reused for steps 5-19" % (B, H, N, d, Kc),
            "clustering_share": round(t_c / t_qa, 5), "cluster_ms_total": round(t_c, 3),
            "quantize_attention_ms_total": round(t_qa, 3),
-           "rmse_rows": "head 0, %d rows evenly spaced, vs binary64 exact attention (oracle)" % rows.size,
+           "rmse_rows": "head 0, %d rows evenly spaced, vs binary64 softmax(Q K^T / sqrt(d)) V from the bf16 "
+                        "inputs" % rows.size,
            "steps": steps}
     print(json.dumps(res), flush=True)
 
@@ -164,6 +292,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
+    ap.add_argument("--attn-mode", default="vc", choices=["vc", "expcast", "exp"],
+                    help="with --attention-only: vc = V-Smooth + ExpCast (the path); expcast = ExpCast bytes "
+                         "without mean restoration; exp = exp-then-cast probabilities without mean restoration "
+                         "(instruction-count comparison of the probability stage)")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
@@ -184,6 +316,9 @@ def main():
 
     if args.workload == "schedule":
         run_schedule(args)
+        return
+    if args.workload in ("oracle", "oracle-c0"):
+        run_oracle_timing(args)
         return
 
     import torch
@@ -218,12 +353,16 @@ def main():
 
     ev = {k: [] for k in ("cluster", "quantize", "attention")}
 
+    mode = args.attn_mode if args.attention_only else "vc"
+    attn_flags = 0 if mode == "exp" else vc.VC_F_EXPCAST
+    attn_restore = mode == "vc"
+
     def step(record):
         if args.attention_only:
             if record:
                 e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+            vc.vc_attention(q, O, beta=BETA, flags=attn_flags, restore_mean=attn_restore)
             if record:
                 e1.record(); ev["attention"].append((e0, e1))
             return
@@ -270,6 +409,10 @@ def main():
                    "parallelism": "single GPU"},
         "stage_ms": {k: (round(v, 3) if v is not None else None) for k, v in avg.items()},
         "attention_tflops": round(att_tflops, 2),
+        "quantize_attention_tflops": (round(flops / ((avg["quantize"] + avg["attention"]) / 1e3) / 1e12, 2)
+                                      if avg["quantize"] else None),
+        "stage_rates": stage_rates(B, H, N, d, Kc, 2, avg),
+        "device": device_info(),
         "attention_pct_fp8_peak": round(100.0 * att_tflops / FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": profiled_traffic(),
@@ -277,7 +420,11 @@ def main():
                      "kernel": "attn_fwd<128,ExpCast,restore>", "algorithmic_flops_per_launch": flops},
     }
     if args.attention_only:
-        res["config"]["workload"] += " (attention kernel only)"
+        res["config"]["workload"] += " (attention kernel only%s)" % {
+            "vc": "", "expcast": ", ExpCast without mean restoration",
+            "exp": ", exp-then-cast probabilities, no mean restoration"}[mode]
+        res["roofline"]["kernel"] = {"vc": "attn_fwd<128,ExpCast,restore>", "expcast": "attn_fwd<128,ExpCast>",
+                                     "exp": "attn_fwd<128,exp-then-cast>"}[mode]
     if not args.no_cpu_baseline and not args.attention_only:
         import oracle
         log("[bench] timing the CPU oracle on a bounded sample ...")

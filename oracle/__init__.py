@@ -89,7 +89,7 @@ def lib() -> ctypes.CDLL:
         _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
         _lib.or_quantize.restype = I
         _lib.or_quantize.argtypes = [P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
-        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P]
+        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P]
         _lib.or_attention_exact.argtypes = [P, P, P, I, I, I, P, P]
         _lib.or_exact_mean.restype = ctypes.c_double
         _lib.or_exact_mean.argtypes = [P, L, I]
@@ -213,25 +213,64 @@ def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOT
 
 # ---------------------------------------------------------------- attention
 def attention_emul(q: dict, rows, beta: float = -0.35, mode: int = MODE_EXPCAST, restore_mean: bool = True,
-                   dump_block: int = -1, want_m: bool = False):
+                   dump_block: int = -1, want_m: bool = False, want_weights: bool = False):
     """Online-softmax emulation on the given query rows. Returns O [rows, d] (binary64)
-    and, when dump_block >= 0, the probability bytes of that key block [rows, 128]."""
+    and, when dump_block >= 0, the probability bytes of that key block [rows, 128]; with
+    want_m the running max after each key block [rows, N/128]; with want_weights the
+    effective weight of every key in the output [rows, N] (keys in the quantised order):
+    the decoded probability times 2^(m'_j - m'_final) / l, binary64."""
     rows = _c(rows, np.int32)
     N, d = q["Qq"].shape
     O = np.empty((rows.size, d), np.float64)
     dump = np.zeros((rows.size, BLOCK), np.uint8) if dump_block >= 0 else None
     mm = np.zeros((rows.size, N // BLOCK), np.float32) if want_m else None
+    W = np.zeros((rows.size, N), np.float64) if want_weights else None
     mu = q["mu_scaled"] if (restore_mean and (q["flags"] & FLAG_VSMOOTH)) else None
     lib().or_attention_emul(_p(q["Qq"]), _p(q["sQ"]), _p(q["Kq"]), _p(q["sK"]), _p(q["Vq"]), _p(q["sV"]),
                             None if mu is None else _p(_c(mu, np.float32)), N, d, float(np.float32(beta)),
                             int(mode), rows.size, _p(rows), _p(O), int(dump_block),
-                            None if dump is None else _p(dump), None if mm is None else _p(mm))
+                            None if dump is None else _p(dump), None if mm is None else _p(mm),
+                            None if W is None else _p(W))
     res = [O]
     if dump is not None:
         res.append(dump)
     if mm is not None:
         res.append(mm)
+    if W is not None:
+        res.append(W)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def error_terms(Q_bits, K_bits, V_bits, q: dict, perm, rows, beta: float = -0.35, mode: int = MODE_EXPCAST):
+    """Split the emulated output's error into a probability term and a value term.
+
+    With P the exact softmax probabilities (binary64 from the bf16 inputs), W the effective
+    key weights of the quantised path and V_q the values it actually multiplies
+    (s_V * (dec(R_q) + mu/s_V), or s_V * dec(V_q) without V-Smooth), both in the quantised
+    key order, O_q - O = (W - P) V + W (V_q - V). Returns the two terms and O_q - O for the
+    given rows (each [rows, d]); the terms sum to the third up to binary64 rounding.
+    Requires a path whose row sum is the sum of the probabilities it multiplies the values
+    by (ExpCast, unquantised probabilities), or no mean restoration (exp-then-cast
+    without V-Smooth)."""
+    rows = _c(rows, np.int32)
+    N, d = q["Qq"].shape
+    vs = bool(q["flags"] & FLAG_VSMOOTH)
+    if mode == MODE_EXP_THEN_CAST and vs:
+        raise ValueError("error_terms: exp-then-cast with mean restoration has two row sums")
+    O_q, W = attention_emul(q, rows, beta=beta, mode=mode, want_weights=True)
+    order = np.arange(N) if perm is None else np.asarray(perm, np.int64)
+    Qf = bf16_bits_to_f32(_c(Q_bits, np.uint16)[rows]).astype(np.float64)
+    Kf = bf16_bits_to_f32(_c(K_bits, np.uint16)[order]).astype(np.float64)
+    Vf = bf16_bits_to_f32(_c(V_bits, np.uint16)[order]).astype(np.float64)
+    s = Qf @ Kf.T / np.sqrt(d)
+    P = np.exp(s - s.max(axis=1, keepdims=True))
+    P /= P.sum(axis=1, keepdims=True)
+    Vq = e4m3_decode(q["Vq"]).astype(np.float64)
+    if vs:
+        Vq = Vq + np.repeat(q["mu_scaled"].astype(np.float64), BLOCK, axis=0)
+    Vq *= q["sV"].astype(np.float64)[None, :]
+    O = P @ Vf
+    return (W - P) @ Vf, W @ (Vq - Vf), O_q - O, O
 
 
 def attention_exact(Q_bits, K_bits, V_bits, rows) -> np.ndarray:

@@ -493,7 +493,8 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
                        int N, int d, float beta, int mode,
                        int nrows, const int32_t* rows, double* O /* [nrows, d] */,
                        int dump_block, uint8_t* dump_codes /* [nrows, 128] or NULL */,
-                       float* dump_m /* [nrows, N/128] running max after each block, or NULL */) {
+                       float* dump_m /* [nrows, N/128] running max after each block, or NULL */,
+                       double* weights /* [nrows, N] effective weight of each key in O, or NULL */) {
   int nb = N / 128;
   const float C0 = 120.0f + beta;
   /* decoded operand tables as exact integers */
@@ -505,6 +506,7 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
     int32_t* qu = (int32_t*)malloc(sizeof(int32_t) * d);
     float* acc = (float*)malloc(sizeof(float) * 128);
     double* A = (double*)malloc(sizeof(double) * d);
+    double* mblk = weights ? (double*)malloc(sizeof(double) * nb) : NULL;
     int32_t pu[128];
     double pt[128];
 #pragma omp for schedule(dynamic, 1)
@@ -550,6 +552,11 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
           r += pt[t];
         }
         l = alpha * l + r;
+        if (weights) { /* probability that multiplies the value of key t (before the final scaling) */
+          for (int t = 0; t < 128; t++)
+            weights[(int64_t)ri * N + j * 128 + t] = mode == 2 ? pt[t] : ldexp((double)pu[t], -9);
+          mblk[j] = mp;
+        }
         for (int c = 0; c < d; c++) {
           double pv;
           if (mode == 2) {
@@ -567,8 +574,13 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
         if (dump_m) dump_m[(int64_t)ri * nb + j] = mp;
       }
       for (int c = 0; c < d; c++) O[(int64_t)ri * d + c] = (double)sV[c] * A[c] / l;
+      if (weights) /* block j's terms reach the end scaled by the product of the later alphas */
+        for (int j = 0; j < nb; j++) {
+          double f = exp2(mblk[j] - m) / l;
+          for (int t = 0; t < 128; t++) weights[(int64_t)ri * N + j * 128 + t] *= f;
+        }
     }
-    free(qu); free(acc); free(A);
+    free(qu); free(acc); free(A); free(mblk);
   }
   free(Ku);
   free(Vu);
