@@ -36,6 +36,12 @@ FLAG_VSMOOTH = 2
 MODE_EXPCAST = 0
 MODE_EXP_THEN_CAST = 1
 MODE_EXACT_PROB = 2
+MODE_EXPCAST_E5M2 = 3
+# ExpCast offsets: the pages print -0.35 for E4M3; for E5M2 (an extension the paper page's
+# future directions name) the same minimax centring of the mantissa error
+# eps2(m) = m - 4 log2(1 + m/4) over m in [0, 4) gives -0.172, taken to two digits.
+BETA_E4M3 = -0.35
+BETA_E5M2 = -0.17
 BLOCK = 128
 
 # which test pins each oracle function (tests/test_oracle_*.py)
@@ -80,6 +86,7 @@ def lib() -> ctypes.CDLL:
         _lib.or_e4m3_encode.argtypes = [F]
         _lib.or_e4m3_encode_array.argtypes = [P, P, L]
         _lib.or_e4m3_decode_array.argtypes = [P, P, L]
+        _lib.or_e5m2_decode_array.argtypes = [P, P, L]
         _lib.or_expcast.restype = ctypes.c_uint8
         _lib.or_expcast.argtypes = [F, F, F]
         _lib.or_expcast_array.argtypes = [P, P, P, P, L]
@@ -128,6 +135,13 @@ def e4m3_decode(codes) -> np.ndarray:
     c = _c(codes, np.uint8)
     out = np.empty(c.shape, np.float64)
     lib().or_e4m3_decode_array(_p(c), _p(out), c.size)
+    return out
+
+
+def e5m2_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().or_e5m2_decode_array(_p(c), _p(out), c.size)
     return out
 
 
@@ -257,6 +271,7 @@ def error_terms(Q_bits, K_bits, V_bits, q: dict, perm, rows, beta: float = -0.35
     vs = bool(q["flags"] & FLAG_VSMOOTH)
     if mode == MODE_EXP_THEN_CAST and vs:
         raise ValueError("error_terms: exp-then-cast with mean restoration has two row sums")
+
     O_q, W = attention_emul(q, rows, beta=beta, mode=mode, want_weights=True)
     order = np.arange(N) if perm is None else np.asarray(perm, np.int64)
     Qf = bf16_bits_to_f32(_c(Q_bits, np.uint16)[rows]).astype(np.float64)

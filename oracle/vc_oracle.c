@@ -216,6 +216,25 @@ void or_e4m3_decode_array(const uint8_t* b, double* out, int64_t n) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* OCP E5M2 (bias 15, 2 mantissa bits, exponent 31 = infinity / NaN, max    */
+/* 57344). The paper page's future directions name E5M2 as a format to carry */
+/* ExpCast to, with its own affine coefficients and bound; as an integer, a  */
+/* positive normal E5M2 byte is 4 log2 v + 60 + eps2(m),                      */
+/* eps2(m) = m - 4 log2(1 + m/4).                                             */
+/* ------------------------------------------------------------------------ */
+double or_e5m2_decode(uint8_t b) {
+  int s = b >> 7, e = (b >> 2) & 31, m = b & 3;
+  double v;
+  if (e == 31) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -16);     /* subnormal: m * 2^-16 */
+  else v = ldexp(1.0 + m / 4.0, e - 15);          /* normal: (1+m/4) * 2^(e-15) */
+  return s ? -v : v;
+}
+void or_e5m2_decode_array(const uint8_t* b, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; i++) out[i] = or_e5m2_decode(b[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* ExpCast-FP8 (paper page, method step (4); news page, ExpCast section).    */
 /* For a log2-domain score u = (s - m') log2 e <= 0 the byte is             */
 /* clip(Round(8(u+8) + 56 + beta), 0, 120), read as E4M3. With the score    */
@@ -477,11 +496,20 @@ int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const i
 /*        c = e4m3(fl32(256 P)), p = dec(c), row-sum term 256 P              */
 /* mode 2 (no probability quantisation): p = 256 * 2^(fl32(sigma acc) - m')  */
 /*        in binary64, row-sum term p                                       */
+/* mode 3 (ExpCast with E5M2 bytes, the extension the paper page's future    */
+/*        directions name): c = clamp(rne(fma(acc, 4 sigma,                 */
+/*        fl32(C0 - 4 m'))), 0, 120) with C0 = fl32(120 + beta), read as     */
+/*        E5M2 (code 120 = 2^15 at u = 0), p = dec(c), row-sum term p        */
 /*   r = sum_t (row-sum term);  l = alpha l + r                             */
 /*   A = alpha A + sum_t p_t dec(Rq_t) + r mu_scaled_j                       */
 /* O = sV * A / l (binary64). A and l are binary64.                          */
 /* Optionally the codes of block `dump_block` for each row are written out.  */
 /* ------------------------------------------------------------------------ */
+static inline int64_t e5m2_units(uint8_t b) { /* value * 2^16 of a finite code, exact integer */
+  int e = (b >> 2) & 31, m = b & 3;
+  int64_t v = e == 0 ? m : ((int64_t)(4 + m) << (e - 1));
+  return (b >> 7) ? -v : v;
+}
 static inline int32_t e4m3_units(uint8_t b) { /* value * 2^9, exact integer */
   int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
   int32_t v = e == 0 ? m : ((8 + m) << (e - 1));
@@ -507,7 +535,7 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
     float* acc = (float*)malloc(sizeof(float) * 128);
     double* A = (double*)malloc(sizeof(double) * d);
     double* mblk = weights ? (double*)malloc(sizeof(double) * nb) : NULL;
-    int32_t pu[128];
+    int64_t pu[128];
     double pt[128];
 #pragma omp for schedule(dynamic, 1)
     for (int ri = 0; ri < nrows; ri++) {
@@ -529,14 +557,16 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
         float mnew = sigma * mx;
         float mp = (float)m > mnew ? (float)m : mnew; /* m is always a binary32 value */
         double alpha = (m == -INFINITY) ? 0.0 : exp2((double)((float)m) - (double)mp);
-        float bias = C0 - 8.0f * mp;
-        float s8 = 8.0f * sigma;
+        /* ExpCast slope: 8 codes per octave for E4M3, 4 for E5M2 (mode 3) */
+        float slope = mode == 3 ? 4.0f : 8.0f;
+        float bias = C0 - slope * mp;
+        float s8 = slope * sigma;
         double r = 0.0;
         for (int t = 0; t < 128; t++) {
-          if (mode == 0) {
+          if (mode == 0 || mode == 3) {
             uint8_t code = or_expcast(acc[t], s8, bias);
-            pu[t] = e4m3_units(code);
-            pt[t] = ldexp((double)pu[t], -9);
+            pu[t] = mode == 0 ? e4m3_units(code) : e5m2_units(code);
+            pt[t] = ldexp((double)pu[t], mode == 0 ? -9 : -16);
             if (dump_codes && j == dump_block) dump_codes[(int64_t)ri * 128 + t] = code;
           } else if (mode == 1) {
             float u = sigma * acc[t] - mp;
@@ -554,7 +584,7 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
         l = alpha * l + r;
         if (weights) { /* probability that multiplies the value of key t (before the final scaling) */
           for (int t = 0; t < 128; t++)
-            weights[(int64_t)ri * N + j * 128 + t] = mode == 2 ? pt[t] : ldexp((double)pu[t], -9);
+            weights[(int64_t)ri * N + j * 128 + t] = mode == 1 ? ldexp((double)pu[t], -9) : pt[t];
           mblk[j] = mp;
         }
         for (int c = 0; c < d; c++) {
@@ -563,9 +593,11 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
             pv = 0.0;
             for (int t = 0; t < 128; t++) pv += pt[t] * ldexp((double)Vu[(int64_t)(j * 128 + t) * d + c], -9);
           } else {
-            int64_t b = 0; /* exact: codes and residual bytes are multiples of 2^-9 */
-            for (int t = 0; t < 128; t++) b += (int64_t)pu[t] * Vu[(int64_t)(j * 128 + t) * d + c];
-            pv = ldexp((double)b, -18);
+            /* exact: E4M3 codes and residual bytes are multiples of 2^-9, E5M2 codes of
+             * 2^-16; |sum| < 128 * 2^31 * 2^18 fits in 64 bits */
+            int64_t b = 0;
+            for (int t = 0; t < 128; t++) b += pu[t] * Vu[(int64_t)(j * 128 + t) * d + c];
+            pv = ldexp((double)b, mode == 3 ? -25 : -18);
           }
           double mu = mu_scaled ? (double)mu_scaled[(int64_t)j * d + c] : 0.0;
           A[c] = alpha * A[c] + pv + r * mu;

@@ -35,3 +35,12 @@ def round_half_even(x: Fraction) -> int:
     if rem < Fraction(1, 2):
         return fl
     return fl if fl % 2 == 0 else fl + 1
+
+
+def e5m2_value(code: int) -> Fraction:
+    """Value of a finite OCP E5M2 byte from its fields (1 sign, 5 exponent bits with bias 15, 2 mantissa bits)."""
+    s, e, m = code >> 7, (code >> 2) & 31, code & 3
+    if e == 31:
+        raise ValueError("infinity or NaN")
+    v = Fraction(m, 1 << 16) if e == 0 else Fraction(4 + m, 4) * Fraction(2) ** (e - 15)
+    return -v if s else v
