@@ -8,7 +8,7 @@ whole step, 4*B*H*N^2*d / t_step; the per-stage times and the attention kernel's
 TFLOPS (from HIP events on the launch stream) are reported beside it.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule|oracle]
-                       [--no-cpu-baseline] [--attention-only [--attn-mode vc|expcast|exp]]
+                       [--no-cpu-baseline] [--attention-only [--attn-mode vc|vc_e5m2|expcast|exp]]
 """
 from __future__ import annotations
 
@@ -26,6 +26,7 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA (published)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16 MFMA (published)
 HBM_PEAK_GBS = 8000.0
 BETA = -0.35
+BETA_E5M2 = -0.17              # minimax offset of the E5M2 ExpCast code
 
 
 def log(*a):
@@ -292,10 +293,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
-    ap.add_argument("--attn-mode", default="vc", choices=["vc", "expcast", "exp"],
-                    help="with --attention-only: vc = V-Smooth + ExpCast (the path); expcast = ExpCast bytes "
-                         "without mean restoration; exp = exp-then-cast probabilities without mean restoration "
-                         "(instruction-count comparison of the probability stage)")
+    ap.add_argument("--attn-mode", default="vc", choices=["vc", "vc_e5m2", "expcast", "exp"],
+                    help="with --attention-only: vc = V-Smooth + ExpCast (the path); vc_e5m2 = the same with "
+                         "E5M2 probability bytes; expcast = ExpCast bytes without mean restoration; exp = "
+                         "exp-then-cast probabilities without mean restoration (instruction-count comparison of "
+                         "the probability stage)")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
@@ -354,15 +356,17 @@ def main():
     ev = {k: [] for k in ("cluster", "quantize", "attention")}
 
     mode = args.attn_mode if args.attention_only else "vc"
-    attn_flags = 0 if mode == "exp" else vc.VC_F_EXPCAST
-    attn_restore = mode == "vc"
+    attn_flags = {"vc": vc.VC_F_EXPCAST, "vc_e5m2": vc.VC_F_EXPCAST | vc.VC_F_E5M2, "expcast": vc.VC_F_EXPCAST,
+                  "exp": 0}[mode]
+    attn_beta = BETA_E5M2 if mode == "vc_e5m2" else BETA
+    attn_restore = mode in ("vc", "vc_e5m2")
 
     def step(record):
         if args.attention_only:
             if record:
                 e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            vc.vc_attention(q, O, beta=BETA, flags=attn_flags, restore_mean=attn_restore)
+            vc.vc_attention(q, O, beta=attn_beta, flags=attn_flags, restore_mean=attn_restore)
             if record:
                 e1.record(); ev["attention"].append((e0, e1))
             return
@@ -421,10 +425,10 @@ def main():
     }
     if args.attention_only:
         res["config"]["workload"] += " (attention kernel only%s)" % {
-            "vc": "", "expcast": ", ExpCast without mean restoration",
+            "vc": "", "vc_e5m2": ", E5M2 ExpCast bytes (beta -0.17)", "expcast": ", ExpCast without mean restoration",
             "exp": ", exp-then-cast probabilities, no mean restoration"}[mode]
-        res["roofline"]["kernel"] = {"vc": "attn_fwd<128,ExpCast,restore>", "expcast": "attn_fwd<128,ExpCast>",
-                                     "exp": "attn_fwd<128,exp-then-cast>"}[mode]
+        res["roofline"]["kernel"] = {"vc": "attn_fwd<128,ExpCast,restore>", "vc_e5m2": "attn_fwd<128,ExpCast-E5M2,restore>",
+                                     "expcast": "attn_fwd<128,ExpCast>", "exp": "attn_fwd<128,exp-then-cast>"}[mode]
     if not args.no_cpu_baseline and not args.attention_only:
         import oracle
         log("[bench] timing the CPU oracle on a bounded sample ...")

@@ -15,7 +15,7 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
-                                   float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
+                                   float beta, int pmode, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
 extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
                                  hipStream_t st);
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
@@ -140,7 +140,9 @@ static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint
                                   void* stream) {
   if (!Qq || !sQ || !Kq || !sK || !Vq || !sV || !O) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
-  if (!isfinite(beta) || (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST))) return VC_E_PARAM;
+  if (!isfinite(beta) || (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_E5M2)))
+    return VC_E_PARAM;
+  if ((flags & VC_F_E5M2) && !(flags & VC_F_EXPCAST)) return VC_E_PARAM;  // E5M2 bytes exist only as ExpCast
   const void* ptrs[] = {Qq, sQ, Kq, sK, Vq, sV, mu_pack, O, codes};
   for (const void* p : ptrs)
     if (!aligned16(p)) return VC_E_UNSUPPORTED;
@@ -153,7 +155,8 @@ static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
-  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, (flags & VC_F_EXPCAST) ? 1 : 0,
+  const int pmode = (flags & VC_F_EXPCAST) ? ((flags & VC_F_E5M2) ? 2 : 1) : 0;
+  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, pmode,
                           (uint16_t*)O, dump_block, codes, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;

@@ -143,13 +143,19 @@ __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f7
 //   O^T (d x queries) += V_j^T P^T with the same instruction (K = 64 keys per half).
 //   Mean restoration: O^T[c][q] += r_q mu~_j[c], accumulated on the matrix core once
 //   per 8 key blocks (bf16 hi/lo split, v_mfma_f32_32x32x16_bf16).
-template <int D, bool EXPCAST, bool RESTORE, bool DUMP>
+// PM selects the probability bytes: 0 exp-then-cast (E4M3), 1 ExpCast E4M3 (8 codes per
+// octave, code 120 = 2^8), 2 ExpCast E5M2 (4 codes per octave, code 120 = 2^15; the PV and
+// row-sum MFMAs read their B operand as BF8).
+template <int D, int PM, bool RESTORE, bool DUMP>
 __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
                                                          const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
                                                          const uint8_t* __restrict__ Vq, const float* __restrict__ sV,
                                                          const uint16_t* __restrict__ mu_pack, int N, int total,
                                                          float C0, uint16_t* __restrict__ O, int dump_block,
                                                          uint8_t* __restrict__ dump) {
+  constexpr bool EXPCAST = PM != 0;
+  constexpr int PFMT = PM == 2 ? 1 : 0;         // MFMA operand format of the bytes: FP8 or BF8
+  constexpr float SLOPE = PM == 2 ? 4.0f : 8.0f; // ExpCast codes per octave
   constexpr int TILE = kBlock * D;              // bytes per K (or V) tile
   constexpr int NCH = TILE / 16;                // 16-byte chunks per tile
   constexpr int PW = NCH / kAThreads;           // chunks per thread per tile (4 or 2)
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     for (int db = 0; db < NDB; db++) {
       const int vo = 32 * db * 128;
       const v8i a = ld_frag(vt + A0 + vo, vt + B0 + vo);
-      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, oacc[db], 0, 0, 0, 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, oacc[db], 0, PFMT, 0, 0, 0, 0);
     }
   };
 
@@ -358,8 +364,9 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     float r = 0.0f;
     v4f rs;
     // ExpCast bytes: cvt_pk_u8_f32 rounds half-even and saturates to [0, 255] (NaN -> 0), so
-    // clamp(rne(t), 0, 120) = min(cvt(t), 120). For |m'| < 2^16 every t = fma(S, 8 sigma, bias)
-    // stays below 120.5 and the min is idle; otherwise (uniform per wave, rare) a packed
+    // clamp(rne(t), 0, 120) = min(cvt(t), 120). For |m'| < 2^16 every t = fma(S, SLOPE sigma,
+    // bias) stays below 120.5 (for either slope, C0 <= 120 and the roundings of m' and of the
+    // bias add less than 0.05) and the min is idle; otherwise (uniform per wave, rare) a packed
     // per-byte min fixes the operand before its MFMAs read it.
     const bool fix = EXPCAST && __ballot(fabsf(mp) >= 65536.0f);
     auto bytes_half = [&](int kh) {
@@ -367,8 +374,8 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
         for (int qd = 0; qd < 4; qd++) {
           uint32_t w = 0;
           if (EXPCAST) {
-            const float bias = C0 - 8.0f * mp;
-            const float s8 = 8.0f * sigma;
+            const float bias = C0 - SLOPE * mp;
+            const float s8 = SLOPE * sigma;
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 0], s8, bias), 0, w);
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 1], s8, bias), 1, w);
             w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 2], s8, bias), 2, w);
@@ -391,8 +398,8 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     s_part(Other{}, 0);  // K_{j+1} (stale, and unused, after the last tile)
     bytes_half(1);
     if (EXPCAST) {  // row sum of the decoded bytes on the matrix core
-      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[0], zero4, 0, 0, 0, 0, 0, 0);
-      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[1], rs, 0, 0, 0, 0, 0, 0);
+      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[0], zero4, 0, PFMT, 0, 0, 0, 0);
+      rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pf[1], rs, 0, PFMT, 0, 0, 0, 0);
     }
     pv_part(vt, 1, pf[1]);
     s_part(Other{}, 2);
@@ -447,44 +454,49 @@ __global__ void expcast_kernel(const float* __restrict__ acc, const float* __res
   if (i < n) out[i] = (uint8_t)expcast_byte(acc[i], s8[i], bias[i], 0u, 0);
 }
 
-template <int D, bool E, bool R, bool DU>
+template <int D, int PM, bool R, bool DU>
 static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
                         const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                         uint8_t* dump, hipStream_t st) {
   const int total = BH * ((N / kBlock + kQB - 1) / kQB);
-  attn_fwd<D, E, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
+  attn_fwd<D, PM, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
 }
 
-template <int D, bool E, bool R>
+template <int D, int PM>
 static void launch_attn_d(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
                           const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                           uint8_t* dump, hipStream_t st) {
-  if (dump) launch_attn<D, E, R, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-  else launch_attn<D, E, R, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  if (mu) {
+    if (dump) launch_attn<D, PM, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn<D, PM, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  } else {
+    if (dump) launch_attn<D, PM, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn<D, PM, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  }
+}
+
+template <int D>
+static void launch_attn_pm(int pmode, const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
+                           const uint8_t* Vq, const float* sV, const uint16_t* mu, int BH, int N, float C0,
+                           uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
+  if (pmode == 2) launch_attn_d<D, 2>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else if (pmode == 1) launch_attn_d<D, 1>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else launch_attn_d<D, 0>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
 }
 
 }  // namespace vc
 
 using namespace vc;
 
+// pmode: 0 exp-then-cast, 1 ExpCast E4M3, 2 ExpCast E5M2
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
-                                   float beta, int expcast, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
+                                   float beta, int pmode, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
   const uint16_t* mu = (const uint16_t*)mu_pack;
   const int BH = B * H;
   const float C0 = 120.0f + beta;  // fl32(120 + beta)
-  const bool R = mu != nullptr;
-  if (d == 128) {
-    if (expcast) { if (R) launch_attn_d<128, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-                   else launch_attn_d<128, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
-    else { if (R) launch_attn_d<128, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-           else launch_attn_d<128, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
-  } else {
-    if (expcast) { if (R) launch_attn_d<64, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-                   else launch_attn_d<64, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
-    else { if (R) launch_attn_d<64, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-           else launch_attn_d<64, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st); }
-  }
+  if (d == 128) launch_attn_pm<128>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else launch_attn_pm<64>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

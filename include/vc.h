@@ -54,7 +54,8 @@ enum {
 enum {
   VC_F_KSMOOTH = 1u, /* subtract the per-channel key mean over all N tokens */
   VC_F_VSMOOTH = 2u, /* block-mean removal of V' and mean restoration */
-  VC_F_EXPCAST = 4u  /* ExpCast-FP8 probability bytes (else exp2 then cast) */
+  VC_F_EXPCAST = 4u, /* ExpCast-FP8 probability bytes (else exp2 then cast) */
+  VC_F_E5M2 = 8u     /* with VC_F_EXPCAST: the bytes are E5M2 (4 codes per octave) */
 };
 
 /* Static description of a status code (host function, never NULL). */
@@ -137,7 +138,12 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
  * For each query row i and every 128-key block j in ascending order:
  *   S = Qq_i . Kq_j^T on FP8 matrix cores (binary32 accumulation),
  *   sigma = fl32(sQ[i/128] * sK[j]),  m' = max(m, fl32(sigma * max S)),
- *   VC_F_EXPCAST: c = clamp(rne(fma(S, 8 sigma, fl32(fl32(120 + beta) - 8 m'))), 0, 120)
+ *   VC_F_EXPCAST: c = clamp(rne(fma(S, 8 sigma, fl32(fl32(120 + beta) - 8 m'))), 0, 120),
+ *                 read as E4M3 (code 120 = 2^8 at u = 0)
+ *   VC_F_EXPCAST | VC_F_E5M2 (ExpCast carried to E5M2, a direction the paper page's
+ *                 future work names): c = clamp(rne(fma(S, 4 sigma,
+ *                 fl32(fl32(120 + beta) - 4 m'))), 0, 120), read as E5M2 (code 120 =
+ *                 2^15 at u = 0); the minimax offset for this format is beta = -0.17
  *   otherwise:    c = e4m3(256 * exp2(fl32(sigma S) - m')),
  *   r = row sum of the probabilities, l = 2^(m - m') l + r,
  *   A = 2^(m - m') A + c . Vq_j + r * mu_scaled_j   (mu term only if mu_pack != NULL),
@@ -146,8 +152,9 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
  * error ~2^-16 of that term).
  *
  *   O      bf16 [B,H,N,d] output; must not overlap any input
- *   beta   finite; the pages use -0.35
- *   flags  VC_F_EXPCAST selects ExpCast; other bits ignored
+ *   beta   finite; the pages use -0.35 (E4M3)
+ *   flags  VC_F_EXPCAST selects ExpCast, VC_F_E5M2 its E5M2 variant (VC_E_PARAM without
+ *          VC_F_EXPCAST); VC_F_KSMOOTH / VC_F_VSMOOTH are ignored, other bits VC_E_PARAM
  * ------------------------------------------------------------------------ */
 vc_status vc_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                        const uint8_t* Vq, const float* sV, const void* mu_pack,

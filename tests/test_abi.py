@@ -85,6 +85,8 @@ def test_attention_rejects_bad_arguments(L):
     assert _attn(L, beta=float("nan")) == 3
     assert _attn(L, beta=float("inf")) == 3
     assert _attn(L, flags=1 << 8) == 3
+    assert _attn(L, flags=8) == 3          # E5M2 bytes exist only as ExpCast
+    assert _attn(L, flags=8 | 3) == 3
     assert _attn(L, O=FAKE) == 7
     assert _attn(L, Vq=ctypes.c_void_p((4 << 20) + 8)) == 5
 

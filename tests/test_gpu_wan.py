@@ -23,7 +23,7 @@ from tests.gpu_util import bf16_bits, mu_pack_expected, rel_l2, to_dev_bf16, vq_
 
 HEADS = (0, 23)
 KC = 550
-BETA = -0.35
+BETA = oracle.BETA_E4M3
 
 
 @pytest.fixture(scope="module")
@@ -54,12 +54,14 @@ def run():
     vc.vc_attention(qp, Op, beta=BETA, flags=0, restore_mean=False)
     Oe = torch.empty_like(O)
     vc.vc_attention(qp, Oe, beta=BETA, flags=vc.VC_F_EXPCAST, restore_mean=False)
+    O5 = torch.empty_like(O)  # the VC path with E5M2 ExpCast bytes
+    vc.vc_attention(q, O5, beta=oracle.BETA_E5M2, flags=vc.VC_F_EXPCAST | vc.VC_F_E5M2)
     torch.cuda.synchronize()
     print("[wan] GPU path done in %.1fs" % (time.time() - t0), flush=True)
     res = dict(w=w, Cw=Cw.cpu().numpy(), C=C.cpu().numpy(), lab=lab.cpu().numpy(), perm=perm.cpu().numpy(),
                q={k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in q.items()},
-               O=bf16_bits(O), Ovs=bf16_bits(Ovs), Op=bf16_bits(Op), Oe=bf16_bits(Oe))
-    del Q, K, V, Vp, q, qp, O, Op, Ovs, Oe
+               O=bf16_bits(O), Ovs=bf16_bits(Ovs), Op=bf16_bits(Op), Oe=bf16_bits(Oe), O5=bf16_bits(O5))
+    del Q, K, V, Vp, q, qp, O, Op, Ovs, Oe, O5
     torch.cuda.empty_cache()
     return res
 
@@ -119,18 +121,24 @@ def test_wan_attention_sampled_rows(run, oracle_heads):
     w = run["w"]
     N = w["Q"].shape[2]
     rng = np.random.default_rng(77)
-    errs = []
-    e = {k: [] for k in ("vc", "vsmooth", "plain", "expcast")}
+    errs, errs5 = [], []
+    e = {k: [] for k in ("vc", "vsmooth", "plain", "expcast", "vc_e5m2")}
     for h in HEADS:
         rows = np.sort(rng.choice(N, 64, replace=False)).astype(np.int32)
         O_em = oracle.attention_emul(oracle_heads[h]["q"], rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+        O_em5 = oracle.attention_emul(oracle_heads[h]["q"], rows, beta=oracle.BETA_E5M2,
+                                      mode=oracle.MODE_EXPCAST_E5M2)
         got = lambda key: synth.bf16_to_f32(run[key][0, h][rows]).astype(np.float64)
         errs.append(rel_l2(got("O"), O_em))
+        errs5.append(rel_l2(got("O5"), O_em5))
         O_ex = oracle.attention_exact(w["Q"][0, h], w["K"][0, h], w["V"][0, h], rows)
-        for k, key in (("vc", "O"), ("vsmooth", "Ovs"), ("plain", "Op"), ("expcast", "Oe")):
+        for k, key in (("vc", "O"), ("vsmooth", "Ovs"), ("plain", "Op"), ("expcast", "Oe"), ("vc_e5m2", "O5")):
             e[k].append(rel_l2(got(key), O_ex))
     m = {k: float(np.mean(v)) for k, v in e.items()}
-    print("[wan] rel-L2 vs emulation %s; rMSE vs exact %s" % (errs, m), flush=True)
+    print("[wan] rel-L2 vs emulation %s (E5M2 %s); rMSE vs exact %s" % (errs, errs5, m), flush=True)
     assert max(errs) <= 2e-3
+    # E5M2 bytes: one code step is 2^(1/4), so a byte moved by the matrix core's score
+    # rounding weighs (2^(1/4) - 1) / (2^(1/8) - 1) = 2.09 times as much as with E4M3
+    assert max(errs5) <= 2e-3 * (2 ** 0.25 - 1) / (2 ** 0.125 - 1)
     assert m["vsmooth"] < m["plain"]
     assert m["vc"] < m["expcast"]
