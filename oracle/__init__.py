@@ -33,6 +33,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 FLAG_KSMOOTH = 1
 FLAG_VSMOOTH = 2
+FLAG_HADAMARD = 16
 MODE_EXPCAST = 0
 MODE_EXP_THEN_CAST = 1
 MODE_EXACT_PROB = 2
@@ -96,6 +97,9 @@ def lib() -> ctypes.CDLL:
         _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
         _lib.or_quantize.restype = I
         _lib.or_quantize.argtypes = [P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
+        _lib.or_quantize_ex.argtypes = [P, P, P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
+        _lib.or_rope.argtypes = [P, P, P, I, I, P]
+        _lib.or_fwht_rows.argtypes = [P, I, I]
         _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P]
         _lib.or_attention_exact.argtypes = [P, P, P, I, I, I, P, P]
         _lib.or_exact_mean.restype = ctypes.c_double
@@ -200,8 +204,28 @@ def kmeans(V_bits: np.ndarray, K: int, iters: int, cold: bool, C: np.ndarray | N
 
 
 # ---------------------------------------------------------------- quantiser
-def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOTH) -> dict:
-    """Fused quantiser for one head. All outputs row-major; Vq rows are in permuted order."""
+def rope(x_bits, cos_t, sin_t) -> np.ndarray:
+    """RoPE on interleaved channel pairs with binary32 tables [N, d/2]; bf16 result."""
+    x = _c(x_bits, np.uint16)
+    N, d = x.shape
+    out = np.empty_like(x)
+    lib().or_rope(_p(x), _p(_c(cos_t, np.float32)), _p(_c(sin_t, np.float32)), N, d, _p(out))
+    return out
+
+
+def fwht_rows(x) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform of every row (binary32, fixed stage order)."""
+    a = np.array(x, dtype=np.float32, order="C", copy=True)
+    rows, d = a.shape
+    lib().or_fwht_rows(_p(a), rows, d)
+    return a
+
+
+def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOTH, rope_cos=None,
+             rope_sin=None) -> dict:
+    """Fused quantiser for one head. All outputs row-major; Vq rows are in permuted order.
+    With rope_cos/rope_sin ([N, d/2] binary32) Q and K are rotated first; FLAG_HADAMARD
+    applies the Q/K Hadamard rotation before quantisation."""
     Q = _c(Q_bits, np.uint16)
     K = _c(K_bits, np.uint16)
     V = _c(V_bits, np.uint16)
@@ -215,8 +239,10 @@ def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOT
         mu=np.zeros((nb, d), np.uint16), mu_scaled=np.zeros((nb, d), np.float32),
         kbar=np.empty(d, np.float32),
     )
-    rc = lib().or_quantize(_p(Q), _p(K), _p(V), None if pm is None else _p(pm), N, d, int(flags),
-                           float(log2e_over_sqrt_d(d)),
+    rc_, rs_ = (None, None) if rope_cos is None else (_c(rope_cos, np.float32), _c(rope_sin, np.float32))
+    rc = lib().or_quantize_ex(_p(Q), _p(K), _p(V), None if pm is None else _p(pm),
+                              None if rc_ is None else _p(rc_), None if rs_ is None else _p(rs_), N, d, int(flags),
+                              float(log2e_over_sqrt_d(d)),
                            _p(out["Qq"]), _p(out["sQ"]), _p(out["Kq"]), _p(out["sK"]), _p(out["Vq"]),
                            _p(out["sV"]), _p(out["mu"]), _p(out["mu_scaled"]), _p(out["kbar"]))
     if rc != 0:

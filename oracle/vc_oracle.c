@@ -408,12 +408,71 @@ static void quant_block(const float* x, int rows, int d, uint8_t* codes, float* 
   for (int64_t i = 0; i < (int64_t)rows * d; i++) codes[i] = or_e4m3_encode(x[i] * inv);
 }
 
-int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
-                int N, int d, int flags, float cL,
-                uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
-                uint16_t* mu, float* mu_scaled, float* kbar_out) {
+/* ------------------------------------------------------------------------ */
+/* Preprocessing that the pages' fused quantiser absorbs (paper page, core   */
+/* method: the fused kernel takes in RoPE, the mean, the gather, the         */
+/* Hadamard rotation and the quantiser).                                     */
+/* Reading (RoPE): interleaved channel pairs (2i, 2i+1) of token t rotated by */
+/* the caller's angle, cos/sin tables [N, d/2] in binary32:                  */
+/*   x'_2i = fl32(fl32(x_2i c) - fl32(x_2i+1 s)),                            */
+/*   x'_2i+1 = fl32(fl32(x_2i s) + fl32(x_2i+1 c)),                           */
+/* then rounded to bf16 -- the tensor the unfused chain would hand over.     */
+/* Reading (Hadamard): the unnormalised Sylvester matrix H_d (entries +-1) on */
+/* the channels of every Q row and every smoothed K row, as the fast         */
+/* Walsh-Hadamard transform: stages h = 1, 2, 4, ..., d/2 in that order, each */
+/* pair (i, i+h) with i & h == 0 becoming (fl32(a+b), fl32(a-b)). Since       */
+/* (Q H)(K H)^T = d Q K^T, the factor 1/d is folded exactly into sQ'.        */
+/* ------------------------------------------------------------------------ */
+static void rope_row(const uint16_t* in, const float* c, const float* s, int d, uint16_t* out) {
+  for (int i = 0; i < d / 2; i++) {
+    float a = bf16_val(in[2 * i]), b = bf16_val(in[2 * i + 1]);
+    float ac = a * c[i], bs = b * s[i], as = a * s[i], bc = b * c[i];
+    out[2 * i] = f32_to_bf16(ac - bs);
+    out[2 * i + 1] = f32_to_bf16(as + bc);
+  }
+}
+
+void or_rope(const uint16_t* x, const float* cosv, const float* sinv, int N, int d, uint16_t* out) {
+  for (int t = 0; t < N; t++)
+    rope_row(x + (int64_t)t * d, cosv + (int64_t)t * (d / 2), sinv + (int64_t)t * (d / 2), d, out + (int64_t)t * d);
+}
+
+static void fwht(float* x, int d) {
+  for (int h = 1; h < d; h <<= 1)
+    for (int i = 0; i < d; i++)
+      if (!(i & h)) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+}
+
+void or_fwht_rows(float* x, int rows, int d) {
+  for (int r = 0; r < rows; r++) fwht(x + (int64_t)r * d, d);
+}
+
+int or_quantize_ex(const uint16_t* Qin, const uint16_t* Kin, const uint16_t* V, const int32_t* perm,
+                   const float* rope_cos, const float* rope_sin,
+                   int N, int d, int flags, float cL,
+                   uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                   uint16_t* mu, float* mu_scaled, float* kbar_out) {
   if (N % 128) return 2;
   int nb = N / 128;
+  int log2d = 0;
+  while ((1 << log2d) < d) log2d++;
+  const int had = (flags & 16) != 0;
+  /* RoPE'd Q and K (bf16), or the inputs themselves */
+  const uint16_t* Q = Qin;
+  const uint16_t* K = Kin;
+  uint16_t *Qr = NULL, *Kr = NULL;
+  if (rope_cos && rope_sin) {
+    Qr = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * d);
+    Kr = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * d);
+    or_rope(Qin, rope_cos, rope_sin, N, d, Qr);
+    or_rope(Kin, rope_cos, rope_sin, N, d, Kr);
+    Q = Qr;
+    K = Kr;
+  }
   float* kbar = (float*)malloc(sizeof(float) * d);
   for (int j = 0; j < d; j++) {
     if (flags & 1) {
@@ -429,9 +488,11 @@ int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const i
   for (int b = 0; b < nb; b++) {
     float* x = (float*)malloc(sizeof(float) * 128 * d);
     for (int i = 0; i < 128 * d; i++) x[i] = bf16_val(Q[(int64_t)b * 128 * d + i]);
+    if (had) or_fwht_rows(x, 128, d);
     float s;
     quant_block(x, 128, d, Qq + (int64_t)b * 128 * d, &s);
     sQ[b] = s * cL;
+    if (had) sQ[b] = ldexpf(sQ[b], -log2d); /* exact: a power of two */
     free(x);
   }
   /* K' blocks */
@@ -442,9 +503,12 @@ int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const i
       int64_t src = perm ? perm[b * 128 + i] : (int64_t)(b * 128 + i);
       for (int j = 0; j < d; j++) x[i * d + j] = bf16_val(K[src * d + j]) - kbar[j];
     }
+    if (had) or_fwht_rows(x, 128, d);
     quant_block(x, 128, d, Kq + (int64_t)b * 128 * d, &sK[b]);
     free(x);
   }
+  free(Qr);
+  free(Kr);
   /* V': block means and residual */
   float* R = (float*)malloc(sizeof(float) * (size_t)N * d);
 #pragma omp parallel for schedule(static)
@@ -482,6 +546,13 @@ int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const i
   free(R);
   free(kbar);
   return 0;
+}
+
+int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                int N, int d, int flags, float cL,
+                uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                uint16_t* mu, float* mu_scaled, float* kbar_out) {
+  return or_quantize_ex(Q, K, V, perm, NULL, NULL, N, d, flags, cL, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, kbar_out);
 }
 
 /* ------------------------------------------------------------------------ */
