@@ -299,6 +299,9 @@ def main():
                          "exp-then-cast probabilities without mean restoration (instruction-count comparison of "
                          "the probability stage)")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
+    ap.add_argument("--quant-prep", default="none", choices=["none", "rope", "hadamard", "rope_hadamard"],
+                    help="preprocessing fused into the quantiser: RoPE on the video grid and/or the Q/K Hadamard "
+                         "rotation")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -351,6 +354,13 @@ def main():
     ws_q = vc.workspace(vc.vc_quantize_workspace_bytes(B, H, N, d))
     O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
     flags_q = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
+    rope_c = rope_s = None
+    if "rope" in args.quant_prep:
+        import synth
+        grid = synth.WAN_GRID if N == 70400 else None
+        rope_c, rope_s = (torch.from_numpy(t).cuda() for t in synth.rope_tables(N, d, grid))
+    if "hadamard" in args.quant_prep:
+        flags_q |= vc.VC_F_HADAMARD
     torch.cuda.synchronize()
 
     ev = {k: [] for k in ("cluster", "quantize", "attention")}
@@ -375,7 +385,7 @@ def main():
         if record: es[0].record()
         vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
         if record: es[1].record()
-        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q)
+        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q, rope_cos=rope_c, rope_sin=rope_s)
         if record: es[2].record()
         vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
         if record:
@@ -385,7 +395,7 @@ def main():
     if args.attention_only:
         C.copy_(Cw)
         vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
-        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q)
+        vc.vc_quantize(Qd, Kd, Vd, perm, flags_q, q, ws=ws_q, rope_cos=rope_c, rope_sin=rope_s)
     for i in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -423,6 +433,11 @@ def main():
                      "traffic_unit": "GB per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": "attn_fwd<128,ExpCast,restore>", "algorithmic_flops_per_launch": flops},
     }
+    if args.quant_prep != "none":
+        res["config"]["workload"] += " (quantiser with %s%s)" % (
+            {"rope": "RoPE", "hadamard": "the Q/K Hadamard rotation",
+             "rope_hadamard": "RoPE and the Q/K Hadamard rotation"}[args.quant_prep],
+            " on the 22x40x80 video grid" if "rope" in args.quant_prep and N == 70400 else "")
     if args.attention_only:
         res["config"]["workload"] += " (attention kernel only%s)" % {
             "vc": "", "vc_e5m2": ", E5M2 ExpCast bytes (beta -0.17)", "expcast": ", ExpCast without mean restoration",

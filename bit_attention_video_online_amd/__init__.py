@@ -24,6 +24,7 @@ VC_F_KSMOOTH = 1
 VC_F_VSMOOTH = 2
 VC_F_EXPCAST = 4
 VC_F_E5M2 = 8
+VC_F_HADAMARD = 16
 BLOCK = 128
 
 _STATUS = {0: "VC_OK", 1: "VC_E_NULLPTR", 2: "VC_E_SHAPE", 3: "VC_E_PARAM", 4: "VC_E_WORKSPACE",
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.vc_quantize_workspace_bytes.argtypes = [I, I, I, I, I]
         L.vc_quantize.restype = I
         L.vc_quantize.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, S, P]
+        L.vc_quantize_rope.restype = I
+        L.vc_quantize_rope.argtypes = [P, P, P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, S, P]
         L.vc_mu_pack_size.restype = S
         L.vc_mu_pack_size.argtypes = [I, I, I, I]
         L.vc_attention.restype = I
@@ -156,8 +159,9 @@ def quantize_outputs(B, H, N, d, device="cuda"):
     )
 
 
-def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK):
-    """Fused quantiser; `out` is a dict as returned by quantize_outputs()."""
+def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK, rope_cos=None, rope_sin=None):
+    """Fused quantiser; `out` is a dict as returned by quantize_outputs(). With rope_cos /
+    rope_sin (float32 [N, d/2]) Q and K are rotated first (vc_quantize_rope)."""
     B, H, N, d = _dims(Q)
     for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, (B, H, N, d), n)
@@ -166,11 +170,16 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK):
     need = vc_quantize_workspace_bytes(B, H, N, d, block)
     if ws is None:
         ws = workspace(need, Q.device)
-    st = lib().vc_quantize(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, int(block), int(flags),
-                           _ptr(out["Qq"]), _ptr(out["sQ"]), _ptr(out["Kq"]), _ptr(out["sK"]), _ptr(out["Vq"]),
-                           _ptr(out["sV"]), _ptr(out.get("mu")), _ptr(out.get("mu_scaled")), _ptr(out.get("mu_pack")),
-                           _ptr(ws), ws.numel(),
-                           _stream(stream))
+    outs = (_ptr(out["Qq"]), _ptr(out["sQ"]), _ptr(out["Kq"]), _ptr(out["sK"]), _ptr(out["Vq"]), _ptr(out["sV"]),
+            _ptr(out.get("mu")), _ptr(out.get("mu_scaled")), _ptr(out.get("mu_pack")), _ptr(ws), ws.numel(),
+            _stream(stream))
+    if rope_cos is None and rope_sin is None:
+        st = lib().vc_quantize(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, int(block), int(flags), *outs)
+    else:
+        _need(rope_cos, torch.float32, (N, d // 2), "rope_cos")
+        _need(rope_sin, torch.float32, (N, d // 2), "rope_sin")
+        st = lib().vc_quantize_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(rope_cos), _ptr(rope_sin), B, H, N,
+                                    d, int(block), int(flags), *outs)
     _check(st)
     return out
 

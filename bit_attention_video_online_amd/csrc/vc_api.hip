@@ -8,10 +8,10 @@
 
 #include "../../include/vc.h"
 
-extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
-                                  int d, uint32_t flags, float cL, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* ws,
-                                  hipStream_t st);
+extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, const float* rc,
+                                  const float* rs, int B, int H, int N, int d, uint32_t flags, float cL, uint8_t* Qq,
+                                  float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV, void* mu, float* mu_scaled,
+                                  void* mu_pack, void* ws, hipStream_t st);
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
@@ -107,20 +107,24 @@ extern "C" size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int bl
   return vc_quantize_ws_bytes(B, H, N, d);
 }
 
-extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
-                                 int d, int block, uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                 uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* workspace,
+static vc_status quantize_common(const void* Q, const void* K, const void* V, const int32_t* perm,
+                                 const float* rope_cos, const float* rope_sin, int B, int H, int N, int d, int block,
+                                 uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq,
+                                 float* sV, void* mu, float* mu_scaled, void* mu_pack, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || !workspace) return VC_E_NULLPTR;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
-  if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST)) return VC_E_PARAM;
+  if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_HADAMARD)) return VC_E_PARAM;
   if (workspace_bytes < vc_quantize_ws_bytes(B, H, N, d)) return VC_E_WORKSPACE;
-  const void* ptrs[] = {Q, K, V, perm, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, mu_pack, workspace};
+  const void* ptrs[] = {Q, K, V, perm, rope_cos, rope_sin, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, mu_pack, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return VC_E_UNSUPPORTED;
   const size_t el = (size_t)B * H * N * d, nbk = (size_t)B * H * (N / 128);
+  const size_t tab = (size_t)N * (d / 2) * 4;
   const Range ins[] = {{(const char*)Q, el * 2}, {(const char*)K, el * 2}, {(const char*)V, el * 2},
-                       {(const char*)perm, (size_t)B * H * N * 4}};
+                       {(const char*)perm, (size_t)B * H * N * 4}, {(const char*)rope_cos, tab},
+                       {(const char*)rope_sin, tab}};
   const Range outs[] = {{(const char*)Qq, el}, {(const char*)sQ, nbk * 4}, {(const char*)Kq, el},
                         {(const char*)sK, nbk * 4}, {(const char*)Vq, el}, {(const char*)sV, (size_t)B * H * d * 4},
                         {(const char*)mu, nbk * d * 2}, {(const char*)mu_scaled, nbk * d * 4},
@@ -128,10 +132,28 @@ extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, co
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
-  if (vc_launch_quantize(Q, K, V, perm, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled,
-                         mu_pack, workspace, (hipStream_t)stream) != 0)
+  if (vc_launch_quantize(Q, K, V, perm, rope_cos, rope_sin, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK,
+                         Vq, sV, mu, mu_scaled, mu_pack, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
+}
+
+extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
+                                 int d, int block, uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
+                                 uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return quantize_common(Q, K, V, perm, nullptr, nullptr, B, H, N, d, block, flags, Qq, sQ, Kq, sK, Vq, sV, mu,
+                         mu_scaled, mu_pack, workspace, workspace_bytes, stream);
+}
+
+extern "C" vc_status vc_quantize_rope(const void* Q, const void* K, const void* V, const int32_t* perm,
+                                      const float* rope_cos, const float* rope_sin, int B, int H, int N, int d,
+                                      int block, uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
+                                      uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!rope_cos || !rope_sin) return VC_E_NULLPTR;
+  return quantize_common(Q, K, V, perm, rope_cos, rope_sin, B, H, N, d, block, flags, Qq, sQ, Kq, sK, Vq, sV, mu,
+                         mu_scaled, mu_pack, workspace, workspace_bytes, stream);
 }
 
 static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,

@@ -12,6 +12,11 @@
 //   quant_reduce : per (b,h): kbar = fl32(exact mean), sV = fl32(amax/448), 448/amax.
 //   quant_apply  : per (b,h,block): K~' codes + scale; residual codes (block-transposed
 //                  layout) and mu / sV.
+// Optional preprocessing that the pages' fused quantiser also absorbs: RoPE on Q and K
+// (interleaved channel pairs, caller's binary32 cos/sin tables [N, d/2], binary32
+// products, result rounded to bf16) and the Q/K Hadamard rotation (unnormalised
+// Sylvester matrix by the fast Walsh-Hadamard transform, ascending stages, binary32; its
+// factor 1/d is folded exactly into sQ').
 // Tiles stay in registers (no LDS staging): every load is a 16-byte vector of one token
 // row (rows of V' and K' gathered through pi) and per-channel reductions use lane
 // shuffles plus a small LDS step. Exact sums use binary64, which is exact for these
@@ -53,6 +58,66 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, const int32_t* p
     int src = perm_blk ? perm_blk[r] : r;
     src = ((unsigned)src < (unsigned)nrows) ? src : 0;
     unpack8(*reinterpret_cast<const uint4*>(base + (size_t)src * D + 8 * chunk), x[i]);
+  }
+}
+
+constexpr uint32_t kFlagHadamard = 16u;  // flag bit of the Q/K rotation
+
+// RoPE on the thread's RPT rows (channel pairs 4*chunk .. +3 of each row); `pos` gives the
+// token whose angles apply (its row in the tables). Each rotated value is rounded to bf16.
+template <int D>
+__device__ __forceinline__ void rope_tile(float (&x)[Lay<D>::RPT][8], const float* __restrict__ rc,
+                                          const float* __restrict__ rs, const int (&pos)[Lay<D>::RPT]) {
+  constexpr int RPT = Lay<D>::RPT;
+  const int chunk = threadIdx.x % Lay<D>::CH;
+  for (int i = 0; i < RPT; i++) {
+    const float4 c = *reinterpret_cast<const float4*>(rc + (size_t)pos[i] * (D / 2) + 4 * chunk);
+    const float4 sn = *reinterpret_cast<const float4*>(rs + (size_t)pos[i] * (D / 2) + 4 * chunk);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+    for (int k = 0; k < 4; k++) {
+      const float a = x[i][2 * k], b = x[i][2 * k + 1];
+      const float ac = a * cc[k], bsn = b * ss[k], asn = a * ss[k], bc = b * cc[k];
+      x[i][2 * k] = bf16_to_f32(f32_to_bf16(ac - bsn));
+      x[i][2 * k + 1] = bf16_to_f32(f32_to_bf16(asn + bc));
+    }
+  }
+}
+
+// Row positions of the thread's rows: contiguous block rows, or the permutation's sources
+// (clamped like load_tile)
+template <int D>
+__device__ __forceinline__ void tile_rows(const int32_t* perm_blk, int row0, int nrows, int (&pos)[Lay<D>::RPT]) {
+  constexpr int RPT = Lay<D>::RPT;
+  const int rg = threadIdx.x / Lay<D>::CH;
+  for (int i = 0; i < RPT; i++) {
+    const int r = RPT * rg + i;
+    int src = perm_blk ? perm_blk[r] : row0 + r;
+    pos[i] = ((unsigned)src < (unsigned)nrows) ? src : 0;
+  }
+}
+
+// Unnormalised fast Walsh-Hadamard transform of every row of the tile: stages h = 1, 2, 4
+// inside the thread's 8 channels, then h = 8, 16, ... across the lanes that hold the other
+// chunks of the row (chunk bit k = lane bit k); the pair (i, i+h) becomes (a+b, a-b).
+template <int D>
+__device__ __forceinline__ void fwht_tile(float (&x)[Lay<D>::RPT][8]) {
+  constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
+  const int chunk = threadIdx.x % CH;
+  for (int i = 0; i < RPT; i++)
+    for (int h = 1; h < 8; h <<= 1)
+      for (int e = 0; e < 8; e++)
+        if (!(e & h)) {
+          const float a = x[i][e], b = x[i][e + h];
+          x[i][e] = a + b;
+          x[i][e + h] = a - b;
+        }
+  for (int m = 1; m < CH; m <<= 1) {
+    const bool upper = (chunk & m) != 0;
+    for (int i = 0; i < RPT; i++)
+      for (int e = 0; e < 8; e++) {
+        const float p = __shfl_xor(x[i][e], m);
+        x[i][e] = upper ? p - x[i][e] : x[i][e] + p;
+      }
   }
 }
 
@@ -114,9 +179,12 @@ __device__ __forceinline__ void column_sums(const float (&x)[Lay<D>::RPT][8], do
   __syncthreads();
 }
 
-template <int D>
+// ROPE / HAD select the optional preprocessing at compile time, so the plain path keeps
+// its small register footprint.
+template <int D, bool ROPE, bool HAD>
 __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                          const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                         const float* __restrict__ rc, const float* __restrict__ rs,
                                                          int N, uint32_t flags, float cL,
                                                          uint8_t* __restrict__ Qq, float* __restrict__ sQ,
                                                          uint16_t* __restrict__ mu, double* __restrict__ ksum,
@@ -133,14 +201,20 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
   const int chunk = threadIdx.x % CH, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float x[RPT][8];
 
+  int pos[RPT];
+  if (ROPE) tile_rows<D>(nullptr, j * kBlock, N, pos);
+
   // ---- Q block (original order): codes and scale
   load_tile<D>(Q + head + jrow, nullptr, kBlock, x);
+  if (ROPE) rope_tile<D>(x, rc, rs, pos);
+  if (HAD) fwht_tile<D>(x);
   const float s = quant_rows<D>(x, Qq + head + jrow, red);
-  if (threadIdx.x == 0) sQ[(size_t)bh * nb + j] = s * cL;
+  if (threadIdx.x == 0) sQ[(size_t)bh * nb + j] = HAD ? ldexpf(s * cL, -__builtin_ctz(D)) : s * cL;
 
   // ---- key channel partial sums (token order is irrelevant for a sum)
   if (flags & 1u) {
     load_tile<D>(K + head + jrow, nullptr, kBlock, x);
+    if (ROPE) rope_tile<D>(x, rc, rs, pos);
     column_sums<D>(x, part, colsum);
     if (threadIdx.x < D) ksum[((size_t)bh * nb + j) * D + threadIdx.x] = colsum[threadIdx.x];
   }
@@ -210,9 +284,10 @@ __global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags,
   }
 }
 
-template <int D>
+template <int D, bool ROPE, bool HAD>
 __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                                         const int32_t* __restrict__ perm, int N, uint32_t flags,
+                                                         const int32_t* __restrict__ perm, const float* __restrict__ rc,
+                                                         const float* __restrict__ rs, int N, uint32_t flags,
                                                          const float* __restrict__ kbar, const float* __restrict__ sV,
                                                          const float* __restrict__ vinv, const uint16_t* __restrict__ mu,
                                                          uint8_t* __restrict__ Kq, float* __restrict__ sK,
@@ -234,8 +309,14 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
     const float kb[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
     if (pblk) load_tile<D>(K + head, pblk, N, x);
     else load_tile<D>(K + head + jrow, nullptr, kBlock, x);
+    if (ROPE) {  // the angles of each key's original position
+      int pos[RPT];
+      tile_rows<D>(pblk, j * kBlock, N, pos);
+      rope_tile<D>(x, rc, rs, pos);
+    }
     for (int i = 0; i < RPT; i++)
       for (int e = 0; e < 8; e++) x[i][e] = x[i][e] - kb[e];
+    if (HAD) fwht_tile<D>(x);
     const float s = quant_rows<D>(x, Kq + head + jrow, red);
     if (threadIdx.x == 0) sK[(size_t)bh * nb + j] = s;
   }
@@ -291,14 +372,43 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
   }
 }
 
+struct QArgs {
+  const uint16_t *Q, *K, *V;
+  const int32_t* perm;
+  const float *rc, *rs;
+  int N;
+  uint32_t flags;
+  float cL;
+  uint8_t* Qq;
+  float* sQ;
+  uint8_t* Kq;
+  float* sK;
+  uint8_t* Vq;
+  float* sV;
+  uint16_t* mu;
+  float* mu_scaled;
+  uint16_t* mu_pack;
+  double* ksum;
+  float *vamax, *kbar, *vinv;
+};
+
+template <int D, bool ROPE, bool HAD>
+static void launch_quant(const QArgs& a, dim3 grid, int BH, hipStream_t st) {
+  quant_stats<D, ROPE, HAD><<<grid, kQThreads, 0, st>>>(a.Q, a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.cL, a.Qq,
+                                                         a.sQ, a.mu, a.ksum, a.vamax);
+  quant_reduce<D><<<BH, kQThreads, 0, st>>>(a.N, a.flags, a.ksum, a.vamax, a.kbar, a.sV, a.vinv);
+  quant_apply<D, ROPE, HAD><<<grid, kQThreads, 0, st>>>(a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.kbar, a.sV,
+                                                         a.vinv, a.mu, a.Kq, a.sK, a.Vq, a.mu_scaled, a.mu_pack);
+}
+
 }  // namespace vc
 
 using namespace vc;
 
-extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, int B, int H, int N,
-                                  int d, uint32_t flags, float cL, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK,
-                                  uint8_t* Vq, float* sV, void* mu, float* mu_scaled, void* mu_pack, void* ws,
-                                  hipStream_t st) {
+extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, const int32_t* perm, const float* rc,
+                                  const float* rs, int B, int H, int N, int d, uint32_t flags, float cL, uint8_t* Qq,
+                                  float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV, void* mu, float* mu_scaled,
+                                  void* mu_pack, void* ws, hipStream_t st) {
   const int nb = N / kBlock, BH = B * H;
   // workspace: ksum double [BH,nb,d] | vamax float [BH,nb,d] | kbar float [BH,d] | vinv float [BH,d] | mu (if caller's NULL)
   char* w = (char*)ws;
@@ -309,18 +419,15 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
   uint16_t* muw = (uint16_t*)w;
   uint16_t* mup = mu ? (uint16_t*)mu : muw;
   dim3 grid(nb, BH);
+  const QArgs a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, rc, rs, N, flags, cL, Qq, sQ,
+                Kq, sK, Vq, sV, mup, mu_scaled, (uint16_t*)mu_pack, ksum, vamax, kbar, vinv};
+  const bool rope = rc != nullptr, had = (flags & kFlagHadamard) != 0;
   if (d == 128) {
-    quant_stats<128><<<grid, kQThreads, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, N, flags, cL,
-                                                Qq, sQ, mup, ksum, vamax);
-    quant_reduce<128><<<BH, kQThreads, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
-    quant_apply<128><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
-                                                Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
+    if (rope) { if (had) launch_quant<128, true, true>(a, grid, BH, st); else launch_quant<128, true, false>(a, grid, BH, st); }
+    else { if (had) launch_quant<128, false, true>(a, grid, BH, st); else launch_quant<128, false, false>(a, grid, BH, st); }
   } else {
-    quant_stats<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, N, flags, cL,
-                                               Qq, sQ, mup, ksum, vamax);
-    quant_reduce<64><<<BH, kQThreads, 0, st>>>(N, flags, ksum, vamax, kbar, sV, vinv);
-    quant_apply<64><<<grid, kQThreads, 0, st>>>((const uint16_t*)K, (const uint16_t*)V, perm, N, flags, kbar, sV, vinv, mup,
-                                               Kq, sK, Vq, mu_scaled, (uint16_t*)mu_pack);
+    if (rope) { if (had) launch_quant<64, true, true>(a, grid, BH, st); else launch_quant<64, true, false>(a, grid, BH, st); }
+    else { if (had) launch_quant<64, false, true>(a, grid, BH, st); else launch_quant<64, false, false>(a, grid, BH, st); }
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -55,7 +55,8 @@ enum {
   VC_F_KSMOOTH = 1u, /* subtract the per-channel key mean over all N tokens */
   VC_F_VSMOOTH = 2u, /* block-mean removal of V' and mean restoration */
   VC_F_EXPCAST = 4u, /* ExpCast-FP8 probability bytes (else exp2 then cast) */
-  VC_F_E5M2 = 8u     /* with VC_F_EXPCAST: the bytes are E5M2 (4 codes per octave) */
+  VC_F_E5M2 = 8u,    /* with VC_F_EXPCAST: the bytes are E5M2 (4 codes per octave) */
+  VC_F_HADAMARD = 16u /* quantiser: rotate Q and K~' rows by the Hadamard matrix first */
 };
 
 /* Static description of a status code (host function, never NULL). */
@@ -101,7 +102,7 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
  *   Q, K, V    bf16 [B,H,N,d]
  *   perm       int32 [B,H,N], or NULL for the identity (plain FP8 path)
  *   block      must be 128
- *   flags      VC_F_KSMOOTH | VC_F_VSMOOTH (VC_F_EXPCAST ignored)
+ *   flags      VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_HADAMARD (VC_F_EXPCAST ignored)
  * Outputs (all written on success):
  *   Qq   uint8 [B,H,N,d]           E4M3 codes of Q, original token order
  *   sQ   float [B,H,N/128]         Q block scale times fl32(log2(e)/sqrt(d))
@@ -121,6 +122,11 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
  * Arithmetic: block and channel scales are fl32(amax/448) with codes
  * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
  * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).
+ * VC_F_HADAMARD (the rotation that the pages' fused preprocessing carries): every Q row
+ * and every K~' row is multiplied by the unnormalised Sylvester Hadamard matrix H_d
+ * before its block is quantised, evaluated as the fast Walsh-Hadamard transform in
+ * binary32 (stages h = 1, 2, ..., d/2 in that order; pair (i, i+h) -> (a+b, a-b)); the
+ * factor 1/d of (Q H)(K H)^T = d Q K^T is folded exactly into sQ (times 2^-log2(d)).
  * workspace >= vc_quantize_workspace_bytes(B,H,N,d,block).
  * ------------------------------------------------------------------------ */
 size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int block);
@@ -130,6 +136,27 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
                       uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
                       void* mu, float* mu_scaled, void* mu_pack, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * vc_quantize_rope -- vc_quantize with rotary position embedding applied to Q and K
+ * first (the pages' fused preprocessing absorbs RoPE into the quantiser).
+ *
+ *   rope_cos, rope_sin  float [N, d/2], shared by all (b,h): the angle of channel pair i
+ *                       of token t (original order) -- any 1-D or multi-axis RoPE
+ *                       expressed as per-token angles. Both required (VC_E_NULLPTR).
+ * Each token's interleaved pairs (x_2i, x_2i+1) become
+ *   (fl32(fl32(x_2i c) - fl32(x_2i+1 s)), fl32(fl32(x_2i s) + fl32(x_2i+1 c))),
+ * rounded to bf16 (the tensor an unfused chain would hand to the quantiser), and the
+ * rest is vc_quantize on the rotated Q and K (key mean over the rotated keys; a key's
+ * angles are those of its original position, whatever the permutation). V is not
+ * rotated. Other arguments, outputs and errors as vc_quantize.
+ * ------------------------------------------------------------------------ */
+vc_status vc_quantize_rope(const void* Q, const void* K, const void* V, const int32_t* perm,
+                           const float* rope_cos, const float* rope_sin,
+                           int B, int H, int N, int d, int block, uint32_t flags,
+                           uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                           void* mu, float* mu_scaled, void* mu_pack, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * vc_attention -- non-causal attention over the quantised tensors (paper page,

@@ -86,6 +86,36 @@ def rand_perm(N: int, seed: int, b: int = 0, h: int = 0) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ workloads
+def rope_tables(N: int, d: int, grid=None, base: float = 10000.0):
+    """Rotary angle tables (cos, sin), float32 [N, d/2], for tokens in raster order.
+
+    Without `grid`: 1-D positions t with angle t * base^(-2i/d) for pair i. With
+    grid = (F, Hh, Ww), F*Hh*Ww = N, a video layout: the channels are split between the
+    frame, row and column axes in the proportions a video DiT uses (frame axis
+    d - 4*(d//6) channels, each spatial axis 2*(d//6)), and pair i of an axis with c
+    channels turns by pos * base^(-2i/c), pos being the token's coordinate on that axis."""
+    half = d // 2
+    if grid is None:
+        pos = np.arange(N, dtype=np.float64)[:, None]
+        ang = pos * base ** (-2.0 * np.arange(half)[None, :] / d)
+    else:
+        F, Hh, Ww = grid
+        assert F * Hh * Ww == N
+        cs = (d - 4 * (d // 6), 2 * (d // 6), 2 * (d // 6))
+        t = np.arange(N)
+        coords = (t // (Hh * Ww), (t // Ww) % Hh, t % Ww)
+        parts = []
+        for c, p in zip(cs, coords):
+            parts.append(p[:, None].astype(np.float64) * base ** (-2.0 * np.arange(c // 2)[None, :] / c))
+        ang = np.concatenate(parts, axis=1)
+        assert ang.shape[1] == half
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+# Video grid (frames, rows, columns) of the Wan-shaped workload's 70,400 tokens
+WAN_GRID = (22, 40, 80)
+
+
 WORKLOADS = {
     "tiny": dict(seed=0, B=1, H=1, N=1024, d=128, clusters=8, iters=4, cold=True),
     "expcast": dict(seed=1, B=1, H=8, N=8192, d=128),

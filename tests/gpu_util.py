@@ -18,11 +18,14 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def gpu_quantize(Q, K, V, perm, flags):
-    """Q, K, V: numpy bf16 bits [B,H,N,d]; perm numpy int32 [B,H,N] or None."""
+def gpu_quantize(Q, K, V, perm, flags, rope=None):
+    """Q, K, V: numpy bf16 bits [B,H,N,d]; perm numpy int32 [B,H,N] or None; rope = (cos, sin)
+    float32 [N, d/2] tables or None."""
     B, H, N, d = Q.shape
     out = vc.quantize_outputs(B, H, N, d)
-    vc.vc_quantize(to_dev_bf16(Q), to_dev_bf16(K), to_dev_bf16(V), None if perm is None else to_dev(perm), flags, out)
+    rc, rs = (None, None) if rope is None else (to_dev(rope[0]), to_dev(rope[1]))
+    vc.vc_quantize(to_dev_bf16(Q), to_dev_bf16(K), to_dev_bf16(V), None if perm is None else to_dev(perm), flags, out,
+                   rope_cos=rc, rope_sin=rs)
     torch.cuda.synchronize()
     return out
 

@@ -56,6 +56,28 @@ def _quant(L, **kw):
                          a["st"])
 
 
+def _quant_rope(L, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, perm=None, rc=ctypes.c_void_p(11 << 20), rs=ctypes.c_void_p(12 << 20), B=1, H=1,
+             N=256, d=128, block=128, flags=3 | 16,
+             Qq=ctypes.c_void_p(1 << 20), sQ=ctypes.c_void_p(2 << 20), Kq=ctypes.c_void_p(3 << 20),
+             sK=ctypes.c_void_p(4 << 20), Vq=ctypes.c_void_p(5 << 20), sV=ctypes.c_void_p(6 << 20),
+             mu=ctypes.c_void_p(7 << 20), mus=ctypes.c_void_p(8 << 20), mup=ctypes.c_void_p(10 << 20),
+             ws=ctypes.c_void_p(9 << 20), wsb=1 << 30, st=None)
+    a.update(kw)
+    return L.vc_quantize_rope(a["Q"], a["K"], a["V"], a["perm"], a["rc"], a["rs"], a["B"], a["H"], a["N"], a["d"],
+                              a["block"], a["flags"], a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"],
+                              a["mus"], a["mup"], a["ws"], a["wsb"], a["st"])
+
+
+def test_quantize_rope_rejects_bad_arguments(L):
+    assert _quant_rope(L, rc=None) == 1
+    assert _quant_rope(L, rs=None) == 1
+    assert _quant_rope(L, N=200) == 2
+    assert _quant_rope(L, flags=64) == 3
+    assert _quant_rope(L, rs=ctypes.c_void_p((12 << 20) + 4)) == 5          # misaligned table
+    assert _quant_rope(L, rc=ctypes.c_void_p((1 << 20) + 256)) == 7         # table inside an output
+
+
 def test_quantize_rejects_bad_arguments(L):
     assert _quant(L, Q=None) == 1
     assert _quant(L, N=200) == 2          # not a multiple of 128

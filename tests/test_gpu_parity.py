@@ -101,6 +101,43 @@ def test_quantize_bitexact_shapes(d, N):
             _compare_quant(out, q_or, b, h, True)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rope,had", [(True, False), (False, True), (True, True)])
+def test_quantize_rope_hadamard_bitexact(d, rope, had):
+    """RoPE (video-grid angle tables) and the Q/K Hadamard rotation inside the quantiser,
+    ragged 3-block heads, permuted keys: every output bit-exact against the oracle."""
+    B, H, N = 1, 2, 384
+    w = synth.gen("wan", seed=8, B=B, H=H, N=N, d=d)
+    perm = np.stack([np.stack([synth.rand_perm(N, 11, b, h) for h in range(H)]) for b in range(B)])
+    tabs = synth.rope_tables(N, d, (3, 8, 16)) if rope else None
+    flags = FLAGS_ALL | (vc.VC_F_HADAMARD if had else 0)
+    out = gpu_quantize(w["Q"], w["K"], w["V"], perm, flags, rope=tabs)
+    for h in range(H):
+        q_or = oracle.quantize(w["Q"][0, h], w["K"][0, h], w["V"][0, h], perm[0, h],
+                               oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH | (oracle.FLAG_HADAMARD if had else 0),
+                               rope_cos=None if tabs is None else tabs[0], rope_sin=None if tabs is None else tabs[1])
+        _compare_quant(out, q_or, 0, h, True)
+
+
+@pytest.mark.parametrize("e5m2", [False, True])
+def test_attention_after_rope_hadamard_matches_emulation(e5m2):
+    w = synth.gen("tiny")
+    N, d = 1024, 128
+    perm = synth.rand_perm(N, 2)
+    tabs = synth.rope_tables(N, d, (4, 16, 16))
+    out = gpu_quantize(w["Q"], w["K"], w["V"], perm[None, None], FLAGS_ALL | vc.VC_F_HADAMARD, rope=tabs)
+    O, _ = _gpu_attention(out, N, d, 1, 1, True, True, e5m2=e5m2)
+    q_or = oracle.quantize(w["Q"][0, 0], w["K"][0, 0], w["V"][0, 0], perm,
+                           oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH | oracle.FLAG_HADAMARD,
+                           rope_cos=tabs[0], rope_sin=tabs[1])
+    rows = np.arange(N, dtype=np.int32)
+    O_or = oracle.attention_emul(q_or, rows, beta=BETA2 if e5m2 else BETA,
+                                 mode=oracle.MODE_EXPCAST_E5M2 if e5m2 else oracle.MODE_EXPCAST)
+    err = rel_l2(_o_f64(O[0, 0]), O_or)
+    print("[rope+hadamard %s] rel-L2 vs emulation %.3e" % ("e5m2" if e5m2 else "e4m3", err))
+    assert err <= (TOL_E5M2 if e5m2 else TOL), err
+
+
 def test_quantize_exact_construction():
     from tests._construct import representable_head
     hd = representable_head(N=512, d=128, seed=3)

@@ -142,3 +142,49 @@ def test_wan_attention_sampled_rows(run, oracle_heads):
     assert max(errs5) <= 2e-3 * (2 ** 0.25 - 1) / (2 ** 0.125 - 1)
     assert m["vsmooth"] < m["plain"]
     assert m["vc"] < m["expcast"]
+
+
+def test_wan_rope_hadamard_sampled_heads(run, oracle_heads):
+    """RoPE on the video grid (22 x 40 x 80) and the Q/K Hadamard rotation inside the
+    quantiser at full size: quantiser outputs of two heads bit-exact, attention on sampled
+    rows within 2e-3 of the emulation; error against exact attention on the RoPE'd inputs
+    printed for the path with and without the rotation."""
+    w = run["w"]
+    B, H, N, d = w["Q"].shape
+    tabs = synth.rope_tables(N, d, synth.WAN_GRID)
+    rc, rs = (torch.from_numpy(t).cuda() for t in tabs)
+    Q, K, V = (to_dev_bf16(w[k]) for k in ("Q", "K", "V"))
+    perm = torch.from_numpy(run["perm"]).cuda()
+    res = {}
+    for had in (False, True):
+        flags = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH | (vc.VC_F_HADAMARD if had else 0)
+        q = vc.quantize_outputs(B, H, N, d)
+        vc.vc_quantize(Q, K, V, perm, flags, q, rope_cos=rc, rope_sin=rs)
+        O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+        torch.cuda.synchronize()
+        res[had] = ({k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in q.items()},
+                    bf16_bits(O))
+        del q, O
+    del Q, K, V
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(78)
+    err_ex = {False: [], True: []}
+    for h in HEADS:
+        rows = np.sort(rng.choice(N, 64, replace=False)).astype(np.int32)
+        O_ex = oracle.attention_exact(oracle.rope(w["Q"][0, h], *tabs), oracle.rope(w["K"][0, h], *tabs),
+                                      w["V"][0, h], rows)
+        for had in (False, True):
+            g, O = res[had]
+            o = oracle.quantize(w["Q"][0, h], w["K"][0, h], w["V"][0, h], oracle_heads[h]["perm"],
+                                oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH | (oracle.FLAG_HADAMARD if had else 0),
+                                rope_cos=tabs[0], rope_sin=tabs[1])
+            for k in ("Qq", "sQ", "Kq", "sK", "sV", "mu_scaled"):
+                assert np.array_equal(g[k][0, h], o[k]), (had, h, k)
+            assert np.array_equal(vq_rowmajor(g["Vq"])[0, h], o["Vq"])
+            got = synth.bf16_to_f32(O[0, h][rows]).astype(np.float64)
+            O_em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+            assert rel_l2(got, O_em) <= 2e-3, (had, h)
+            err_ex[had].append(rel_l2(got, O_ex))
+    print("[wan rope] rMSE vs exact on the RoPE'd inputs: without rotation %.4f, with Hadamard %.4f"
+          % (np.mean(err_ex[False]), np.mean(err_ex[True])), flush=True)
