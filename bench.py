@@ -245,6 +245,9 @@ def run_schedule(args):
     Qr = Qd[0, 0][rows_t].double()
     Kh = Kd[0, 0].double()
     gen = torch.Generator(device="cuda")
+    cost = torch.empty((B, H), dtype=torch.float64, device="cuda")
+    ws_cost = vc.workspace(int(vc.lib().vc_cluster_cost_workspace_bytes(B, H, N, d)))
+    cost_ref = None
     steps = []
     for s in range(S):
         if s > 0:
@@ -255,10 +258,29 @@ def run_schedule(args):
             del xi, Vf
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
-        if s == 0:
-            vc.vc_cluster(V, Kc, 4, True, C, lab, perm, ws=ws_c)
-        elif s <= 4:
-            vc.vc_cluster(V, Kc, 2, False, C, lab, perm, ws=ws_c)
+        clustered, drift = False, None
+        if args.refresh == "fixed":
+            if s == 0:
+                vc.vc_cluster(V, Kc, 4, True, C, lab, perm, ws=ws_c)
+            elif s <= 4:
+                vc.vc_cluster(V, Kc, 2, False, C, lab, perm, ws=ws_c)
+            clustered = s <= 4
+        else:
+            # drift-triggered refresh: the k-means objective of the current values under the
+            # kept clustering, relative to its value right after the last clustering; the host
+            # reads it back, so the decision's latency counts as clustering time
+            if s == 0:
+                vc.vc_cluster(V, Kc, 4, True, C, lab, perm, ws=ws_c)
+                clustered = True
+            else:
+                vc.vc_cluster_cost(V, C, lab, cost, ws=ws_cost)
+                drift = float((cost.cpu().numpy() / cost_ref).mean()) - 1.0
+                if drift > args.drift_threshold:
+                    vc.vc_cluster(V, Kc, 2, False, C, lab, perm, ws=ws_c)
+                    clustered = True
+            if clustered:
+                vc.vc_cluster_cost(V, C, lab, cost, ws=ws_cost)
+                cost_ref = cost.cpu().numpy()
         ev[1].record()
         vc.vc_quantize(Qd, Kd, V, perm, flags_q, q, ws=ws_q)
         ev[2].record()
@@ -269,13 +291,20 @@ def run_schedule(args):
         O_ex = exact_attention_rows(Qr, Kh, V[0, 0].double())
         rmse = float(torch.linalg.norm(O[0, 0][rows_t].double() - O_ex) / torch.linalg.norm(O_ex))
         steps.append(dict(step=s, cluster_ms=round(tc, 3), quantize_ms=round(tq, 3), attention_ms=round(ta, 3),
-                          rmse=round(rmse, 6)))
-        log("[schedule] step %2d: cluster %.3f ms, quantize %.3f ms, attention %.3f ms, rMSE %.4f%%"
-            % (s, tc, tq, ta, 100 * rmse))
+                          rmse=round(rmse, 6), clustered=clustered,
+                          drift=None if drift is None else round(drift, 5)))
+        log("[schedule] step %2d: cluster %.3f ms%s, quantize %.3f ms, attention %.3f ms, rMSE %.4f%%%s"
+            % (s, tc, " (clustered)" if clustered else "", tq, ta, 100 * rmse,
+               "" if drift is None else ", drift %.4f" % drift))
     t_c = sum(x["cluster_ms"] for x in steps)
     t_qa = sum(x["quantize_ms"] + x["attention_ms"] for x in steps)
-    res = {"workload": "20-step amortised schedule, B=%d H=%d N=%d d=%d, %d clusters; cluster at steps 0-4 "
-                       "(cold x4, then warm x2), permutation of step 4 reused for steps 5-19" % (B, H, N, d, Kc),
+    sched = ("cluster at steps 0-4 (cold x4, then warm x2), permutation of step 4 reused for steps 5-19"
+             if args.refresh == "fixed" else
+             "cluster cold x4 at step 0; afterwards re-cluster (warm x2) whenever the mean over heads of the "
+             "k-means objective under the kept clustering exceeds its post-clustering value by more than %g"
+             % args.drift_threshold)
+    res = {"workload": "20-step amortised schedule, B=%d H=%d N=%d d=%d, %d clusters; %s" % (B, H, N, d, Kc, sched),
+           "clusterings": sum(1 for x in steps if x["clustered"]),
            "clustering_share": round(t_c / t_qa, 5), "cluster_ms_total": round(t_c, 3),
            "quantize_attention_ms_total": round(t_qa, 3),
            "rmse_rows": "head 0, %d rows evenly spaced, vs binary64 softmax(Q K^T / sqrt(d)) V from the bf16 "
@@ -299,6 +328,10 @@ def main():
                          "exp-then-cast probabilities without mean restoration (instruction-count comparison of "
                          "the probability stage)")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
+    ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift"],
+                    help="schedule workload: fixed clustering steps 0-4, or drift-triggered refresh")
+    ap.add_argument("--drift-threshold", type=float, default=0.05,
+                    help="relative growth of the k-means objective that triggers a refresh")
     ap.add_argument("--quant-prep", default="none", choices=["none", "rope", "hadamard", "rope_hadamard"],
                     help="preprocessing fused into the quantiser: RoPE on the video grid and/or the Q/K Hadamard "
                          "rotation")

@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
         L.vc_cluster.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, S, P]
         L.vc_quantize_workspace_bytes.restype = S
         L.vc_quantize_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.vc_cluster_cost_workspace_bytes.restype = S
+        L.vc_cluster_cost_workspace_bytes.argtypes = [I, I, I, I]
+        L.vc_cluster_cost.restype = I
+        L.vc_cluster_cost.argtypes = [P, P, P, I, I, I, I, I, P, P, S, P]
         L.vc_quantize.restype = I
         L.vc_quantize.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P, S, P]
         L.vc_quantize_rope.restype = I
@@ -182,6 +186,21 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK, ro
                                     d, int(block), int(flags), *outs)
     _check(st)
     return out
+
+
+def vc_cluster_cost(V, C, labels, cost, ws=None, stream=None):
+    """k-means objective per (b,h) into cost (float64 [B,H]): (1/N) sum ||V_t - bf16(C_z)||^2."""
+    B, H, N, d = _dims(V)
+    K = C.shape[2]
+    _need(V, torch.bfloat16, (B, H, N, d), "V")
+    _need(C, torch.float32, (B, H, K, d), "centroids")
+    _need(labels, torch.int32, (B, H, N), "labels")
+    _need(cost, torch.float64, (B, H), "cost")
+    if ws is None:
+        ws = workspace(int(lib().vc_cluster_cost_workspace_bytes(B, H, N, d)), V.device)
+    _check(lib().vc_cluster_cost(_ptr(V), _ptr(C), _ptr(labels), B, H, N, d, K, _ptr(cost), _ptr(ws), ws.numel(),
+                                 _stream(stream)))
+    return cost
 
 
 def vc_attention(q, O, beta=-0.35, flags=VC_F_EXPCAST, restore_mean=True, stream=None, block=BLOCK):

@@ -13,6 +13,9 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
                                   float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV, void* mu, float* mu_scaled,
                                   void* mu_pack, void* ws, hipStream_t st);
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
+extern "C" size_t vc_cluster_cost_ws_bytes(int B, int H, int N);
+extern "C" int vc_launch_cluster_cost(const void* V, const float* C, const int32_t* labels, int B, int H, int N, int d,
+                                      int K, double* cost, void* ws, hipStream_t st);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
                                    float beta, int pmode, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
@@ -93,6 +96,33 @@ extern "C" vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K
     return VC_E_ALIAS;
   if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
                         (hipStream_t)stream) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" size_t vc_cluster_cost_workspace_bytes(int B, int H, int N, int d) {
+  if (!shape_ok(B, H, N, d)) return 0;
+  return vc_cluster_cost_ws_bytes(B, H, N);
+}
+
+extern "C" vc_status vc_cluster_cost(const void* V, const float* centroids, const int32_t* labels, int B, int H, int N,
+                                     int d, int K, double* cost, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (!V || !centroids || !labels || !cost || !workspace) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d)) return VC_E_SHAPE;
+  if (K < 1 || K > N) return VC_E_PARAM;
+  if (workspace_bytes < vc_cluster_cost_ws_bytes(B, H, N)) return VC_E_WORKSPACE;
+  if (!aligned16(V) || !aligned16(centroids) || !aligned16(labels) || !aligned16(workspace)) return VC_E_UNSUPPORTED;
+  if (((uintptr_t)cost) & 7u) return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N;
+  const Range outs[] = {{(const char*)cost, (size_t)B * H * 8}, {(const char*)workspace, workspace_bytes}};
+  const Range ins[] = {{(const char*)V, el * d * 2}, {(const char*)centroids, (size_t)B * H * K * d * 4},
+                       {(const char*)labels, el * 4}};
+  for (const Range& o : outs)
+    for (const Range& i : ins)
+      if (overlaps(o, i)) return VC_E_ALIAS;
+  if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
+  if (vc_launch_cluster_cost(V, centroids, labels, B, H, N, d, K, cost, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
 }

@@ -351,9 +351,71 @@ __global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V,
   }
 }
 
+// k-means objective of the values under fixed labels and centroids (a drift statistic:
+// the paper page's weakness list suggests detecting layout drift to refresh the
+// clustering early). Partial sums of ||V_t - bf16(C_{z_t})||^2 over kCostTokens tokens per
+// work-group: the difference of two bf16 values is exact in binary64, its square and the
+// sums are binary64 roundings (relative error ~1e-13 over a head).
+constexpr int kCostTokens = 1024;
+
+template <int D>
+__global__ __launch_bounds__(256) void cl_cost_part(const uint16_t* __restrict__ V, const float* __restrict__ C,
+                                                    const int32_t* __restrict__ labels, int N, int K, int nblk,
+                                                    double* __restrict__ part) {
+  constexpr int CH = D / 8, G = 256 / CH;
+  __shared__ double red[256];
+  const int blk = blockIdx.x, bh = blockIdx.y;
+  const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
+  const int t0 = blk * kCostTokens, t1 = min(N, t0 + kCostTokens);
+  double acc = 0.0;
+  for (int t = t0 + g; t < t1; t += G) {
+    int z = labels[(size_t)bh * N + t];
+    z = ((unsigned)z < (unsigned)K) ? z : 0;
+    const uint4 raw = *reinterpret_cast<const uint4*>(V + ((size_t)bh * N + t) * D + 8 * chunk);
+    const float4 c0 = *reinterpret_cast<const float4*>(C + ((size_t)bh * K + z) * D + 8 * chunk);
+    const float4 c1 = *reinterpret_cast<const float4*>(C + ((size_t)bh * K + z) * D + 8 * chunk + 4);
+    const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int e = 0; e < 8; e++) {
+      const float v = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+      const double df = (double)v - (double)bf16_to_f32(f32_to_bf16(cf[e]));
+      acc += df * df;
+    }
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(size_t)bh * nblk + blk] = red[0];
+}
+
+__global__ void cl_cost_final(const double* __restrict__ part, int nblk, int N, int BH, double* __restrict__ cost) {
+  const int bh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  double s = 0.0;
+  for (int b = 0; b < nblk; b++) s += part[(size_t)bh * nblk + b];
+  cost[bh] = s / (double)N;
+}
+
 }  // namespace vc
 
 using namespace vc;
+
+extern "C" size_t vc_cluster_cost_ws_bytes(int B, int H, int N) {
+  return (size_t)B * H * ((N + kCostTokens - 1) / kCostTokens) * sizeof(double) + 256;
+}
+
+extern "C" int vc_launch_cluster_cost(const void* V, const float* C, const int32_t* labels, int B, int H, int N, int d,
+                                      int K, double* cost, void* ws, hipStream_t st) {
+  const int BH = B * H, nblk = (N + kCostTokens - 1) / kCostTokens;
+  double* part = (double*)ws;
+  if (d == 128) cl_cost_part<128><<<dim3(nblk, BH), 256, 0, st>>>((const uint16_t*)V, C, labels, N, K, nblk, part);
+  else cl_cost_part<64><<<dim3(nblk, BH), 256, 0, st>>>((const uint16_t*)V, C, labels, N, K, nblk, part);
+  cl_cost_final<<<(BH + 63) / 64, 64, 0, st>>>(part, nblk, N, BH, cost);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K) {
   const size_t BH = (size_t)B * H, nch = ((size_t)N + kChunk - 1) / kChunk;

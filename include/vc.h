@@ -97,6 +97,23 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * vc_cluster_cost -- the k-means objective of the current values under a kept
+ * clustering, a drift statistic for refreshing the permutation early (the paper
+ * page's weakness list: the reused permutation loses accuracy when the layout
+ * drifts; detect the drift and re-cluster).
+ *
+ *   V          bf16 [B,H,N,d]    current values
+ *   centroids  float [B,H,K,d]   as vc_cluster left them; labels int32 [B,H,N] in [0,K)
+ *   cost       double [B,H] out  (1/N) sum_t ||V_t - bf16(C_{z_t})||^2 (the assignment
+ *                                distance), binary64 sums (relative error ~1e-13); a label
+ *                                outside [0,K) is read as 0
+ *   workspace  >= vc_cluster_cost_workspace_bytes(B,H,N,d); cost must be 8-byte aligned
+ * ------------------------------------------------------------------------ */
+size_t vc_cluster_cost_workspace_bytes(int B, int H, int N, int d);
+vc_status vc_cluster_cost(const void* V, const float* centroids, const int32_t* labels, int B, int H, int N, int d,
+                          int K, double* cost, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * vc_quantize -- fused quantiser (paper page, method step (2); study notes 2-2).
  *
  *   Q, K, V    bf16 [B,H,N,d]

@@ -95,6 +95,8 @@ def lib() -> ctypes.CDLL:
         _lib.or_stable_argsort.argtypes = [P, I, I, P]
         _lib.or_kmeans_update.argtypes = [P, I, I, P, I, P]
         _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
+        _lib.or_kmeans_cost.restype = ctypes.c_double
+        _lib.or_kmeans_cost.argtypes = [P, I, I, P, I, P]
         _lib.or_quantize.restype = I
         _lib.or_quantize.argtypes = [P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
         _lib.or_quantize_ex.argtypes = [P, P, P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
@@ -219,6 +221,14 @@ def fwht_rows(x) -> np.ndarray:
     rows, d = a.shape
     lib().or_fwht_rows(_p(a), rows, d)
     return a
+
+
+def kmeans_cost(V_bits, C, labels) -> float:
+    """(1/N) sum_t ||V_t - bf16(C_{z_t})||^2, exact sum, one rounding to binary64."""
+    V = _c(V_bits, np.uint16)
+    N, d = V.shape
+    Cc = _c(C, np.float32)
+    return float(lib().or_kmeans_cost(_p(V), N, d, _p(Cc), Cc.shape[0], _p(_c(labels, np.int32))))
 
 
 def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOTH, rope_cos=None,

@@ -384,6 +384,26 @@ void or_kmeans(const uint16_t* V, int N, int d, int K, int iters, int cold,
   free(chat);
 }
 
+/* k-means objective of values under given labels and centroids (the paper  */
+/* page's weakness list: detect layout drift to trigger an early             */
+/* re-clustering). J = (1/N) sum_t ||V_t - bf16(C_{z_t})||^2 with the        */
+/* distance of the assignment step, exact sum, one rounding to binary64.     */
+double or_kmeans_cost(const uint16_t* V, int N, int d, const float* C, int K, const int32_t* labels) {
+  xacc s;
+  xa_zero(&s);
+  for (int t = 0; t < N; t++) {
+    int z = labels[t];
+    if (z < 0 || z >= K) return NAN;
+    for (int j = 0; j < d; j++) {
+      double v = bf16_val(V[(int64_t)t * d + j]), c = bf16_val(f32_to_bf16(C[(int64_t)z * d + j]));
+      xa_add_prod(&s, v, v);
+      xa_add_prod(&s, v, -2.0 * c); /* -2c is exact */
+      xa_add_prod(&s, c, c);
+    }
+  }
+  return xa_round_div(&s, (uint32_t)N, 53);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Quantizer (paper page, method step (2); study notes 2-2).                 */
 /* Per (batch, head), N a multiple of 128, blocks of 128 rows:              */

@@ -199,6 +199,23 @@ def test_cluster_ties_duplicate_centroids():
     assert np.array_equal(C[0, 0], c_or)
 
 
+@pytest.mark.parametrize("d,N,K", [(128, 1024, 8), (64, 2560, 37), (128, 3072, 300)])
+def test_cluster_cost_matches_oracle(d, N, K):
+    """k-means objective under given (arbitrary) labels and centroids, several heads,
+    a ragged last work-group: binary64 sums within 1e-11 of the exact value."""
+    B, H = 1, 3
+    rng = np.random.default_rng(N + K)
+    w = synth.gen("wan", seed=12, B=B, H=H, N=N, d=d)
+    C = (rng.standard_normal((B, H, K, d)) * 2).astype(np.float32)
+    lab = rng.integers(0, K, (B, H, N)).astype(np.int32)
+    cost = torch.empty((B, H), dtype=torch.float64, device="cuda")
+    vc.vc_cluster_cost(to_dev_bf16(w["V"]), to_dev(C), to_dev(lab), cost)
+    got = cost.cpu().numpy()
+    for h in range(H):
+        want = oracle.kmeans_cost(w["V"][0, h], C[0, h], lab[0, h])
+        assert abs(got[0, h] - want) <= 1e-11 * want, (h, got[0, h], want)
+
+
 def test_cluster_deterministic():
     w = synth.gen("wan", seed=8, B=1, H=2, N=2048, d=128)
     a = _gpu_cluster(w["V"], 16, 2, True)

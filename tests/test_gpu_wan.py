@@ -96,6 +96,21 @@ def test_wan_kmeans_bitexact_sampled_heads(run, oracle_heads):
         assert np.array_equal(run["C"][0, h], o["C"]), h
 
 
+def test_wan_cluster_cost_sampled_heads(run, oracle_heads):
+    """The drift statistic at full size: k-means objective of V under the warm-started
+    clustering, all heads on the GPU, two heads against the oracle (relative 1e-11)."""
+    w = run["w"]
+    B, H, N, d = w["V"].shape
+    cost = torch.empty((B, H), dtype=torch.float64, device="cuda")
+    vc.vc_cluster_cost(to_dev_bf16(w["V"]), torch.from_numpy(run["C"]).cuda(), torch.from_numpy(run["lab"]).cuda(),
+                       cost)
+    got = cost.cpu().numpy()
+    for h in HEADS:
+        want = oracle.kmeans_cost(w["V"][0, h], oracle_heads[h]["C"], oracle_heads[h]["lab"])
+        assert abs(got[0, h] - want) <= 1e-11 * want, (h, got[0, h], want)
+    assert np.all(got > 0)
+
+
 def test_wan_quantize_bitexact_sampled_heads(run, oracle_heads):
     g = run["q"]
     for h in HEADS:

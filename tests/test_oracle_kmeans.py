@@ -105,3 +105,24 @@ def test_cold_start_picks_strided_tokens():
     labels, perm, C = oracle.kmeans(V, K, 1, cold=True)
     init = synth.bf16_to_f32(V[[(2 * k + 1) * N // (2 * K) for k in range(K)]])
     assert np.array_equal(labels, oracle.kmeans_assign(V, init))
+
+
+def test_kmeans_cost_brute_force_and_zero():
+    """k-means objective (drift statistic): exact rational (1/N) sum ||V_t - bf16(C_z)||^2,
+    correctly rounded; zero when every token is its own centroid."""
+    from fractions import Fraction
+    rng = np.random.default_rng(41)
+    N, d, K = 96, 8, 5
+    V = synth.bf16_bits((rng.standard_normal((N, d)) * np.exp2(rng.integers(-6, 6, (N, d)))).astype(np.float32))
+    C = (rng.standard_normal((K, d)) * 2).astype(np.float32)
+    z = rng.integers(0, K, N).astype(np.int32)
+    Vf = synth.bf16_to_f32(V)
+    Ch = synth.bf16_to_f32(synth.bf16_bits(C))
+    tot = Fraction(0)
+    for t in range(N):
+        for j in range(d):
+            df = Fraction(float(Vf[t, j])) - Fraction(float(Ch[z[t], j]))
+            tot += df * df
+    assert oracle.kmeans_cost(V, C, z) == float(tot / N)
+    Vs = synth.bf16_bits(rng.standard_normal((16, d)).astype(np.float32))
+    assert oracle.kmeans_cost(Vs, synth.bf16_to_f32(Vs), np.arange(16, dtype=np.int32)) == 0.0
