@@ -34,6 +34,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 FLAG_KSMOOTH = 1
 FLAG_VSMOOTH = 2
 FLAG_HADAMARD = 16
+FLAG_MXFP4 = 32
 MODE_EXPCAST = 0
 MODE_EXP_THEN_CAST = 1
 MODE_EXACT_PROB = 2
@@ -88,6 +89,10 @@ def lib() -> ctypes.CDLL:
         _lib.or_e4m3_encode_array.argtypes = [P, P, L]
         _lib.or_e4m3_decode_array.argtypes = [P, P, L]
         _lib.or_e5m2_decode_array.argtypes = [P, P, L]
+        _lib.or_e2m1_decode.restype = ctypes.c_double
+        _lib.or_e2m1_decode.argtypes = [ctypes.c_uint8]
+        _lib.or_e2m1_encode.restype = ctypes.c_uint8
+        _lib.or_e2m1_encode.argtypes = [ctypes.c_double]
         _lib.or_expcast.restype = ctypes.c_uint8
         _lib.or_expcast.argtypes = [F, F, F]
         _lib.or_expcast_array.argtypes = [P, P, P, P, L]
@@ -99,10 +104,10 @@ def lib() -> ctypes.CDLL:
         _lib.or_kmeans_cost.argtypes = [P, I, I, P, I, P]
         _lib.or_quantize.restype = I
         _lib.or_quantize.argtypes = [P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
-        _lib.or_quantize_ex.argtypes = [P, P, P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P]
+        _lib.or_quantize_ex.argtypes = [P, P, P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P, P]
         _lib.or_rope.argtypes = [P, P, P, I, I, P]
         _lib.or_fwht_rows.argtypes = [P, I, I]
-        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P]
+        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P, P]
         _lib.or_attention_exact.argtypes = [P, P, P, I, I, I, P, P]
         _lib.or_exact_mean.restype = ctypes.c_double
         _lib.or_exact_mean.argtypes = [P, L, I]
@@ -149,6 +154,16 @@ def e5m2_decode(codes) -> np.ndarray:
     out = np.empty(c.shape, np.float64)
     lib().or_e5m2_decode_array(_p(c), _p(out), c.size)
     return out
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, np.uint8)
+    return np.vectorize(lambda v: lib().or_e2m1_decode(int(v)), otypes=[np.float64])(c)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    a = np.asarray(x, np.float64)
+    return np.vectorize(lambda v: lib().or_e2m1_encode(float(v)), otypes=[np.uint8])(a)
 
 
 def e4m3_encode(x) -> np.ndarray:
@@ -249,12 +264,15 @@ def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOT
         mu=np.zeros((nb, d), np.uint16), mu_scaled=np.zeros((nb, d), np.float32),
         kbar=np.empty(d, np.float32),
     )
+    if flags & FLAG_MXFP4:
+        out["Vs"] = np.empty((nb, d, 4), np.uint8)
     rc_, rs_ = (None, None) if rope_cos is None else (_c(rope_cos, np.float32), _c(rope_sin, np.float32))
     rc = lib().or_quantize_ex(_p(Q), _p(K), _p(V), None if pm is None else _p(pm),
                               None if rc_ is None else _p(rc_), None if rs_ is None else _p(rs_), N, d, int(flags),
                               float(log2e_over_sqrt_d(d)),
                            _p(out["Qq"]), _p(out["sQ"]), _p(out["Kq"]), _p(out["sK"]), _p(out["Vq"]),
-                           _p(out["sV"]), _p(out["mu"]), _p(out["mu_scaled"]), _p(out["kbar"]))
+                           _p(out["sV"]), _p(out["mu"]), _p(out["mu_scaled"]), _p(out["kbar"]),
+                           _p(out["Vs"]) if "Vs" in out else None)
     if rc != 0:
         raise ValueError("oracle quantize: N must be a multiple of 128")
     out["flags"] = flags
@@ -280,7 +298,7 @@ def attention_emul(q: dict, rows, beta: float = -0.35, mode: int = MODE_EXPCAST,
                             None if mu is None else _p(_c(mu, np.float32)), N, d, float(np.float32(beta)),
                             int(mode), rows.size, _p(rows), _p(O), int(dump_block),
                             None if dump is None else _p(dump), None if mm is None else _p(mm),
-                            None if W is None else _p(W))
+                            None if W is None else _p(W), _p(q["Vs"]) if "Vs" in q else None)
     res = [O]
     if dump is not None:
         res.append(dump)
@@ -316,7 +334,12 @@ def error_terms(Q_bits, K_bits, V_bits, q: dict, perm, rows, beta: float = -0.35
     s = Qf @ Kf.T / np.sqrt(d)
     P = np.exp(s - s.max(axis=1, keepdims=True))
     P /= P.sum(axis=1, keepdims=True)
-    Vq = e4m3_decode(q["Vq"]).astype(np.float64)
+    if "Vs" in q:   # MXFP4: E2M1 codes times each group's power-of-two scale
+        grp = 2 * (np.arange(BLOCK) >> 6) + ((np.arange(BLOCK) >> 4) & 1)
+        sc = np.exp2(q["Vs"].astype(np.float64) - 127.0)                      # [nb, d, 4]
+        Vq = e2m1_decode(q["Vq"]) * sc[:, :, grp].transpose(0, 2, 1).reshape(N, d)
+    else:
+        Vq = e4m3_decode(q["Vq"]).astype(np.float64)
     if vs:
         Vq = Vq + np.repeat(q["mu_scaled"].astype(np.float64), BLOCK, axis=0)
     Vq *= q["sV"].astype(np.float64)[None, :]

@@ -419,6 +419,49 @@ double or_kmeans_cost(const uint16_t* V, int N, int d, const float* C, int K, co
 /* Layout of every array here: row-major [N, d] (Vq too).                   */
 /* flags: 1 = K smoothing, 2 = V-Smooth (block means)                       */
 /* ------------------------------------------------------------------------ */
+/* ------------------------------------------------------------------------ */
+/* 4-bit residual (paper page, method step (2): the residual is quantised    */
+/* to 4 bits on workstation parts; news page: the 4-bit path). Reading:      */
+/* OCP MXFP4 -- E2M1 elements (1 sign, 2 exponent bits with bias 1, 1        */
+/* mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6) sharing one power-of-two (E8M0)  */
+/* scale per group of 32 keys of one channel; the scale is the smallest 2^e  */
+/* with amax <= 6 * 2^e (no element clips), amax = 0 gives 2^0 and zero      */
+/* codes, e is clamped to [-127, 127]; elements are the E2M1 value nearest to */
+/* x / 2^e, ties to even mantissa; a value that rounds to zero keeps a plus   */
+/* sign. Groups: within each 64-key half of a 128-key block, group g (0, 1)   */
+/* holds the keys 16g..16g+15 and 32+16g..32+16g+15 -- the 32 elements that  */
+/* the matrix core scales together.                                          */
+/* ------------------------------------------------------------------------ */
+double or_e2m1_decode(uint8_t c) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  return (c & 8) ? -mag[c & 7] : mag[c & 7];
+}
+
+/* nearest E2M1 code of x (|x| <= 6), ties to even mantissa */
+uint8_t or_e2m1_encode(double x) {
+  double a = fabs(x);
+  int best = 0;
+  for (int c = 1; c < 8; c++) { /* codes increase in value; pick nearest, ties to the even code */
+    double dc = fabs(or_e2m1_decode((uint8_t)c) - a), db = fabs(or_e2m1_decode((uint8_t)best) - a);
+    if (dc < db || (dc == db && (c & 1) == 0 && (best & 1) == 1)) best = c;
+  }
+  return (uint8_t)(best == 0 ? 0 : (x < 0 ? (best | 8) : best));
+}
+
+/* group (0..3) of key t (0..127) of a block: 2 * half + ((t >> 4) & 1) */
+static inline int mx_group(int t) { return 2 * (t >> 6) + ((t >> 4) & 1); }
+
+/* E8M0 exponent for a group maximum: the smallest e with amax <= 6 * 2^e */
+static int mx_exponent(double amax) {
+  if (amax == 0.0) return 0;
+  int e = ilogb(amax) - 2;
+  while (ldexp(6.0, e) < amax) e++;
+  while (ldexp(6.0, e - 1) >= amax) e--;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
 static void quant_block(const float* x, int rows, int d, uint8_t* codes, float* scale) {
   float a = 0.0f;
   for (int64_t i = 0; i < (int64_t)rows * d; i++) { float m = fabsf(x[i]); if (m > a) a = m; }
@@ -475,7 +518,8 @@ int or_quantize_ex(const uint16_t* Qin, const uint16_t* Kin, const uint16_t* V, 
                    const float* rope_cos, const float* rope_sin,
                    int N, int d, int flags, float cL,
                    uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
-                   uint16_t* mu, float* mu_scaled, float* kbar_out) {
+                   uint16_t* mu, float* mu_scaled, float* kbar_out,
+                   uint8_t* vscale /* [N/128, d, 4] E8M0 bytes with flag 32 (MXFP4), else unused */) {
   if (N % 128) return 2;
   int nb = N / 128;
   int log2d = 0;
@@ -552,16 +596,38 @@ int or_quantize_ex(const uint16_t* Qin, const uint16_t* Kin, const uint16_t* V, 
       }
     }
   }
-  for (int j = 0; j < d; j++) {
-    float a = 0.0f;
-    for (int t = 0; t < N; t++) { float m = fabsf(R[(int64_t)t * d + j]); if (m > a) a = m; }
-    float s, inv;
-    if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; }
-    else { s = 1.0f; inv = 0.0f; }
-    sV[j] = s;
-    for (int t = 0; t < N; t++) Vq[(int64_t)t * d + j] = or_e4m3_encode(R[(int64_t)t * d + j] * inv);
-    if (mu_scaled)
-      for (int b = 0; b < nb; b++) mu_scaled[(int64_t)b * d + j] = (flags & 2) ? bf16_val(mu[(int64_t)b * d + j]) / s : 0.0f;
+  if (flags & 32) { /* MXFP4 residual: one code (0..15) per byte of Vq, scales in vscale, sV = 1 */
+    for (int b = 0; b < nb; b++)
+      for (int j = 0; j < d; j++)
+        for (int g = 0; g < 4; g++) {
+          double a = 0.0;
+          for (int t = 0; t < 128; t++)
+            if (mx_group(t) == g) { double m = fabs((double)R[((int64_t)b * 128 + t) * d + j]); if (m > a) a = m; }
+          int e = mx_exponent(a);
+          vscale[((int64_t)b * d + j) * 4 + g] = (uint8_t)(e + 127);
+          for (int t = 0; t < 128; t++)
+            if (mx_group(t) == g) {
+              int64_t o = ((int64_t)b * 128 + t) * d + j;
+              Vq[o] = or_e2m1_encode(ldexp((double)R[o], -e));
+            }
+        }
+    for (int j = 0; j < d; j++) {
+      sV[j] = 1.0f;
+      if (mu_scaled)
+        for (int b = 0; b < nb; b++) mu_scaled[(int64_t)b * d + j] = (flags & 2) ? bf16_val(mu[(int64_t)b * d + j]) : 0.0f;
+    }
+  } else {
+    for (int j = 0; j < d; j++) {
+      float a = 0.0f;
+      for (int t = 0; t < N; t++) { float m = fabsf(R[(int64_t)t * d + j]); if (m > a) a = m; }
+      float s, inv;
+      if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; }
+      else { s = 1.0f; inv = 0.0f; }
+      sV[j] = s;
+      for (int t = 0; t < N; t++) Vq[(int64_t)t * d + j] = or_e4m3_encode(R[(int64_t)t * d + j] * inv);
+      if (mu_scaled)
+        for (int b = 0; b < nb; b++) mu_scaled[(int64_t)b * d + j] = (flags & 2) ? bf16_val(mu[(int64_t)b * d + j]) / s : 0.0f;
+    }
   }
   free(R);
   free(kbar);
@@ -572,7 +638,8 @@ int or_quantize(const uint16_t* Q, const uint16_t* K, const uint16_t* V, const i
                 int N, int d, int flags, float cL,
                 uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
                 uint16_t* mu, float* mu_scaled, float* kbar_out) {
-  return or_quantize_ex(Q, K, V, perm, NULL, NULL, N, d, flags, cL, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, kbar_out);
+  return or_quantize_ex(Q, K, V, perm, NULL, NULL, N, d, flags & ~32, cL, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled,
+                        kbar_out, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -613,13 +680,18 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
                        int nrows, const int32_t* rows, double* O /* [nrows, d] */,
                        int dump_block, uint8_t* dump_codes /* [nrows, 128] or NULL */,
                        float* dump_m /* [nrows, N/128] running max after each block, or NULL */,
-                       double* weights /* [nrows, N] effective weight of each key in O, or NULL */) {
+                       double* weights /* [nrows, N] effective weight of each key in O, or NULL */,
+                       const uint8_t* vscale /* [N/128, d, 4] MXFP4 scales: Vq holds E2M1 codes; NULL: E4M3 */) {
   int nb = N / 128;
   const float C0 = 120.0f + beta;
-  /* decoded operand tables as exact integers */
+  /* decoded operand tables as exact integers: E4M3 values * 2^9; with MXFP4, E2M1 values * 2
+   * (the group's power-of-two scale is applied per group below) */
   int32_t* Ku = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * d);
   int32_t* Vu = (int32_t*)malloc(sizeof(int32_t) * (size_t)N * d);
-  for (int64_t i = 0; i < (int64_t)N * d; i++) { Ku[i] = e4m3_units(Kq[i]); Vu[i] = e4m3_units(Vq[i]); }
+  for (int64_t i = 0; i < (int64_t)N * d; i++) {
+    Ku[i] = e4m3_units(Kq[i]);
+    Vu[i] = vscale ? (int32_t)lrint(2.0 * or_e2m1_decode(Vq[i])) : e4m3_units(Vq[i]);
+  }
 #pragma omp parallel
   {
     int32_t* qu = (int32_t*)malloc(sizeof(int32_t) * d);
@@ -682,7 +754,21 @@ void or_attention_emul(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, co
           double pv;
           if (mode == 2) {
             pv = 0.0;
-            for (int t = 0; t < 128; t++) pv += pt[t] * ldexp((double)Vu[(int64_t)(j * 128 + t) * d + c], -9);
+            for (int t = 0; t < 128; t++)
+              pv += pt[t] * (vscale ? ldexp((double)Vu[(int64_t)(j * 128 + t) * d + c],
+                                            (int)vscale[((int64_t)j * d + c) * 4 + mx_group(t)] - 128)
+                                    : ldexp((double)Vu[(int64_t)(j * 128 + t) * d + c], -9));
+          } else if (vscale) {
+            /* MXFP4 values: (Vu/2) * 2^e per group of 32 keys, summed exactly per group */
+            const int pe = mode == 3 ? -16 : -9;
+            pv = 0.0;
+            for (int g = 0; g < 4; g++) {
+              int64_t b = 0;
+              for (int t = 0; t < 128; t++)
+                if (mx_group(t) == g) b += pu[t] * Vu[(int64_t)(j * 128 + t) * d + c];
+              const int e = (int)vscale[((int64_t)j * d + c) * 4 + g] - 127;
+              pv += ldexp((double)b, pe - 1 + e);
+            }
           } else {
             /* exact: E4M3 codes and residual bytes are multiples of 2^-9, E5M2 codes of
              * 2^-16; |sum| < 128 * 2^31 * 2^18 fits in 64 bits */
