@@ -25,6 +25,7 @@ VC_F_VSMOOTH = 2
 VC_F_EXPCAST = 4
 VC_F_E5M2 = 8
 VC_F_HADAMARD = 16
+VC_F_MXFP4 = 32
 BLOCK = 128
 
 _STATUS = {0: "VC_OK", 1: "VC_E_NULLPTR", 2: "VC_E_SHAPE", 3: "VC_E_PARAM", 4: "VC_E_WORKSPACE",

@@ -18,7 +18,8 @@ extern "C" int vc_launch_cluster_cost(const void* V, const float* C, const int32
                                       int K, double* cost, void* ws, hipStream_t st);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
-                                   float beta, int pmode, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st);
+                                   float beta, int pmode, int mx, uint16_t* O, int dump_block, uint8_t* dump,
+                                   hipStream_t st);
 extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
                                  hipStream_t st);
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
@@ -145,7 +146,7 @@ static vc_status quantize_common(const void* Q, const void* K, const void* V, co
   if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || !workspace) return VC_E_NULLPTR;
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
-  if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_HADAMARD)) return VC_E_PARAM;
+  if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_HADAMARD | VC_F_MXFP4)) return VC_E_PARAM;
   if (workspace_bytes < vc_quantize_ws_bytes(B, H, N, d)) return VC_E_WORKSPACE;
   const void* ptrs[] = {Q, K, V, perm, rope_cos, rope_sin, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, mu_pack, workspace};
   for (const void* p : ptrs)
@@ -192,7 +193,8 @@ static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint
                                   void* stream) {
   if (!Qq || !sQ || !Kq || !sK || !Vq || !sV || !O) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
-  if (!isfinite(beta) || (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_E5M2)))
+  if (!isfinite(beta) ||
+      (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_E5M2 | VC_F_MXFP4)))
     return VC_E_PARAM;
   if ((flags & VC_F_E5M2) && !(flags & VC_F_EXPCAST)) return VC_E_PARAM;  // E5M2 bytes exist only as ExpCast
   const void* ptrs[] = {Qq, sQ, Kq, sK, Vq, sV, mu_pack, O, codes};
@@ -208,7 +210,7 @@ static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
   const int pmode = (flags & VC_F_EXPCAST) ? ((flags & VC_F_E5M2) ? 2 : 1) : 0;
-  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, pmode,
+  if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, pmode, (flags & VC_F_MXFP4) ? 1 : 0,
                           (uint16_t*)O, dump_block, codes, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;

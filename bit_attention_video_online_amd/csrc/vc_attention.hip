@@ -59,6 +59,9 @@ __device__ __forceinline__ int k_off(int row, int chunk) {
   return row * D + ((chunk ^ k_swz<D>(row)) << 4);
 }
 __device__ __forceinline__ int v_swz(int row) { return (row >> 1) & 7; }
+// MXFP4 code rows are 64 bytes (4 chunks); row bits 2..3 keep every fragment read
+// conflict-free under the same pass model, and the +32-row d-block offset leaves them alone
+__device__ __forceinline__ int mx_swz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int v_off(int row, int chunk) { return row * 128 + ((chunk ^ v_swz(row)) << 4); }
 
 __device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
@@ -146,7 +149,9 @@ __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0f7
 // PM selects the probability bytes: 0 exp-then-cast (E4M3), 1 ExpCast E4M3 (8 codes per
 // octave, code 120 = 2^8), 2 ExpCast E5M2 (4 codes per octave, code 120 = 2^15; the PV and
 // row-sum MFMAs read their B operand as BF8).
-template <int D, int PM, bool RESTORE, bool DUMP>
+// MX selects the 4-bit value residual (MXFP4): V tiles hold E2M1 codes [channel][64 bytes]
+// in the block-scaled MFMA's operand order plus one E8M0 scale per channel and 32-key group.
+template <int D, int PM, bool RESTORE, bool DUMP, bool MX>
 __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t* __restrict__ Qq, const float* __restrict__ sQ,
                                                          const uint8_t* __restrict__ Kq, const float* __restrict__ sK,
                                                          const uint8_t* __restrict__ Vq, const float* __restrict__ sV,
@@ -225,8 +230,13 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     const int P = wave * 64 + lane;
     const int row = P / CPR, phys = P % CPR;
     ksrc = row * D + 16 * (phys ^ k_swz<D>(row));
-    const int vrow = P >> 3, vphys = P & 7;
-    vsrc = vrow * 128 + 16 * (vphys ^ v_swz(vrow));
+    if (MX) {  // code rows are 64 bytes: 4 chunks, XOR pattern (row >> 2) & 3
+      const int vrow = P >> 2, vphys = P & 3;
+      vsrc = vrow * 64 + 16 * (vphys ^ mx_swz(vrow));
+    } else {
+      const int vrow = P >> 3, vphys = P & 7;
+      vsrc = vrow * 128 + 16 * (vphys ^ v_swz(vrow));
+    }
   }
   auto issue_k = [&](int j, auto st) {  // K_j into stage st (= j & 1)
     uint8_t* kd = decltype(st)::value ? kst1 : kst0;
@@ -235,8 +245,14 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   };
   auto issue_v = [&](int j, auto st) {  // V_j into stage st (= j & 1)
     uint8_t* vd = decltype(st)::value ? vst1 : vst0;
-    for (int i = 0; i < PW; i++)
-      buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
+    if (MX) {  // 64 D bytes of codes, then 4 D bytes of scales (wave 0, lanes < D/4)
+      for (int i = 0; i < PW / 2; i++)
+        buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
+      if (wave == 0 && lane < D / 4) buf2lds16(vrs, lane * 16, j * TILE + 64 * D, (lds_void*)(vd + 64 * D));
+    } else {
+      for (int i = 0; i < PW; i++)
+        buf2lds16(vrs, vsrc, j * TILE + i * kAThreads * 16, (lds_void*)(vd + (wave * 64 + kAThreads * i) * 16));
+    }
   };
   // mean operand of chunk c: NDB x 2 MFMAs x 64 lanes x 16 bytes, one 1 KB piece per wave
   auto issue_pack = [&](int c) {
@@ -255,6 +271,8 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   }
   const int vA0 = v_off(r32, 2 * h), vB0 = v_off(r32, 2 * h + 1);
   const int vA1 = v_off(r32, 4 + 2 * h), vB1 = v_off(r32, 4 + 2 * h + 1);
+  // MXFP4: lane (r32, h) of half kh reads chunk 2 kh + h of code row r32 (+32 per d block)
+  const int vM0 = r32 * 64 + 16 * ((0 + h) ^ mx_swz(r32)), vM1 = r32 * 64 + 16 * ((2 + h) ^ mx_swz(r32));
 
   float m = -__builtin_inff(), lsum = 0.0f;
   v16f oacc[NDB];
@@ -305,6 +323,18 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   };
   // O^T += V_j^T P^T for the 64-key half kh
   auto pv_part = [&](const uint8_t* vt, int kh, const v8i& p) {
+    if (MX) {
+      // A: 32 E2M1 codes in 4 dwords (keys 16h..+15 and 32+16h..+15 of the half); its E8M0
+      // scale, byte 2 kh + h of the channel's four, scales exactly those 32 elements
+      for (int db = 0; db < NDB; db++) {
+        const uint4 f = *reinterpret_cast<const uint4*>(vt + (kh ? vM1 : vM0) + 32 * db * 64);
+        v8i a;
+        a[0] = f.x; a[1] = f.y; a[2] = f.z; a[3] = f.w; a[4] = 0; a[5] = 0; a[6] = 0; a[7] = 0;
+        const int sc = vt[64 * D + 4 * (32 * db + r32) + 2 * kh + h];
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p, oacc[db], 4, PFMT, 0, sc, 0, 127);
+      }
+      return;
+    }
     const int A0 = kh ? vA1 : vA0, B0 = kh ? vB1 : vB0;
     for (int db = 0; db < NDB; db++) {
       const int vo = 32 * db * 128;
@@ -454,49 +484,55 @@ __global__ void expcast_kernel(const float* __restrict__ acc, const float* __res
   if (i < n) out[i] = (uint8_t)expcast_byte(acc[i], s8[i], bias[i], 0u, 0);
 }
 
-template <int D, int PM, bool R, bool DU>
+template <int D, int PM, bool R, bool DU, bool MX>
 static void launch_attn(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
                         const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                         uint8_t* dump, hipStream_t st) {
   const int total = BH * ((N / kBlock + kQB - 1) / kQB);
-  attn_fwd<D, PM, R, DU><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
+  attn_fwd<D, PM, R, DU, MX><<<total, kAThreads, 0, st>>>(Qq, sQ, Kq, sK, Vq, sV, mu, N, total, C0, O, dump_block, dump);
 }
 
-template <int D, int PM>
+template <int D, int PM, bool MX>
 static void launch_attn_d(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK, const uint8_t* Vq,
                           const float* sV, const uint16_t* mu, int BH, int N, float C0, uint16_t* O, int dump_block,
                           uint8_t* dump, hipStream_t st) {
   if (mu) {
-    if (dump) launch_attn<D, PM, true, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-    else launch_attn<D, PM, true, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    if (dump) launch_attn<D, PM, true, true, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn<D, PM, true, false, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
   } else {
-    if (dump) launch_attn<D, PM, false, true>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-    else launch_attn<D, PM, false, false>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    if (dump) launch_attn<D, PM, false, true, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn<D, PM, false, false, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
   }
 }
 
-template <int D>
+template <int D, bool MX>
 static void launch_attn_pm(int pmode, const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                            const uint8_t* Vq, const float* sV, const uint16_t* mu, int BH, int N, float C0,
                            uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
-  if (pmode == 2) launch_attn_d<D, 2>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-  else if (pmode == 1) launch_attn_d<D, 1>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-  else launch_attn_d<D, 0>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  if (pmode == 2) launch_attn_d<D, 2, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else if (pmode == 1) launch_attn_d<D, 1, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  else launch_attn_d<D, 0, MX>(Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
 }
 
 }  // namespace vc
 
 using namespace vc;
 
-// pmode: 0 exp-then-cast, 1 ExpCast E4M3, 2 ExpCast E5M2
+// pmode: 0 exp-then-cast, 1 ExpCast E4M3, 2 ExpCast E5M2; mx: 4-bit (MXFP4) value residual
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
                                    const uint8_t* Vq, const float* sV, const void* mu_pack, int B, int H, int N, int d,
-                                   float beta, int pmode, uint16_t* O, int dump_block, uint8_t* dump, hipStream_t st) {
+                                   float beta, int pmode, int mx, uint16_t* O, int dump_block, uint8_t* dump,
+                                   hipStream_t st) {
   const uint16_t* mu = (const uint16_t*)mu_pack;
   const int BH = B * H;
   const float C0 = 120.0f + beta;  // fl32(120 + beta)
-  if (d == 128) launch_attn_pm<128>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
-  else launch_attn_pm<64>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  if (d == 128) {
+    if (mx) launch_attn_pm<128, true>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn_pm<128, false>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  } else {
+    if (mx) launch_attn_pm<64, true>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+    else launch_attn_pm<64, false>(pmode, Qq, sQ, Kq, sK, Vq, sV, mu, BH, N, C0, O, dump_block, dump, st);
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

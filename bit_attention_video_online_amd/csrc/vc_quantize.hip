@@ -62,6 +62,24 @@ __device__ __forceinline__ void load_tile(const uint16_t* base, const int32_t* p
 }
 
 constexpr uint32_t kFlagHadamard = 16u;  // flag bit of the Q/K rotation
+constexpr uint32_t kFlagMxfp4 = 32u;     // flag bit of the 4-bit (MXFP4) value residual
+
+// MXFP4 value residual. E2M1 code of x (|x| <= 6): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+// ties to the even mantissa; a value that rounds to zero keeps a plus sign.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return (c != 0u && x < 0.0f) ? (c | 8u) : c;
+}
+// group scale exponent: the smallest e with amax <= 6 * 2^e (0 for amax = 0), within [-127, 127]
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  int e = ilogbf(amax) - 2;
+  while (ldexpf(6.0f, e) < amax) e++;
+  while (ldexpf(6.0f, e - 1) >= amax) e--;
+  return min(127, max(-127, e));
+}
 
 // RoPE on the thread's RPT rows (channel pairs 4*chunk .. +3 of each row); `pos` gives the
 // token whose angles apply (its row in the tables). Each rotated value is rounded to bf16.
@@ -278,13 +296,14 @@ __global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags,
     for (int k = 0; k < G; k++) { t += ps[k * D + c]; a = fmaxf(a, pm[k * D + c]); }
     kbar[(size_t)bh * D + c] = (flags & 1u) ? div_to_f32(t, (double)N) : 0.0f;
     float s, inv;
-    if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
+    if (flags & kFlagMxfp4) { s = 1.0f; inv = 0.0f; }  // the group scales carry the range
+    else if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
     sV[(size_t)bh * D + c] = s;
     vinv[(size_t)bh * D + c] = inv;
   }
 }
 
-template <int D, bool ROPE, bool HAD>
+template <int D, bool ROPE, bool HAD, bool MX>
 __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                          const int32_t* __restrict__ perm, const float* __restrict__ rc,
                                                          const float* __restrict__ rs, int N, uint32_t flags,
@@ -333,6 +352,36 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
     if (pblk) load_tile<D>(V + head, pblk, N, x);
     else load_tile<D>(V + head + jrow, nullptr, kBlock, x);
     uint8_t* vb = Vq + head + jrow;
+    if (MX) {
+      // MXFP4: codes [c][64 bytes] then E8M0 scales [c][4] at byte 64 D of the block. Token t
+      // of half q = t>>6 is nibble p = 16((t&63)>>5) + (t&15) of lane group g = (t>>4)&1, at
+      // byte 32q + 16g + p/2 (low nibble first) -- the operand order of the block-scaled MFMA,
+      // whose per-lane scale covers exactly group 2q + g of a channel.
+      __shared__ uint32_t gmax[4 * D];
+      for (int i = threadIdx.x; i < 4 * D; i += kQThreads) gmax[i] = 0u;
+      __syncthreads();
+      const int t0 = RPT * rg;
+      const int q = t0 >> 6, g = (t0 >> 4) & 1, G = 2 * q + g;
+      const int p0 = 16 * ((t0 & 63) >> 5) + (t0 & 15);
+      for (int i = 0; i < RPT; i++)
+        for (int e = 0; e < 8; e++) x[i][e] = x[i][e] - m[e];
+      for (int e = 0; e < 8; e++) {
+        float a = 0.0f;
+        for (int i = 0; i < RPT; i++) a = fmaxf(a, fabsf(x[i][e]));
+        atomicMax(&gmax[G * D + 8 * chunk + e], __float_as_uint(a));  // order-free for non-negative floats
+      }
+      __syncthreads();
+      for (int e = 0; e < 8; e++) {
+        const int ex = mx_exponent(__uint_as_float(gmax[G * D + 8 * chunk + e]));
+        uint32_t wd = 0u;
+        for (int i = 0; i < RPT; i++) wd |= e2m1_code(ldexpf(x[i][e], -ex)) << (4 * i);
+        uint8_t* dst = vb + (size_t)(8 * chunk + e) * 64 + 32 * q + 16 * g + p0 / 2;
+        if (RPT == 8) *reinterpret_cast<uint32_t*>(dst) = wd;
+        else *reinterpret_cast<uint16_t*>(dst) = (uint16_t)wd;
+      }
+      for (int idx = threadIdx.x; idx < 4 * D; idx += kQThreads)
+        vb[64 * D + idx] = (uint8_t)(mx_exponent(__uint_as_float(gmax[(idx & 3) * D + (idx >> 2)])) + 127);
+    } else
     for (int e = 0; e < 8; e++) {
       uint32_t wds[RPT / 4];
       for (int k = 0; k < RPT / 4; k++)
@@ -392,12 +441,12 @@ struct QArgs {
   float *vamax, *kbar, *vinv;
 };
 
-template <int D, bool ROPE, bool HAD>
+template <int D, bool ROPE, bool HAD, bool MX>
 static void launch_quant(const QArgs& a, dim3 grid, int BH, hipStream_t st) {
   quant_stats<D, ROPE, HAD><<<grid, kQThreads, 0, st>>>(a.Q, a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.cL, a.Qq,
                                                          a.sQ, a.mu, a.ksum, a.vamax);
   quant_reduce<D><<<BH, kQThreads, 0, st>>>(a.N, a.flags, a.ksum, a.vamax, a.kbar, a.sV, a.vinv);
-  quant_apply<D, ROPE, HAD><<<grid, kQThreads, 0, st>>>(a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.kbar, a.sV,
+  quant_apply<D, ROPE, HAD, MX><<<grid, kQThreads, 0, st>>>(a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.kbar, a.sV,
                                                          a.vinv, a.mu, a.Kq, a.sK, a.Vq, a.mu_scaled, a.mu_pack);
 }
 
@@ -421,13 +470,30 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
   dim3 grid(nb, BH);
   const QArgs a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, perm, rc, rs, N, flags, cL, Qq, sQ,
                 Kq, sK, Vq, sV, mup, mu_scaled, (uint16_t*)mu_pack, ksum, vamax, kbar, vinv};
-  const bool rope = rc != nullptr, had = (flags & kFlagHadamard) != 0;
+  const bool rope = rc != nullptr, had = (flags & kFlagHadamard) != 0, mx = (flags & kFlagMxfp4) != 0;
+  const int sel = (rope ? 4 : 0) | (had ? 2 : 0) | (mx ? 1 : 0);
   if (d == 128) {
-    if (rope) { if (had) launch_quant<128, true, true>(a, grid, BH, st); else launch_quant<128, true, false>(a, grid, BH, st); }
-    else { if (had) launch_quant<128, false, true>(a, grid, BH, st); else launch_quant<128, false, false>(a, grid, BH, st); }
+    switch (sel) {
+      case 0: launch_quant<128, false, false, false>(a, grid, BH, st); break;
+      case 1: launch_quant<128, false, false, true>(a, grid, BH, st); break;
+      case 2: launch_quant<128, false, true, false>(a, grid, BH, st); break;
+      case 3: launch_quant<128, false, true, true>(a, grid, BH, st); break;
+      case 4: launch_quant<128, true, false, false>(a, grid, BH, st); break;
+      case 5: launch_quant<128, true, false, true>(a, grid, BH, st); break;
+      case 6: launch_quant<128, true, true, false>(a, grid, BH, st); break;
+      default: launch_quant<128, true, true, true>(a, grid, BH, st); break;
+    }
   } else {
-    if (rope) { if (had) launch_quant<64, true, true>(a, grid, BH, st); else launch_quant<64, true, false>(a, grid, BH, st); }
-    else { if (had) launch_quant<64, false, true>(a, grid, BH, st); else launch_quant<64, false, false>(a, grid, BH, st); }
+    switch (sel) {
+      case 0: launch_quant<64, false, false, false>(a, grid, BH, st); break;
+      case 1: launch_quant<64, false, false, true>(a, grid, BH, st); break;
+      case 2: launch_quant<64, false, true, false>(a, grid, BH, st); break;
+      case 3: launch_quant<64, false, true, true>(a, grid, BH, st); break;
+      case 4: launch_quant<64, true, false, false>(a, grid, BH, st); break;
+      case 5: launch_quant<64, true, false, true>(a, grid, BH, st); break;
+      case 6: launch_quant<64, true, true, false>(a, grid, BH, st); break;
+      default: launch_quant<64, true, true, true>(a, grid, BH, st); break;
+    }
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -56,7 +56,8 @@ enum {
   VC_F_VSMOOTH = 2u, /* block-mean removal of V' and mean restoration */
   VC_F_EXPCAST = 4u, /* ExpCast-FP8 probability bytes (else exp2 then cast) */
   VC_F_E5M2 = 8u,    /* with VC_F_EXPCAST: the bytes are E5M2 (4 codes per octave) */
-  VC_F_HADAMARD = 16u /* quantiser: rotate Q and K~' rows by the Hadamard matrix first */
+  VC_F_HADAMARD = 16u, /* quantiser: rotate Q and K~' rows by the Hadamard matrix first */
+  VC_F_MXFP4 = 32u     /* 4-bit (MXFP4) value residual: vc_quantize writes it, vc_attention reads it */
 };
 
 /* Static description of a status code (host function, never NULL). */
@@ -119,7 +120,7 @@ vc_status vc_cluster_cost(const void* V, const float* centroids, const int32_t* 
  *   Q, K, V    bf16 [B,H,N,d]
  *   perm       int32 [B,H,N], or NULL for the identity (plain FP8 path)
  *   block      must be 128
- *   flags      VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_HADAMARD (VC_F_EXPCAST ignored)
+ *   flags      VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_HADAMARD | VC_F_MXFP4 (VC_F_EXPCAST ignored)
  * Outputs (all written on success):
  *   Qq   uint8 [B,H,N,d]           E4M3 codes of Q, original token order
  *   sQ   float [B,H,N/128]         Q block scale times fl32(log2(e)/sqrt(d))
@@ -139,6 +140,16 @@ vc_status vc_cluster_cost(const void* V, const float* centroids, const int32_t* 
  * Arithmetic: block and channel scales are fl32(amax/448) with codes
  * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
  * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).
+ * VC_F_MXFP4 (the 4-bit residual of the pages' workstation path, as OCP MXFP4): the
+ * residual R gets E2M1 codes with one E8M0 scale per group of 32 keys of a channel, the
+ * scale being the smallest 2^e with max|R| <= 6 * 2^e (no clipping; 2^0 for an all-zero
+ * group), codes the nearest E2M1 value of R / 2^e (ties to even mantissa, +0 for zero).
+ * Group g of half q of a block holds keys 64q + 16g + {0..15} and 64q + 32 + 16g + {0..15}
+ * (the 32 elements one lane of the block-scaled MFMA holds). Vq then holds, per block j
+ * at byte offset 128 d j of the head: codes [c][64 bytes] -- key t of half q = t>>6 is
+ * nibble p = 16((t&63)>>5) + (t&15) of group g = (t>>4)&1, at byte 32q + 16g + p/2,
+ * low nibble first -- followed by scales [c][4] (E8M0 bytes, index 2q + g) at byte 64 d;
+ * the rest of the block's 128 d bytes is unused. sV = 1 and mu_scaled = mu.
  * VC_F_HADAMARD (the rotation that the pages' fused preprocessing carries): every Q row
  * and every K~' row is multiplied by the unnormalised Sylvester Hadamard matrix H_d
  * before its block is quantised, evaluated as the fast Walsh-Hadamard transform in

@@ -62,3 +62,21 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def mx_unpack(Vq: np.ndarray):
+    """MXFP4 layout of vc_quantize's Vq ([B,H,nb,d,128] bytes) -> (codes [B,H,N,d], one E2M1
+    code per byte in permuted token order; scales [B,H,nb,d,4] E8M0 bytes)."""
+    B, H, nb, d, T = Vq.shape
+    flat = Vq.reshape(B, H, nb, d * T)
+    codes_b = flat[..., :64 * d].reshape(B, H, nb, d, 64)
+    scales = np.ascontiguousarray(flat[..., 64 * d:68 * d].reshape(B, H, nb, d, 4))
+    b = np.arange(64)
+    q, g, pb = b // 32, (b % 32) // 16, b % 16
+    out = np.empty((B, H, nb, 128, d), np.uint8)
+    for half in (0, 1):                      # low nibble = even p
+        p = 2 * pb + half
+        t = 64 * q + 32 * (p // 16) + 16 * g + (p % 16)
+        nib = (codes_b >> (4 * half)) & 15    # [B,H,nb,d,64]
+        out[:, :, :, t, :] = nib.transpose(0, 1, 2, 4, 3)
+    return out.reshape(B, H, nb * 128, d), scales

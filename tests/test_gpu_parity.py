@@ -18,7 +18,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 vc = pytest.importorskip("bit_attention_video_online_amd")
-from tests.gpu_util import bf16_bits, gpu_quantize, mu_pack_expected, rel_l2, to_dev, to_dev_bf16, vq_rowmajor  # noqa: E402
+from tests.gpu_util import bf16_bits, gpu_quantize, mu_pack_expected, mx_unpack, rel_l2, to_dev, to_dev_bf16, vq_rowmajor  # noqa: E402
 
 BETA = oracle.BETA_E4M3
 BETA2 = oracle.BETA_E5M2
@@ -138,6 +138,27 @@ def test_attention_after_rope_hadamard_matches_emulation(e5m2):
     assert err <= (TOL_E5M2 if e5m2 else TOL), err
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("vsmooth", [False, True])
+def test_quantize_mxfp4_bitexact(d, vsmooth):
+    """4-bit (MXFP4) value residual: codes, group scales and the rest of the quantiser
+    outputs bit-exact against the oracle; ragged 3-block heads with permuted keys."""
+    B, H, N = 1, 2, 384
+    w = synth.gen("wan", seed=14, B=B, H=H, N=N, d=d)
+    perm = np.stack([np.stack([synth.rand_perm(N, 15, b, h) for h in range(H)]) for b in range(B)])
+    flags = vc.VC_F_KSMOOTH | (vc.VC_F_VSMOOTH if vsmooth else 0) | vc.VC_F_MXFP4
+    out = gpu_quantize(w["Q"], w["K"], w["V"], perm, flags)
+    g = {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
+    codes, scales = mx_unpack(g["Vq"])
+    for h in range(H):
+        q_or = oracle.quantize(w["Q"][0, h], w["K"][0, h], w["V"][0, h], perm[0, h], int(flags))
+        assert np.array_equal(codes[0, h], q_or["Vq"]), h
+        assert np.array_equal(scales[0, h], q_or["Vs"]), h
+        for k in ("Qq", "sQ", "Kq", "sK", "sV", "mu_scaled"):
+            assert np.array_equal(g[k][0, h], q_or[k]), (h, k)
+        assert np.array_equal(g["mu_pack"][0, h], mu_pack_expected(q_or["mu_scaled"]))
+
+
 def test_quantize_exact_construction():
     from tests._construct import representable_head
     hd = representable_head(N=512, d=128, seed=3)
@@ -225,9 +246,10 @@ def test_cluster_deterministic():
 
 
 # ------------------------------------------------------------------ attention
-def _gpu_attention(out, N, d, B, H, expcast, restore, dump_block=None, e5m2=False):
+def _gpu_attention(out, N, d, B, H, expcast, restore, dump_block=None, e5m2=False, mx=False):
     O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
     flags = (vc.VC_F_EXPCAST | (vc.VC_F_E5M2 if e5m2 else 0)) if expcast else 0
+    flags |= vc.VC_F_MXFP4 if mx else 0
     beta = BETA2 if e5m2 else BETA
     if dump_block is None:
         vc.vc_attention(out, O, beta=beta, flags=flags, restore_mean=restore)
@@ -281,6 +303,27 @@ def test_attention_matches_emulation_shapes(d, N, e5m2):
             err = rel_l2(_o_f64(O[b, h]), O_or)
             print("[shapes N=%d d=%d %s] (%d,%d) rel-L2 vs emulation %.3e" % (N, d, "e5m2" if e5m2 else "e4m3", b, h, err))
             assert err <= (TOL_E5M2 if e5m2 else TOL), (b, h, err)
+
+
+@pytest.mark.parametrize("d,N", [(128, 1024), (64, 640)])
+@pytest.mark.parametrize("path", ["vsmooth", "vc", "plain"])
+def test_attention_mxfp4_matches_emulation(path, d, N):
+    """4-bit (MXFP4) value residual on the block-scaled MFMA: exp-then-cast with V-Smooth
+    (the pages' 4-bit configuration), ExpCast with V-Smooth, and plain exp-then-cast."""
+    expcast = path == "vc"
+    vs = path != "plain"
+    w = synth.gen("wan", seed=16, B=1, H=1, N=N, d=d)
+    perm = synth.rand_perm(N, 3) if vs else None
+    flags = vc.VC_F_KSMOOTH | (vc.VC_F_VSMOOTH if vs else 0) | vc.VC_F_MXFP4
+    out = gpu_quantize(w["Q"], w["K"], w["V"], None if perm is None else perm[None, None], flags)
+    O, _ = _gpu_attention(out, N, d, 1, 1, expcast, vs, mx=True)
+    q_or = oracle.quantize(w["Q"][0, 0], w["K"][0, 0], w["V"][0, 0], perm, int(flags))
+    rows = np.arange(N, dtype=np.int32)
+    O_or = oracle.attention_emul(q_or, rows, beta=BETA,
+                                 mode=oracle.MODE_EXPCAST if expcast else oracle.MODE_EXP_THEN_CAST, restore_mean=vs)
+    err = rel_l2(_o_f64(O[0, 0]), O_or)
+    print("[mxfp4 %s d=%d] rel-L2 vs emulation %.3e" % (path, d, err))
+    assert err <= TOL, err
 
 
 def _score_error_band(q_or, rows, blk):
