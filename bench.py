@@ -322,11 +322,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
-    ap.add_argument("--attn-mode", default="vc", choices=["vc", "vc_e5m2", "expcast", "exp"],
+    ap.add_argument("--attn-mode", default="vc", choices=["vc", "vc_e5m2", "expcast", "exp", "vs_mx4", "vc_mx4"],
                     help="with --attention-only: vc = V-Smooth + ExpCast (the path); vc_e5m2 = the same with "
                          "E5M2 probability bytes; expcast = ExpCast bytes without mean restoration; exp = "
                          "exp-then-cast probabilities without mean restoration (instruction-count comparison of "
-                         "the probability stage)")
+                         "the probability stage); vs_mx4 / vc_mx4 = the 4-bit (MXFP4) value residual with V-Smooth "
+                         "and exp-then-cast / ExpCast probabilities")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift"],
                     help="schedule workload: fixed clustering steps 0-4, or drift-triggered refresh")
@@ -400,9 +401,11 @@ def main():
 
     mode = args.attn_mode if args.attention_only else "vc"
     attn_flags = {"vc": vc.VC_F_EXPCAST, "vc_e5m2": vc.VC_F_EXPCAST | vc.VC_F_E5M2, "expcast": vc.VC_F_EXPCAST,
-                  "exp": 0}[mode]
+                  "exp": 0, "vs_mx4": vc.VC_F_MXFP4, "vc_mx4": vc.VC_F_EXPCAST | vc.VC_F_MXFP4}[mode]
     attn_beta = BETA_E5M2 if mode == "vc_e5m2" else BETA
-    attn_restore = mode in ("vc", "vc_e5m2")
+    attn_restore = mode in ("vc", "vc_e5m2", "vs_mx4", "vc_mx4")
+    if mode in ("vs_mx4", "vc_mx4"):
+        flags_q |= vc.VC_F_MXFP4
 
     def step(record):
         if args.attention_only:
@@ -474,9 +477,13 @@ def main():
     if args.attention_only:
         res["config"]["workload"] += " (attention kernel only%s)" % {
             "vc": "", "vc_e5m2": ", E5M2 ExpCast bytes (beta -0.17)", "expcast": ", ExpCast without mean restoration",
-            "exp": ", exp-then-cast probabilities, no mean restoration"}[mode]
+            "exp": ", exp-then-cast probabilities, no mean restoration",
+            "vs_mx4": ", 4-bit MXFP4 value residual with V-Smooth, exp-then-cast probabilities",
+            "vc_mx4": ", 4-bit MXFP4 value residual with V-Smooth, ExpCast probabilities"}[mode]
         res["roofline"]["kernel"] = {"vc": "attn_fwd<128,ExpCast,restore>", "vc_e5m2": "attn_fwd<128,ExpCast-E5M2,restore>",
-                                     "expcast": "attn_fwd<128,ExpCast>", "exp": "attn_fwd<128,exp-then-cast>"}[mode]
+                                     "expcast": "attn_fwd<128,ExpCast>", "exp": "attn_fwd<128,exp-then-cast>",
+                                     "vs_mx4": "attn_fwd<128,exp-then-cast,restore,MXFP4>",
+                                     "vc_mx4": "attn_fwd<128,ExpCast,restore,MXFP4>"}[mode]
     if not args.no_cpu_baseline and not args.attention_only:
         import oracle
         log("[bench] timing the CPU oracle on a bounded sample ...")

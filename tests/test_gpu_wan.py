@@ -203,3 +203,40 @@ def test_wan_rope_hadamard_sampled_heads(run, oracle_heads):
             err_ex[had].append(rel_l2(got, O_ex))
     print("[wan rope] rMSE vs exact on the RoPE'd inputs: without rotation %.4f, with Hadamard %.4f"
           % (np.mean(err_ex[False]), np.mean(err_ex[True])), flush=True)
+
+
+def test_wan_mxfp4_sampled_rows(run, oracle_heads):
+    """The 4-bit (MXFP4) value residual at full size with the warm-started permutation:
+    exp-then-cast + V-Smooth (the pages' 4-bit configuration) and ExpCast + V-Smooth, sampled
+    rows of two heads within 2e-3 of the emulation; group scales and codes of the sampled
+    heads bit-exact; error against exact attention printed beside the 8-bit path."""
+    from tests.gpu_util import mx_unpack
+    w = run["w"]
+    B, H, N, d = w["Q"].shape
+    Q, K, V = (to_dev_bf16(w[k]) for k in ("Q", "K", "V"))
+    perm = torch.from_numpy(run["perm"]).cuda()
+    flags = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH | vc.VC_F_MXFP4
+    q = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(Q, K, V, perm, flags, q)
+    O = {}
+    for name, af in (("exp", vc.VC_F_MXFP4), ("vc", vc.VC_F_EXPCAST | vc.VC_F_MXFP4)):
+        O[name] = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+        vc.vc_attention(q, O[name], beta=BETA, flags=af)
+    torch.cuda.synchronize()
+    codes, scales = mx_unpack(q["Vq"].cpu().numpy())
+    O = {k: bf16_bits(v) for k, v in O.items()}
+    del Q, K, V, q
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(79)
+    err_ex = {"exp": [], "vc": []}
+    for h in HEADS:
+        o = oracle.quantize(w["Q"][0, h], w["K"][0, h], w["V"][0, h], oracle_heads[h]["perm"], int(flags))
+        assert np.array_equal(codes[0, h], o["Vq"]) and np.array_equal(scales[0, h], o["Vs"]), h
+        rows = np.sort(rng.choice(N, 64, replace=False)).astype(np.int32)
+        O_ex = oracle.attention_exact(w["Q"][0, h], w["K"][0, h], w["V"][0, h], rows)
+        for name, mode in (("exp", oracle.MODE_EXP_THEN_CAST), ("vc", oracle.MODE_EXPCAST)):
+            got = synth.bf16_to_f32(O[name][0, h][rows]).astype(np.float64)
+            assert rel_l2(got, oracle.attention_emul(o, rows, beta=BETA, mode=mode)) <= 2e-3, (name, h)
+            err_ex[name].append(rel_l2(got, O_ex))
+    print("[wan mxfp4] rMSE vs exact: exp-then-cast + V-Smooth %.4f, ExpCast + V-Smooth %.4f"
+          % (np.mean(err_ex["exp"]), np.mean(err_ex["vc"])), flush=True)
