@@ -8,7 +8,7 @@
 // of the exact member mean; empty clusters keep their centroid); pi is stable.
 //
 // Kernels, per iteration:
-//   cl_prep    chat = bf16(C) (as binary32), |chat|^2
+//   cl_prep    chat = bf16(C) (bf16 bits), |chat|^2
 //   cl_assign_mfma  distances |c|^2 - 2 v.c with the dot products on bf16 MFMA, a
 //              rigorous per-distance error bound, and a binary64 re-rank of every token
 //              whose best candidate is not separated from the rest by the bounds (exact
@@ -29,12 +29,14 @@ __global__ void cl_cold(const uint16_t* __restrict__ V, float* __restrict__ C, i
   C[((size_t)bh * K + k) * D + c] = bf16_to_f32(V[((size_t)bh * N + t) * D + c]);
 }
 
-__global__ void cl_prep(const float* __restrict__ C, float* __restrict__ chat, float* __restrict__ cnorm, int K, int D) {
+__global__ void cl_prep(const float* __restrict__ C, uint16_t* __restrict__ chat, float* __restrict__ cnorm, int K,
+                        int D) {
   __shared__ double part[128];
   const int k = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
   const size_t o = ((size_t)bh * K + k) * D + c;
-  const float h = bf16_to_f32(f32_to_bf16(C[o]));
-  chat[o] = h;
+  const uint16_t hb = f32_to_bf16(C[o]);
+  const float h = bf16_to_f32(hb);
+  chat[o] = hb;
   part[c] = (double)h * (double)h;  // exact square of a bf16 value
   __syncthreads();
   if (c == 0) {
@@ -44,12 +46,28 @@ __global__ void cl_prep(const float* __restrict__ C, float* __restrict__ chat, f
   }
 }
 
-// per-token record of one lane group: best distance' d1, its bounds lo1 = d1 - e1 and
-// hi1 = d1 + e1, L = min over the group's other centroids of d_k - e_k, and the index
+// per-token record of one lane group: best distance' d1, the smallest distance' d2 of its
+// other centroids, and the best index
 struct Best {
-  float d1, lo1, hi1, L;
+  float d1, d2;
   int k;
 };
+
+// Rigorous lower bound of d_k - e_k over every centroid whose computed distance' is >= x
+// (x = d2): with |c_k| <= |v| + sqrt(D_k) and D_k <= d_k + e_k + |v|^2, the bound
+// e_k <= F(e) = 2(2 gam |v| c(e) + u (c(e)^2 + |x|)), c(e) = |v| + sqrt(x + e + |v|^2),
+// is increasing in x, so x - E(x) is increasing too and bounds every other centroid. E is
+// taken from above: two steps of F from a crude upper starting value, then doubled.
+__device__ __forceinline__ double others_lower_bound(double x, double vn, double gam, double u) {
+  auto F = [&](double e) {
+    const double c = vn + sqrt(fmax(x + e + vn * vn, 0.0));
+    return 2.0 * (2.0 * gam * vn * c + u * (c * c + fabs(x)));
+  };
+  const double e0 = 0.5 * (fabs(x) + vn * vn) + 1.0;
+  const double e1 = F(e0);
+  if (!(e1 <= e0)) return -__builtin_inf();  // the crude start was not above the fixed point
+  return x - 2.0 * F(e1);
+}
 
 // ---------------------------------------------------------------------------
 // Assignment on the matrix cores. S^T = chat V^T with v_mfma_f32_16x16x32_bf16: the
@@ -57,39 +75,44 @@ struct Best {
 // measured at <= 2^-21.3 sum|v_c chat_c| on adversarial wide-range data, far inside
 // the binary32 recursive-summation bound gamma_d sum|v_c chat_c| used below (doubled),
 // so the same certainty test and binary64 re-rank apply.
-// Work-group: 4 waves x 32 tokens (two 16-token groups). Centroid chunks of 64 rows of
+// Work-group: 4 waves x 64 tokens (four 16-token groups), so every staged centroid chunk
+// serves 256 tokens. Centroid chunks of 64 rows of
 // bf16 are staged in LDS with a padded row stride (conflict-free 16-byte fragment
 // reads). Per MFMA the lane holds one token (lane % 16) and four centroids
 // (4 * (lane / 16) + i); the four lane groups of a token are merged at the end.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+constexpr int kAssignTokens = 256;  // tokens per assignment work-group
+
 template <int D>
-__global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict__ V, const float* __restrict__ chat,
+__global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict__ V, const uint16_t* __restrict__ chat,
                                                       const float* __restrict__ cnorm, int N, int K,
                                                       int32_t* __restrict__ labels) {
   constexpr int KS = D / 32;            // MFMA k-steps over the feature dimension
   constexpr int ROWB = 2 * D + 16;      // padded LDS row stride (bytes)
   constexpr int CCH = 64;               // centroids per chunk
+  constexpr int NG = kAssignTokens / 64; // 16-token groups per wave
   __shared__ __attribute__((aligned(16))) uint8_t Cs[CCH * ROWB];
-  __shared__ float cn_s[CCH], ea_s[CCH], eb_s[CCH];
-  __shared__ Best rec[128][4];
-  __shared__ int unsure[128];
+  __shared__ float cn_s[CCH];
+  __shared__ float vn_s[kAssignTokens];
+  __shared__ Best rec[kAssignTokens][4];
+  __shared__ int unsure[kAssignTokens];
   __shared__ int n_unsure;
   __shared__ double red_d[256];
   __shared__ int red_k[256];
 
-  const int bh = blockIdx.y, t0 = blockIdx.x * 128;
+  const int bh = blockIdx.y, t0 = blockIdx.x * kAssignTokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, lg = lane >> 4;
   const uint16_t* Vh = V + (size_t)bh * N * D;
-  const float* Ch = chat + (size_t)bh * K * D;
+  const uint16_t* Ch = chat + (size_t)bh * K * D;
   const float* Nh = cnorm + (size_t)bh * K;
 
   // token fragments (B operand): token row, features [32 ks + 8 lg, +8)
-  bf16x8 vb[2][KS];
-  float vn[2];
-  for (int g = 0; g < 2; g++) {
-    const int t = t0 + wave * 32 + g * 16 + r16;
+  bf16x8 vb[NG][KS];
+  float vn[NG];
+  for (int g = 0; g < NG; g++) {
+    const int t = min(t0 + wave * 16 * NG + g * 16 + r16, N - 1);  // tokens past N repeat the last
     float s = 0.0f;
     for (int ks = 0; ks < KS; ks++) {
       uint4 raw = *reinterpret_cast<const uint4*>(Vh + (size_t)t * D + 32 * ks + 8 * lg);
@@ -107,68 +130,52 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     s = __uint_as_float(b[0]) + __uint_as_float(b[1]);
     vn[g] = sqrtf(s) * 1.0001f;  // upper bound of |v|
+    if (lg == 0) vn_s[wave * 16 * NG + g * 16 + r16] = vn[g];
   }
   const float u = 5.9604645e-8f;  // 2^-24
   const float gam = (float)D * u / (1.0f - (float)D * u);
   // Every computed distance' d_k is within e_k = 2(2 gamma |v||c_k| + u(|c_k|^2 + |d_k|))
   // of its exact value (bf16 products are exact; the accumulation error is inside the
-  // binary32 bound). Per token and lane group the loop tracks, branch-free, the best d1 with
-  // its index, lo1 = d1 - e1 and hi1 = d1 + e1, and L = min over the other centroids of
-  // d_k - e_k; L > hi1 proves the best index exact. A lane group meets its centroids in
-  // increasing index order, so only a strictly smaller distance replaces the best.
-  float d1[2], lo1[2], hi1[2], L[2];
-  int kbest[2];
-  for (int g = 0; g < 2; g++) {
-    d1[g] = __builtin_inff(); lo1[g] = __builtin_inff(); hi1[g] = __builtin_inff(); L[g] = __builtin_inff();
+  // binary32 bound). Per token and lane group the loop tracks, branch-free, only the best
+  // d1 with its index and the smallest distance' d2 of the other centroids; at the end
+  // others_lower_bound(d2) > d1 + e1 proves the best index exact. A lane group meets its
+  // centroids in increasing index order, so only a strictly smaller distance replaces the
+  // best (a tie leaves d2 = d1 and goes to the exact re-rank).
+  float d1[NG], d2[NG];
+  int kbest[NG];
+  for (int g = 0; g < NG; g++) {
+    d1[g] = __builtin_inff(); d2[g] = __builtin_inff();
     kbest[g] = 0x7fffffff;
   }
-  const float twou = 2.0f * u;
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int k0 = 0; k0 < K; k0 += CCH) {
     __syncthreads();
-    // stage chat rows [k0, k0+64) as bf16 (exact: chat holds bf16 values)
+    // stage chat rows [k0, k0+64) (bf16)
     for (int i = tid; i < CCH * (D / 8); i += 256) {
       const int k = i / (D / 8), c8 = (i % (D / 8)) * 8;
       uint4 w = make_uint4(0, 0, 0, 0);
-      if (k0 + k < K) {
-        const float4* src = reinterpret_cast<const float4*>(Ch + (size_t)(k0 + k) * D + c8);
-        float4 x = src[0], y = src[1];
-        w.x = (__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xffff0000u);
-        w.y = (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xffff0000u);
-        w.z = (__float_as_uint(y.x) >> 16) | (__float_as_uint(y.y) & 0xffff0000u);
-        w.w = (__float_as_uint(y.z) >> 16) | (__float_as_uint(y.w) & 0xffff0000u);
-      }
+      if (k0 + k < K) w = *reinterpret_cast<const uint4*>(Ch + (size_t)(k0 + k) * D + c8);
       *reinterpret_cast<uint4*>(Cs + k * ROWB + 2 * c8) = w;
     }
-    // per-centroid bound terms e_k = A_k |v| + B_k + 2u |d_k|; padding past K gets zero rows
-    // and a huge finite norm, so its distance never wins and no bound overflows
-    if (tid < CCH) {
-      const bool ok = k0 + tid < K;
-      const float cnk = ok ? Nh[k0 + tid] : 3.0e38f;
-      cn_s[tid] = cnk;
-      ea_s[tid] = ok ? 4.0f * gam * (sqrtf(cnk) * 1.0001f) : 0.0f;
-      eb_s[tid] = twou * cnk + 1e-30f;
-    }
+    // padding past K gets zero rows and a huge finite norm, so its distance never wins
+    if (tid < CCH) cn_s[tid] = (k0 + tid < K) ? Nh[k0 + tid] : 3.0e38f;
     __syncthreads();
     for (int cb = 0; cb < CCH / 16; cb++) {
-      v4f acc[2] = {zero4, zero4};
+      v4f acc[NG];
+      for (int g = 0; g < NG; g++) acc[g] = zero4;
       for (int ks = 0; ks < KS; ks++) {
         bf16x8 a;
         memcpy(&a, Cs + (16 * cb + r16) * ROWB + 2 * (32 * ks + 8 * lg), 16);
-        for (int g = 0; g < 2; g++) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[g][ks], acc[g], 0, 0, 0);
+        for (int g = 0; g < NG; g++) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vb[g][ks], acc[g], 0, 0, 0);
       }
       for (int i = 0; i < 4; i++) {
         const int kl = 16 * cb + 4 * lg + i;
-        const float cnk = cn_s[kl], ea = ea_s[kl], eb = eb_s[kl];
-        for (int g = 0; g < 2; g++) {
+        const float cnk = cn_s[kl];
+        for (int g = 0; g < NG; g++) {
           const float dd = __builtin_fmaf(-2.0f, acc[g][i], cnk);  // exact scaling, one rounding
-          const float e = __builtin_fmaf(twou, fabsf(dd), __builtin_fmaf(ea, vn[g], eb));
-          const float lo = dd - e;
           const bool better = dd < d1[g];
-          L[g] = fminf(L[g], better ? lo1[g] : lo);
-          lo1[g] = better ? lo : lo1[g];
-          hi1[g] = better ? dd + e : hi1[g];
+          d2[g] = fminf(d2[g], better ? d1[g] : dd);
           d1[g] = better ? dd : d1[g];
           kbest[g] = better ? k0 + kl : kbest[g];
         }
@@ -177,20 +184,27 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   }
   // merge the four lane groups of each token through LDS
   if (tid == 0) n_unsure = 0;
-  for (int g = 0; g < 2; g++) rec[wave * 32 + g * 16 + r16][lg] = Best{d1[g], lo1[g], hi1[g], L[g], kbest[g]};
+  for (int g = 0; g < NG; g++) rec[wave * 16 * NG + g * 16 + r16][lg] = Best{d1[g], d2[g], kbest[g]};
   __syncthreads();
-  if (tid < 128) {
+  if (tid < kAssignTokens && t0 + tid < N) {
     Best a = rec[tid][0];
     for (int x = 1; x < 4; x++) {
       const Best& o = rec[tid][x];
       if (o.d1 < a.d1 || (o.d1 == a.d1 && o.k < a.k)) {
-        a.L = fminf(fminf(a.L, o.L), a.lo1);
-        a.d1 = o.d1; a.lo1 = o.lo1; a.hi1 = o.hi1; a.k = o.k;
+        a.d2 = fminf(fminf(a.d2, o.d2), a.d1);
+        a.d1 = o.d1; a.k = o.k;
       } else {
-        a.L = fminf(fminf(a.L, o.L), o.lo1);
+        a.d2 = fminf(fminf(a.d2, o.d2), o.d1);
       }
     }
-    if (a.L > a.hi1) {
+    bool certain = false;
+    if ((unsigned)a.k < (unsigned)K) {
+      const double vn = vn_s[tid], dg = (double)gam, du = (double)u;
+      const double cnk = Nh[a.k], ck = sqrt(cnk) * 1.0001;
+      const double e1 = 2.0 * (2.0 * dg * vn * ck + du * (cnk + fabs((double)a.d1))) * (1.0 + 1e-6);
+      certain = !(a.d2 < __builtin_inff()) || others_lower_bound((double)a.d2, vn, dg, du) > (double)a.d1 + e1;
+    }
+    if (certain) {
       labels[(size_t)bh * N + t0 + tid] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
     } else {
       unsure[atomicAdd(&n_unsure, 1)] = tid;
@@ -205,10 +219,10 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
     double best = __builtin_inf();
     int bk = 0x7fffffff;
     for (int k = tid; k < K; k += 256) {
-      const float* ck = Ch + (size_t)k * D;
+      const uint16_t* ck = Ch + (size_t)k * D;
       double s = 0.0;
       for (int c = 0; c < D; c++) {
-        double df = (double)bf16_to_f32(vt[c]) - (double)ck[c];
+        double df = (double)bf16_to_f32(vt[c]) - (double)bf16_to_f32(ck[c]);
         s = fma(df, df, s);
       }
       if (s < best) { best = s; bk = k; }
@@ -428,7 +442,7 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
   const uint16_t* V = (const uint16_t*)Vv;
   const int BH = B * H, nch = (N + kChunk - 1) / kChunk;
   char* w = (char*)ws;
-  float* chat = (float*)w; w += (size_t)BH * K * d * sizeof(float);
+  uint16_t* chat = (uint16_t*)w; w += (size_t)BH * K * d * sizeof(float);
   float* cnorm = (float*)w; w += (size_t)BH * K * sizeof(float);
   int32_t* counts = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
   int32_t* offs = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
@@ -436,7 +450,7 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
   int32_t* csize = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
   int32_t* ctotal = (int32_t*)w;
   if (cold) cl_cold<<<dim3(K, BH), d, 0, st>>>(V, C, N, K, d);
-  const dim3 gmf(N / 128, BH), gch(nch, BH), gk(K, BH);
+  const dim3 gmf((N + kAssignTokens - 1) / kAssignTokens, BH), gch(nch, BH), gk(K, BH);
   for (int it = 0; it < iters; it++) {
     cl_prep<<<gk, d, 0, st>>>(C, chat, cnorm, K, d);
     if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
