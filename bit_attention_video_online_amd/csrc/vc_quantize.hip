@@ -262,16 +262,18 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
 }
 
 // Per (b,h): kbar = fl32(exact mean) of the keys, residual scale sV = fl32(amax/448) and
-// 448/amax. kQThreads threads: channel c = t % D, group t / D takes every G-th block.
+// 448/amax. Work-group (bh, channel slice of 16): channel c = slice*16 + t % 16, group
+// t / 16 takes every 16th block (two chains); the exact sums make the order immaterial.
+constexpr int kRedCh = 16;
 template <int D>
 __global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags, const double* __restrict__ ksum,
                                                           const float* __restrict__ vamax, float* __restrict__ kbar,
                                                           float* __restrict__ sV, float* __restrict__ vinv) {
-  constexpr int G = kQThreads / D;
+  constexpr int G = kQThreads / kRedCh;
   __shared__ double ps[kQThreads];
   __shared__ float pm[kQThreads];
   const int nb = N / kBlock;
-  const int bh = blockIdx.x, c = threadIdx.x % D, g = threadIdx.x / D;
+  const int bh = blockIdx.x, c = blockIdx.y * kRedCh + threadIdx.x % kRedCh, g = threadIdx.x / kRedCh;
   double t0 = 0.0, t1 = 0.0;
   float a0 = 0.0f, a1 = 0.0f;
   int jb = g;
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags,
   if (g == 0) {
     double t = 0.0;
     float a = 0.0f;
-    for (int k = 0; k < G; k++) { t += ps[k * D + c]; a = fmaxf(a, pm[k * D + c]); }
+    for (int k = 0; k < G; k++) { t += ps[k * kRedCh + threadIdx.x]; a = fmaxf(a, pm[k * kRedCh + threadIdx.x]); }
     kbar[(size_t)bh * D + c] = (flags & 1u) ? div_to_f32(t, (double)N) : 0.0f;
     float s, inv;
     if (flags & kFlagMxfp4) { s = 1.0f; inv = 0.0f; }  // the group scales carry the range
@@ -445,7 +447,7 @@ template <int D, bool ROPE, bool HAD, bool MX>
 static void launch_quant(const QArgs& a, dim3 grid, int BH, hipStream_t st) {
   quant_stats<D, ROPE, HAD><<<grid, kQThreads, 0, st>>>(a.Q, a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.cL, a.Qq,
                                                          a.sQ, a.mu, a.ksum, a.vamax);
-  quant_reduce<D><<<BH, kQThreads, 0, st>>>(a.N, a.flags, a.ksum, a.vamax, a.kbar, a.sV, a.vinv);
+  quant_reduce<D><<<dim3(BH, D / kRedCh), kQThreads, 0, st>>>(a.N, a.flags, a.ksum, a.vamax, a.kbar, a.sV, a.vinv);
   quant_apply<D, ROPE, HAD, MX><<<grid, kQThreads, 0, st>>>(a.K, a.V, a.perm, a.rc, a.rs, a.N, a.flags, a.kbar, a.sV,
                                                          a.vinv, a.mu, a.Kq, a.sK, a.Vq, a.mu_scaled, a.mu_pack);
 }
