@@ -112,6 +112,30 @@ def device_info():
     return info
 
 
+def measure_mfma_peak(grid=2048, iters=20000, reps=3):
+    """Sustained rate of the attention kernel's FP8 matrix-core instruction (32x32x64, 131072
+    FLOPs per wave instruction) with register operands and no memory traffic: best of `reps`
+    timed launches each for fixed and pseudo-random operand bits (TFLOP/s)."""
+    import torch
+    import bit_attention_video_online_amd as vc
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    flops = grid * 4.0 * iters * 4 * 131072
+    res = {}
+    for name, rnd in (("fixed_operands", 0), ("random_operands", 1)):
+        vc.vc_debug_mfma_peak(grid, 200, rnd, out)
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            vc.vc_debug_mfma_peak(grid, iters, rnd, out)
+            e1.record()
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3
+            best = t if best is None else min(best, t)
+        res[name] = round(flops / best / 1e12, 1)
+    return res
+
+
 def stage_rates(B, H, N, d, Kc, iters, avg):
     """Algorithmic bytes (and k-means FLOPs) per stage launch and the rates they give.
 
@@ -445,6 +469,9 @@ def main():
     avg = {k: (sum(a.elapsed_time(b) for a, b in v) / len(v) if v else None) for k, v in ev.items()}
     log("[bench] timed %d steps: %.3f ms/step; stage ms %s" % (args.steps, ms_step, avg))
 
+    mfma = measure_mfma_peak()
+    log("[bench] sustained FP8 matrix-core rate (TFLOP/s): %s" % mfma)
+
     flops = 4.0 * B * H * N * N * d
     t_att = avg["attention"] / 1e3
     att_tflops = flops / t_att / 1e12
@@ -464,6 +491,8 @@ def main():
         "stage_rates": stage_rates(B, H, N, d, Kc, 2, avg),
         "device": device_info(),
         "attention_pct_fp8_peak": round(100.0 * att_tflops / FP8_PEAK_TFLOPS, 2),
+        "fp8_mfma_sustained_tflops": mfma,
+        "attention_pct_fp8_sustained": round(100.0 * att_tflops / mfma["random_operands"], 2),
         "roofline": {"bound": "mfma", "achieved": round(att_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / FP8_PEAK_TFLOPS, 4), "traffic": profiled_traffic(),
                      "traffic_unit": "GB per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.vc_attention_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, U, P, I, P, P]
         L.vc_debug_expcast.restype = I
         L.vc_debug_expcast.argtypes = [P, P, P, P, S, P]
+        L.vc_debug_mfma_peak.restype = I
+        L.vc_debug_mfma_peak.argtypes = [I, I, I, P, P]
         _lib = L
     return _lib
 
@@ -224,6 +226,13 @@ def vc_attention_dump(q, O, dump_block, codes, beta=-0.35, flags=VC_F_EXPCAST, r
                                  int(dump_block), _ptr(codes), _stream(stream))
     _check(st)
     return O, codes
+
+
+def vc_debug_mfma_peak(grid, iters, random_bits, out, stream=None):
+    """Sustained FP8 MFMA measurement kernel; out: float32 [grid * 256] on the device."""
+    _need(out, torch.float32, (grid * 256,), "out")
+    _check(lib().vc_debug_mfma_peak(int(grid), int(iters), int(bool(random_bits)), _ptr(out), _stream(stream)))
+    return out
 
 
 def vc_debug_expcast(acc, scale8, bias, codes, stream=None):

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvc.so")
-SOURCES = ["vc_api.hip", "vc_quantize.hip", "vc_attention.hip", "vc_cluster.hip"]
+SOURCES = ["vc_api.hip", "vc_quantize.hip", "vc_attention.hip", "vc_cluster.hip", "vc_peak.hip"]
 # Per-file extra flags. The attention kernel takes finite inputs by contract: without
 # NaN semantics (and with the shader's IEEE mode off) float max needs no operand
 # canonicalisation, which removes one VALU op per score element.

@@ -14,6 +14,7 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
                                   void* mu_pack, void* ws, hipStream_t st);
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d);
 extern "C" size_t vc_cluster_cost_ws_bytes(int B, int H, int N);
+extern "C" int vc_launch_mfma_peak(int grid, int iters, int random_bits, float* out, hipStream_t st);
 extern "C" int vc_launch_cluster_cost(const void* V, const float* C, const int32_t* labels, int B, int H, int N, int d,
                                       int K, double* cost, void* ws, hipStream_t st);
 extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uint8_t* Kq, const float* sK,
@@ -230,6 +231,13 @@ extern "C" vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const
   if (N >= 128 && (dump_block < 0 || dump_block >= N / 128)) return VC_E_PARAM;
   return attention_common(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, block, beta, flags, O, dump_block, codes,
                           stream);
+}
+
+extern "C" vc_status vc_debug_mfma_peak(int grid, int iters, int random_bits, float* out, void* stream) {
+  if (!out) return VC_E_NULLPTR;
+  if (grid < 1 || iters < 1) return VC_E_PARAM;
+  if (vc_launch_mfma_peak(grid, iters, random_bits ? 1 : 0, out, (hipStream_t)stream) != 0) return VC_E_HIP;
+  return VC_OK;
 }
 
 extern "C" vc_status vc_debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes, size_t n,

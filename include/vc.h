@@ -230,6 +230,13 @@ vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const uint8_t* K
 vc_status vc_debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes,
                            size_t n, void* stream);
 
+/* Measurement support: `grid` work-groups of 4 waves each run `iters` rounds of four
+ * independent v_mfma_f32_32x32x64_f8f6f4 (the attention kernel's instruction) on register
+ * operands, fixed (random_bits = 0) or per-lane pseudo-random E4M3 patterns; the host times
+ * it to get the sustained FP8 matrix-core rate: FLOPs = grid * 4 * iters * 4 * 131072.
+ * out: float [grid * 256] scratch written by the kernel (device). */
+vc_status vc_debug_mfma_peak(int grid, int iters, int random_bits, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,9 @@ def test_workspace_queries(L):
 def test_debug_expcast_zero_length_is_ok(L):
     assert L.vc_debug_expcast(None, None, None, None, 0, None) == 0
     assert L.vc_debug_expcast(None, None, None, None, 5, None) == 1
+
+
+def test_debug_mfma_peak_rejects_bad_sizes(L):
+    assert L.vc_debug_mfma_peak(1, 1, 0, None, None) == 1
+    assert L.vc_debug_mfma_peak(0, 1, 0, ctypes.c_void_p(1 << 20), None) == 3
+    assert L.vc_debug_mfma_peak(1, 0, 0, ctypes.c_void_p(1 << 20), None) == 3

@@ -61,6 +61,17 @@ def test_expcast_function_bitexact():
     assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]
 
 
+def test_mfma_peak_kernel_counts_every_instruction():
+    # fixed operands: E4M3 1.0 (A) and 0.5 (B); per round each lane's 16 outputs of the four
+    # chains gain 64 * (0.5 + 0.5 + 1 + 0.25), so the lane sum is exactly 2304 per round
+    grid, iters = 300, 37
+    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    vc.vc_debug_mfma_peak(grid, iters, False, out)
+    assert torch.all(out == 2304.0 * iters)
+    vc.vc_debug_mfma_peak(grid, iters, True, out)
+    assert torch.isfinite(out).all()
+
+
 # ------------------------------------------------------------------ quantiser
 def _compare_quant(out, q_or, b, h, vsmooth):
     g = {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
