@@ -415,7 +415,12 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
             const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
             const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
             const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
-            w = e4m3x4_from_f32(p0, p1, p2, p3);
+            // both conversions as one opaque step right after the exponentials: written
+            // with the builtins, the compiler keeps all 32 scaled values of the half live
+            // until the PV operand is needed and then spills with the MXFP4 value path;
+            // op_sel[3] writes the high word and keeps the low one
+            asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2\n\tv_cvt_pk_fp8_f32 %0, %3, %4 op_sel:[0,0,1]"
+                         : "=&v"(w) : "v"(p0), "v"(p1), "v"(p2), "v"(p3));
             r += (p0 + p1) + (p2 + p3);
           }
           pf[kh][4 * (kb & 1) + qd] = (int)w;
