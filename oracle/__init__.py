@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         _lib.or_stable_argsort.argtypes = [P, I, I, P]
         _lib.or_kmeans_update.argtypes = [P, I, I, P, I, P]
         _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
+        _lib.or_kmeans_assign_biased.argtypes = [P, I, I, P, I, P, P]
+        _lib.or_kmeans_balanced.argtypes = [P, I, I, I, I, I, ctypes.c_float, P, P, P, P]
         _lib.or_kmeans_cost.restype = ctypes.c_double
         _lib.or_kmeans_cost.argtypes = [P, I, I, P, I, P]
         _lib.or_quantize.restype = I
@@ -218,6 +220,32 @@ def kmeans(V_bits: np.ndarray, K: int, iters: int, cold: bool, C: np.ndarray | N
     perm = np.empty(N, np.int32)
     lib().or_kmeans(_p(V), N, d, K, iters, 1 if cold else 0, _p(Cn), _p(labels), _p(perm))
     return labels, perm, Cn
+
+
+def kmeans_assign_biased(V_bits: np.ndarray, chat: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """argmin_k ||v - chat_k||^2 + bias_k per token, exact, ties to the lowest index."""
+    V = _c(V_bits, np.uint16)
+    C = _c(chat, np.float32)
+    N, d = V.shape
+    labels = np.empty(N, np.int32)
+    lib().or_kmeans_assign_biased(_p(V), N, d, _p(C), C.shape[0], _p(_c(bias, np.float32)), _p(labels))
+    return labels
+
+
+def kmeans_balanced(V_bits: np.ndarray, K: int, iters: int, cold: bool, lam: float, counts: np.ndarray,
+                    C: np.ndarray | None = None):
+    """Size-penalised k-means (distance + fl32(lam * n_k), n_k from the previous assignment).
+    Returns (labels, perm, centroids, counts after the last assignment)."""
+    V = _c(V_bits, np.uint16)
+    N, d = V.shape
+    Cn = np.zeros((K, d), np.float32) if C is None else np.array(C, dtype=np.float32, copy=True, order="C")
+    cnt = np.array(counts, dtype=np.int32, copy=True, order="C")
+    assert cnt.shape == (K,)
+    labels = np.empty(N, np.int32)
+    perm = np.empty(N, np.int32)
+    lib().or_kmeans_balanced(_p(V), N, d, K, iters, 1 if cold else 0, ctypes.c_float(lam), _p(cnt), _p(Cn),
+                             _p(labels), _p(perm))
+    return labels, perm, Cn, cnt
 
 
 # ---------------------------------------------------------------- quantiser

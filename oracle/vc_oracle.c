@@ -285,12 +285,13 @@ static void exact_sqdist(const float* v, const float* c, int d, xacc* out) {
 }
 
 /*
- * z = argmin_k ||v - chat_k||^2, exactly. A binary64 pass ranks the clusters;
- * any cluster within a relative 1e-12 of the binary64 minimum (which
- * comfortably covers the binary64 rounding of a 128-term sum of non-negative
- * terms) is re-ranked with the exact accumulator. Ties: lowest index.
+ * z = argmin_k ||v - chat_k||^2 (+ bias_k when bias is given), exactly. A binary64
+ * pass ranks the clusters; any cluster within a relative 1e-12 of the binary64
+ * minimum (which comfortably covers the binary64 rounding of a 128-term sum of
+ * non-negative terms) is re-ranked with the exact accumulator. Ties: lowest index.
  */
-static int32_t assign_one(const float* v, const float* chat, int K, int d, double* dist /* scratch K */) {
+static int32_t assign_one(const float* v, const float* chat, int K, int d, double* dist /* scratch K */,
+                          const float* bias /* [K] or NULL */) {
   double best = INFINITY;
   for (int k = 0; k < K; k++) {
     const float* c = chat + (int64_t)k * d;
@@ -302,7 +303,7 @@ static int32_t assign_one(const float* v, const float* chat, int K, int d, doubl
       s0 += a0 * a0; s1 += a1 * a1; s2 += a2 * a2; s3 += a3 * a3;
     }
     for (; j < d; j++) { double a = (double)v[j] - c[j]; s0 += a * a; }
-    dist[k] = (s0 + s1) + (s2 + s3);
+    dist[k] = (s0 + s1) + (s2 + s3) + (bias ? (double)bias[k] : 0.0);
     if (dist[k] < best) best = dist[k];
   }
   double thr = best + best * 1e-12;
@@ -314,13 +315,16 @@ static int32_t assign_one(const float* v, const float* chat, int K, int d, doubl
   for (int k = 0; k < K; k++) {
     if (dist[k] > thr) continue;
     exact_sqdist(v, chat + (int64_t)k * d, d, &cur);
+    if (bias) xa_add_double(&cur, (double)bias[k]);
     if (bk < 0 || xa_cmp(&cur, &bacc) < 0) { bk = k; bacc = cur; }
   }
   return bk;
 }
 
-/* labels for all tokens against bf16-valued centroids chat (as floats) */
-void or_kmeans_assign(const uint16_t* V, int N, int d, const float* chat, int K, int32_t* labels) {
+/* labels for all tokens against bf16-valued centroids chat (as floats), each
+   distance plus bias_k when bias is given */
+void or_kmeans_assign_biased(const uint16_t* V, int N, int d, const float* chat, int K, const float* bias,
+                             int32_t* labels) {
 #pragma omp parallel
   {
     double* dist = (double*)malloc(sizeof(double) * K);
@@ -328,11 +332,15 @@ void or_kmeans_assign(const uint16_t* V, int N, int d, const float* chat, int K,
 #pragma omp for schedule(dynamic, 64)
     for (int t = 0; t < N; t++) {
       for (int j = 0; j < d; j++) v[j] = bf16_val(V[(int64_t)t * d + j]);
-      labels[t] = assign_one(v, chat, K, d, dist);
+      labels[t] = assign_one(v, chat, K, d, dist, bias);
     }
     free(dist);
     free(v);
   }
+}
+
+void or_kmeans_assign(const uint16_t* V, int N, int d, const float* chat, int K, int32_t* labels) {
+  or_kmeans_assign_biased(V, N, d, chat, K, NULL, labels);
 }
 
 /* stable argsort of labels in [0, K): counting sort, ties by ascending index */
@@ -381,6 +389,37 @@ void or_kmeans(const uint16_t* V, int N, int d, int K, int iters, int cold,
     or_kmeans_update(V, N, d, labels, K, C);
   }
   or_stable_argsort(labels, N, K, perm);
+  free(chat);
+}
+
+/* Size-penalised Lloyd iterations: a cheap form of the balanced clustering   */
+/* the paper page measures and sets aside for its cost (ablation on balanced  */
+/* k-means; the weakness list). Each assignment minimises                    */
+/*   ||v - bf16(C_k)||^2 + b_k,  b_k = fl32(lambda * n_k),                    */
+/* n_k = member count of cluster k after the previous assignment (for the    */
+/* first iteration, the counts passed in), so crowded clusters lose their     */
+/* boundary tokens to neighbours; the update step is the plain one. lambda = 0 */
+/* is plain k-means. counts [K] in/out: out = sizes after the last assignment. */
+void or_kmeans_balanced(const uint16_t* V, int N, int d, int K, int iters, int cold, float lambda,
+                        int32_t* counts, float* C, int32_t* labels, int32_t* perm) {
+  if (cold) {
+    for (int k = 0; k < K; k++) {
+      int64_t t = ((int64_t)(2 * k + 1) * N) / (2 * (int64_t)K);
+      for (int j = 0; j < d; j++) C[(int64_t)k * d + j] = bf16_val(V[t * d + j]);
+    }
+  }
+  float* chat = (float*)malloc(sizeof(float) * (size_t)K * d);
+  float* bias = (float*)malloc(sizeof(float) * (size_t)K);
+  for (int it = 0; it < iters; it++) {
+    for (int64_t i = 0; i < (int64_t)K * d; i++) chat[i] = bf16_val(f32_to_bf16(C[i]));
+    for (int k = 0; k < K; k++) bias[k] = lambda * (float)counts[k]; /* one binary32 rounding */
+    or_kmeans_assign_biased(V, N, d, chat, K, bias, labels);
+    for (int k = 0; k < K; k++) counts[k] = 0;
+    for (int t = 0; t < N; t++) counts[labels[t]]++;
+    or_kmeans_update(V, N, d, labels, K, C);
+  }
+  or_stable_argsort(labels, N, K, perm);
+  free(bias);
   free(chat);
 }
 

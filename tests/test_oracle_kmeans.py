@@ -126,3 +126,77 @@ def test_kmeans_cost_brute_force_and_zero():
     assert oracle.kmeans_cost(V, C, z) == float(tot / N)
     Vs = synth.bf16_bits(rng.standard_normal((16, d)).astype(np.float32))
     assert oracle.kmeans_cost(Vs, synth.bf16_to_f32(Vs), np.arange(16, dtype=np.int32)) == 0.0
+
+
+# ---- size-penalised assignment (cheap balancing): distance + fl32(lambda * n_k)
+def test_biased_assign_brute_force_with_ties():
+    rng = np.random.default_rng(13)
+    N, d, K = 300, 8, 7
+    V = synth.bf16_bits((rng.integers(-4, 5, (N, d)) * 0.5).astype(np.float32))
+    C = (rng.integers(-4, 5, (K, d)) * 0.5).astype(np.float32)
+    C[3] = C[1]   # same centroid, same bias: lower index wins
+    C[5] = C[2]   # same centroid, smaller bias: the higher index wins
+    chat = synth.bf16_to_f32(synth.bf16_bits(C))
+    bias = (rng.integers(0, 8, K) * 0.25).astype(np.float32)
+    bias[3] = bias[1]
+    bias[5] = bias[2] - np.float32(0.25) if bias[2] > 0 else np.float32(0.0)
+    bias[2] = bias[5] + np.float32(0.25)
+    got = oracle.kmeans_assign_biased(V, chat, bias)
+    Vf = [_bits_to_fr(V[t]) for t in range(N)]
+    Cf = [[Fraction(float(x)) for x in chat[k]] for k in range(K)]
+    Bf = [Fraction(float(b)) for b in bias]
+    for t in range(N):
+        dist = [sum((a - b) ** 2 for a, b in zip(Vf[t], Cf[k])) + Bf[k] for k in range(K)]
+        want = min(range(K), key=lambda k: (dist[k], k))
+        assert got[t] == want, t
+    assert not np.any(got == 3) and not np.any(got == 2)
+
+
+def test_balanced_worked_example_on_a_line():
+    # centroids 0 and 10 on channel 0; tokens 0..7 and 10. Plain assignment: 0..5 -> 0
+    # (5 is a tie, lowest index), 6, 7, 10 -> 1, sizes (6, 3). With lambda = 4 and those
+    # sizes the biases are 24 and 12: token t joins cluster 0 iff t^2 + 24 < (10-t)^2 + 12,
+    # i.e. t < 4.4, so token 5 moves. New sizes (5, 4), means 2 and 7.
+    d = 4
+    pos = np.array([0, 1, 2, 3, 4, 5, 6, 7, 10], np.float32)
+    Vf = np.zeros((pos.size, d), np.float32)
+    Vf[:, 0] = pos
+    V = synth.bf16_bits(Vf)
+    C = np.zeros((2, d), np.float32)
+    C[1, 0] = 10
+    lab0, _, _, n0 = oracle.kmeans_balanced(V, 2, 1, False, 0.0, np.zeros(2, np.int32), C)
+    assert lab0.tolist() == [0, 0, 0, 0, 0, 0, 1, 1, 1] and n0.tolist() == [6, 3]
+    lab, perm, Cn, n = oracle.kmeans_balanced(V, 2, 1, False, 4.0, n0, C)
+    assert lab.tolist() == [0, 0, 0, 0, 0, 1, 1, 1, 1]
+    assert n.tolist() == [5, 4]
+    assert perm.tolist() == list(range(9))
+    assert Cn[0, 0] == 2.0 and Cn[1, 0] == 7.0 and not Cn[:, 1:].any()
+
+
+def test_balanced_lambda_zero_is_plain_kmeans():
+    rng = np.random.default_rng(21)
+    N, d, K = 1500, 16, 12
+    V = synth.bf16_bits(rng.standard_normal((N, d)).astype(np.float32))
+    lab, perm, C = oracle.kmeans(V, K, 3, cold=True)
+    lab2, perm2, C2, n2 = oracle.kmeans_balanced(V, K, 3, True, 0.0, np.full(K, 77, np.int32))
+    assert np.array_equal(lab, lab2) and np.array_equal(perm, perm2) and np.array_equal(C, C2)
+    assert np.array_equal(n2, np.bincount(lab, minlength=K))
+
+
+def test_balanced_penalty_evens_out_sizes():
+    # a dense blob of 900 tokens beside 4 small ones; from the same start, a moderate size
+    # penalty ends with less spread in the cluster sizes than plain iterations do
+    rng = np.random.default_rng(5)
+    d, K = 8, 8
+    centres = rng.standard_normal((5, d)).astype(np.float32) * 6
+    sizes = [900, 150, 150, 150, 150]
+    Vf = np.concatenate([centres[i] + rng.standard_normal((s, d)).astype(np.float32) for i, s in enumerate(sizes)])
+    V = synth.bf16_bits(Vf)
+    lab, _, C = oracle.kmeans(V, K, 6, cold=True)
+    n0 = np.bincount(lab, minlength=K).astype(np.int32)
+    labp, _, _ = oracle.kmeans(V, K, 6, cold=False, C=C)
+    plain_spread = np.bincount(labp, minlength=K).std()
+    for lam in (0.005, 0.01):
+        labb, _, _, nb = oracle.kmeans_balanced(V, K, 6, False, lam, n0, C)
+        assert np.array_equal(nb, np.bincount(labb, minlength=K))
+        assert nb.std() < plain_spread, lam
