@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.vc_cluster_workspace_bytes.argtypes = [I, I, I, I, I]
         L.vc_cluster.restype = I
         L.vc_cluster.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, S, P]
+        L.vc_cluster_balanced.restype = I
+        L.vc_cluster_balanced.argtypes = [P, I, I, I, I, I, I, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.vc_quantize_workspace_bytes.restype = S
         L.vc_quantize_workspace_bytes.argtypes = [I, I, I, I, I]
         L.vc_cluster_cost_workspace_bytes.restype = S
@@ -150,6 +152,24 @@ def vc_cluster(V, K, iters, cold_start, centroids, labels, perm, ws=None, stream
         ws = workspace(need, V.device)
     st = lib().vc_cluster(_ptr(V), B, H, N, d, int(K), int(iters), int(bool(cold_start)), _ptr(centroids),
                           _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st)
+
+
+def vc_cluster_balanced(V, K, iters, cold_start, lam, counts, centroids, labels, perm, ws=None, stream=None):
+    """Size-penalised k-means: distances + fl32(lam * n_k); counts [B,H,K] i32 in/out
+    (sizes for the first assignment in, sizes after the last one out)."""
+    B, H, N, d = _dims(V)
+    _need(V, torch.bfloat16, (B, H, N, d), "V")
+    _need(counts, torch.int32, (B, H, K), "counts")
+    _need(centroids, torch.float32, (B, H, K, d), "centroids")
+    _need(labels, torch.int32, (B, H, N), "labels")
+    _need(perm, torch.int32, (B, H, N), "perm")
+    need = vc_cluster_workspace_bytes(B, H, N, d, K)
+    if ws is None:
+        ws = workspace(need, V.device)
+    st = lib().vc_cluster_balanced(_ptr(V), B, H, N, d, int(K), int(iters), int(bool(cold_start)), float(lam),
+                                   _ptr(counts), _ptr(centroids), _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(),
+                                   _stream(stream))
     _check(st)
 
 

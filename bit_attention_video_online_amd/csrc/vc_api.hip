@@ -25,7 +25,7 @@ extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float*
                                  hipStream_t st);
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
 extern "C" int vc_launch_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold, float* C,
-                                 int32_t* labels, int32_t* perm, void* ws, hipStream_t st);
+                                 int32_t* labels, int32_t* perm, void* ws, hipStream_t st, float lam, int32_t* nk_io);
 extern "C" int vc_max_clusters(void);
 
 namespace {
@@ -97,7 +97,34 @@ extern "C" vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K
       overlaps(in, {(const char*)perm, el * 4}) || overlaps({(const char*)labels, el * 4}, {(const char*)perm, el * 4}))
     return VC_E_ALIAS;
   if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
-                        (hipStream_t)stream) != 0)
+                        (hipStream_t)stream, 0.0f, nullptr) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
+                                         float lambda, int32_t* counts, float* centroids, int32_t* labels,
+                                         int32_t* perm, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!V || !counts || !centroids || !labels || !perm || !workspace) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d)) return VC_E_SHAPE;
+  if (K < 1 || K > N || K > vc_max_clusters() || iters < 1 || iters > 1000) return VC_E_PARAM;
+  if (!(lambda >= 0.0f) || !(lambda < __builtin_inff())) return VC_E_PARAM;
+  if (workspace_bytes < vc_cluster_ws_bytes(B, H, N, d, K)) return VC_E_WORKSPACE;
+  if (!aligned16(V) || !aligned16(centroids) || !aligned16(labels) || !aligned16(perm) || !aligned16(workspace) ||
+      !aligned16(counts))
+    return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N;
+  const Range outs[] = {{(const char*)centroids, (size_t)B * H * K * d * 4}, {(const char*)labels, el * 4},
+                        {(const char*)perm, el * 4}, {(const char*)counts, (size_t)B * H * K * 4},
+                        {(const char*)workspace, workspace_bytes}};
+  const Range in{(const char*)V, el * d * 2};
+  for (int i = 0; i < 5; i++) {
+    if (overlaps(in, outs[i])) return VC_E_ALIAS;
+    for (int j = i + 1; j < 5; j++)
+      if (overlaps(outs[i], outs[j])) return VC_E_ALIAS;
+  }
+  if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
+                        (hipStream_t)stream, lambda, counts) != 0)
     return VC_E_HIP;
   return VC_OK;
 }

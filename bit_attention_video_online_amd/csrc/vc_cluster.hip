@@ -15,6 +15,11 @@
 //              for bf16 data of moderate dynamic range).
 //   cl_hist / cl_scan_k / cl_scan_c / cl_scatter   stable counting sort of the labels (pi)
 //   cl_update  C_k = fl32(sum of members / count), binary64 sums in pi order
+// Size-penalised variant (cheap balancing; the paper page's ablation measures balanced
+// k-means and sets it aside for its cost): every distance gets b_k = fl32(lambda n_k),
+// n_k the size of cluster k after the previous assignment, folded into |chat_k|^2 by
+// cl_prep, so the assignment loop is unchanged; only the certainty bound and the exact
+// re-rank take b_k into account.
 // No atomics on floating-point data: every result is run-to-run deterministic.
 #include "vc_device.h"
 
@@ -30,7 +35,7 @@ __global__ void cl_cold(const uint16_t* __restrict__ V, float* __restrict__ C, i
 }
 
 __global__ void cl_prep(const float* __restrict__ C, uint16_t* __restrict__ chat, float* __restrict__ cnorm, int K,
-                        int D) {
+                        int D, const int32_t* __restrict__ nk, float lam) {
   __shared__ double part[128];
   const int k = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
   const size_t o = ((size_t)bh * K + k) * D + c;
@@ -42,6 +47,7 @@ __global__ void cl_prep(const float* __restrict__ C, uint16_t* __restrict__ chat
   if (c == 0) {
     double s = 0.0;
     for (int i = 0; i < D; i++) s += part[i];
+    if (nk) s += (double)(lam * (float)nk[(size_t)bh * K + k]);  // b_k: one binary32 rounding
     cnorm[(size_t)bh * K + k] = (float)s;
   }
 }
@@ -58,10 +64,15 @@ struct Best {
 // e_k <= F(e) = 2(2 gam |v| c(e) + u (c(e)^2 + |x|)), c(e) = |v| + sqrt(x + e + |v|^2),
 // is increasing in x, so x - E(x) is increasing too and bounds every other centroid. E is
 // taken from above: two steps of F from a crude upper starting value, then doubled.
-__device__ __forceinline__ double others_lower_bound(double x, double vn, double gam, double u) {
+// With size penalties b_k >= 0 folded into the norms, the rounding term of a norm is
+// u (|c_k|^2 + b_k), and b_k <= d_k + e_k + |v|^2 as well (the exact distance' minus
+// |v - c_k|^2 - |v|^2 is b_k), so F gains u (x + e + |v|^2); the bound on |c_k| holds
+// unchanged since |v - c_k|^2 <= d_k + e_k + |v|^2 still.
+__device__ __forceinline__ double others_lower_bound(double x, double vn, double gam, double u, bool biased) {
   auto F = [&](double e) {
     const double c = vn + sqrt(fmax(x + e + vn * vn, 0.0));
-    return 2.0 * (2.0 * gam * vn * c + u * (c * c + fabs(x)));
+    const double b = biased ? fmax(x + e + vn * vn, 0.0) : 0.0;
+    return 2.0 * (2.0 * gam * vn * c + u * (c * c + b + fabs(x)));
   };
   const double e0 = 0.5 * (fabs(x) + vn * vn) + 1.0;
   const double e1 = F(e0);
@@ -87,7 +98,8 @@ constexpr int kAssignTokens = 256;  // tokens per assignment work-group
 template <int D>
 __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict__ V, const uint16_t* __restrict__ chat,
                                                       const float* __restrict__ cnorm, int N, int K,
-                                                      int32_t* __restrict__ labels) {
+                                                      int32_t* __restrict__ labels, const int32_t* __restrict__ nk,
+                                                      float lam) {
   constexpr int KS = D / 32;            // MFMA k-steps over the feature dimension
   constexpr int ROWB = 2 * D + 16;      // padded LDS row stride (bytes)
   constexpr int CCH = 64;               // centroids per chunk
@@ -98,7 +110,7 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   __shared__ Best rec[kAssignTokens][4];
   __shared__ int unsure[kAssignTokens];
   __shared__ int n_unsure;
-  __shared__ double red_d[256];
+  __shared__ double red_d[256], red_lo[256];
   __shared__ int red_k[256];
 
   const int bh = blockIdx.y, t0 = blockIdx.x * kAssignTokens;
@@ -202,7 +214,8 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
       const double vn = vn_s[tid], dg = (double)gam, du = (double)u;
       const double cnk = Nh[a.k], ck = sqrt(cnk) * 1.0001;
       const double e1 = 2.0 * (2.0 * dg * vn * ck + du * (cnk + fabs((double)a.d1))) * (1.0 + 1e-6);
-      certain = !(a.d2 < __builtin_inff()) || others_lower_bound((double)a.d2, vn, dg, du) > (double)a.d1 + e1;
+      certain = !(a.d2 < __builtin_inff()) ||
+                others_lower_bound((double)a.d2, vn, dg, du, nk != nullptr) > (double)a.d1 + e1;
     }
     if (certain) {
       labels[(size_t)bh * N + t0 + tid] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
@@ -211,12 +224,15 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
     }
   }
   __syncthreads();
-  // exact re-rank (binary64) of the uncertain tokens, the whole group per token
+  // exact re-rank (binary64) of the uncertain tokens, the whole group per token; with size
+  // penalties the distance is the exact pair (hi, lo) = TwoSum(s, b_k), ranked
+  // lexicographically (hi is the rounding of s + b_k, and rounding is monotone)
   const int nu = n_unsure;
+  const int32_t* nkh = nk ? nk + (size_t)bh * K : nullptr;
   for (int ui = 0; ui < nu; ui++) {
     const int t = t0 + unsure[ui];
     const uint16_t* vt = Vh + (size_t)t * D;
-    double best = __builtin_inf();
+    double best = __builtin_inf(), blo = 0.0;
     int bk = 0x7fffffff;
     for (int k = tid; k < K; k += 256) {
       const uint16_t* ck = Ch + (size_t)k * D;
@@ -225,16 +241,26 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
         double df = (double)bf16_to_f32(vt[c]) - (double)bf16_to_f32(ck[c]);
         s = fma(df, df, s);
       }
-      if (s < best) { best = s; bk = k; }
+      double lo = 0.0;
+      if (nkh) {
+        const double b = (double)(lam * (float)nkh[k]);
+        const double hi = s + b, bb = hi - s;
+        lo = (s - (hi - bb)) + (b - bb);
+        s = hi;
+      }
+      if (s < best || (s == best && lo < blo)) { best = s; blo = lo; bk = k; }
     }
     red_d[tid] = best;
+    red_lo[tid] = blo;
     red_k[tid] = bk;
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if (tid < o) {
-        double d2 = red_d[tid + o];
-        int k2 = red_k[tid + o];
-        if (d2 < red_d[tid] || (d2 == red_d[tid] && k2 < red_k[tid])) { red_d[tid] = d2; red_k[tid] = k2; }
+        const double d2 = red_d[tid + o], l2 = red_lo[tid + o];
+        const int k2 = red_k[tid + o];
+        if (d2 < red_d[tid] || (d2 == red_d[tid] && (l2 < red_lo[tid] || (l2 == red_lo[tid] && k2 < red_k[tid])))) {
+          red_d[tid] = d2; red_lo[tid] = l2; red_k[tid] = k2;
+        }
       }
       __syncthreads();
     }
@@ -437,8 +463,17 @@ extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K) {
          3 * BH * K * sizeof(int32_t) + 1024;
 }
 
+__global__ void cl_copy_sizes(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// nk_io == nullptr: plain Lloyd iterations (lam unused). Otherwise size-penalised: the first
+// assignment uses the sizes in nk_io, later ones the sizes of the previous assignment, and
+// nk_io receives the sizes of the last one.
 extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int K, int iters, int cold, float* C,
-                                 int32_t* labels, int32_t* perm, void* ws, hipStream_t st) {
+                                 int32_t* labels, int32_t* perm, void* ws, hipStream_t st, float lam,
+                                 int32_t* nk_io) {
   const uint16_t* V = (const uint16_t*)Vv;
   const int BH = B * H, nch = (N + kChunk - 1) / kChunk;
   char* w = (char*)ws;
@@ -452,9 +487,10 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
   if (cold) cl_cold<<<dim3(K, BH), d, 0, st>>>(V, C, N, K, d);
   const dim3 gmf((N + kAssignTokens - 1) / kAssignTokens, BH), gch(nch, BH), gk(K, BH);
   for (int it = 0; it < iters; it++) {
-    cl_prep<<<gk, d, 0, st>>>(C, chat, cnorm, K, d);
-    if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
-    else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels);
+    const int32_t* nk = nk_io ? (it == 0 ? nk_io : csize) : nullptr;
+    cl_prep<<<gk, d, 0, st>>>(C, chat, cnorm, K, d, nk, lam);
+    if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nk, lam);
+    else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nk, lam);
     cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
     cl_scan_k<<<dim3((K + 3) / 4, BH), 256, 0, st>>>(counts, K, nch, offs, ctotal);
     cl_scan_c<<<BH, 1024, 0, st>>>(ctotal, K, cstart, csize);
@@ -462,6 +498,7 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
     if (d == 128) cl_update<128><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
     else cl_update<64><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
   }
+  if (nk_io && iters > 0) cl_copy_sizes<<<(BH * K + 255) / 256, 256, 0, st>>>(csize, nk_io, BH * K);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -98,6 +98,34 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * vc_cluster_balanced -- vc_cluster with size-penalised assignment, a cheap form of
+ * the balanced clustering the paper page's ablation measures (better error, but a
+ * grouping cost its authors would not pay; balancing is on its weakness list).
+ *
+ * Every assignment minimises ||v - bf16(C_k)||^2 + b_k with b_k = fl32(lambda * n_k)
+ * (one binary32 product), exactly, ties to the lowest index; n_k is the size of
+ * cluster k after the previous assignment, taken from `counts` for the first
+ * iteration. The update step is vc_cluster's. lambda = 0 gives vc_cluster's result.
+ * A lambda near or above the typical gap between a token's two nearest distances
+ * makes sizes oscillate between iterations (clusters can empty); a useful range is
+ * a small fraction of (mean squared distance) / (N/K).
+ *
+ *   lambda     finite, >= 0 (else VC_E_PARAM); distance units per member
+ *   counts     int32 [B,H,K]  in: sizes for the first assignment (zeros: plain
+ *                             first iteration; a previous call's output: warm
+ *                             start), out: sizes after the last assignment
+ *   other arguments as for vc_cluster; counts must not overlap any other buffer
+ *   (VC_E_ALIAS) and must be 16-byte aligned (VC_E_UNSUPPORTED)
+ *
+ * Exactness as for vc_cluster: the certainty bound also covers the rounding of the
+ * penalised norms, and re-ranked distances are compared as the exact pair
+ * TwoSum(binary64 squared distance, b_k).
+ * ------------------------------------------------------------------------ */
+vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
+                              float lambda, int32_t* counts, float* centroids, int32_t* labels, int32_t* perm,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * vc_cluster_cost -- the k-means objective of the current values under a kept
  * clustering, a drift statistic for refreshing the permutation early (the paper
  * page's weakness list: the reused permutation loses accuracy when the layout

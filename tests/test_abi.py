@@ -141,6 +141,26 @@ def test_cluster_rejects_bad_arguments(L):
     assert call(lab=ctypes.c_void_p(3 << 20)) == 7   # labels alias perm
 
 
+def test_cluster_balanced_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(V=FAKE, B=1, H=1, N=256, d=128, K=8, iters=2, cold=1, lam=0.5, cnt=ctypes.c_void_p(5 << 20),
+                 C=ctypes.c_void_p(1 << 20), lab=ctypes.c_void_p(2 << 20), perm=ctypes.c_void_p(3 << 20),
+                 ws=ctypes.c_void_p(4 << 20), wsb=1 << 19)
+        a.update(kw)
+        return L.vc_cluster_balanced(a["V"], a["B"], a["H"], a["N"], a["d"], a["K"], a["iters"], a["cold"], a["lam"],
+                                     a["cnt"], a["C"], a["lab"], a["perm"], a["ws"], a["wsb"], None)
+    assert call(cnt=None) == 1
+    assert call(N=100) == 2
+    assert call(K=0) == 3
+    assert call(lam=-1.0) == 3
+    assert call(lam=float("nan")) == 3
+    assert call(lam=float("inf")) == 3
+    assert call(wsb=8) == 4
+    assert call(cnt=ctypes.c_void_p((5 << 20) + 4)) == 5
+    assert call(cnt=ctypes.c_void_p(2 << 20)) == 7    # counts alias labels
+    assert call(cnt=ctypes.c_void_p((4 << 20) + 256)) == 7  # counts inside the workspace
+
+
 def test_workspace_queries(L):
     assert vc.vc_quantize_workspace_bytes(1, 40, 70400, 128) > 0
     assert vc.vc_quantize_workspace_bytes(1, 1, 100, 128) == 0

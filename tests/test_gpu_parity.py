@@ -231,6 +231,68 @@ def test_cluster_ties_duplicate_centroids():
     assert np.array_equal(C[0, 0], c_or)
 
 
+def _gpu_cluster_balanced(V, K, iters, cold, lam, counts, C0=None):
+    B, H, N, d = V.shape
+    C = torch.zeros((B, H, K, d), dtype=torch.float32, device="cuda") if C0 is None else to_dev(C0)
+    cnt = to_dev(np.ascontiguousarray(counts, dtype=np.int32))
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    vc.vc_cluster_balanced(to_dev_bf16(V), K, iters, cold, lam, cnt, C, lab, perm)
+    torch.cuda.synchronize()
+    return lab.cpu().numpy(), perm.cpu().numpy(), C.cpu().numpy(), cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,N,K,iters", [(128, 1024, 8, 3), (64, 2560, 37, 2), (128, 3072, 300, 2)])
+@pytest.mark.parametrize("kappa", [0.0, 0.01, 0.3, 30.0])
+def test_cluster_balanced_bitexact(d, N, K, iters, kappa):
+    """Size-penalised k-means, warm start with given sizes, several heads and a ragged last
+    work-group; lambda = kappa * J / (N/K) with J the plain mean squared distance, from no
+    effect up to the oscillating regime. Labels, perm, centroids and sizes bit-exact."""
+    B, H = 1, 2
+    w = synth.gen("wan", seed=14, B=B, H=H, N=N, d=d)
+    rng = np.random.default_rng(N + K)
+    C0 = (rng.standard_normal((B, H, K, d)) * 2).astype(np.float32)
+    cnt0 = rng.integers(0, 3 * N // K + 1, (B, H, K)).astype(np.int32)
+    lab0, _, _ = oracle.kmeans(w["V"][0, 0], K, 1, cold=False, C=C0[0, 0])
+    J = oracle.kmeans_cost(w["V"][0, 0], C0[0, 0], lab0)
+    lam = float(np.float32(kappa * J * K / N))
+    lab, perm, C, cnt = _gpu_cluster_balanced(w["V"], K, iters, False, lam, cnt0, C0)
+    for h in range(H):
+        l_or, p_or, c_or, n_or = oracle.kmeans_balanced(w["V"][0, h], K, iters, False, lam, cnt0[0, h], C0[0, h])
+        assert np.array_equal(lab[0, h], l_or), (h, np.count_nonzero(lab[0, h] != l_or))
+        assert np.array_equal(perm[0, h], p_or)
+        assert np.array_equal(C[0, h], c_or)
+        assert np.array_equal(cnt[0, h], n_or)
+
+
+def test_cluster_balanced_lambda_zero_equals_plain():
+    w = synth.gen("wan", seed=8, B=1, H=2, N=2048, d=128)
+    a = _gpu_cluster(w["V"], 16, 2, True)
+    b = _gpu_cluster_balanced(w["V"], 16, 2, True, 0.0, np.full((1, 2, 16), 99, np.int32))
+    for x, y in zip(a, b[:3]):
+        assert np.array_equal(x, y)
+    assert np.array_equal(b[3][0, 0], np.bincount(a[0][0, 0], minlength=16))
+
+
+def test_cluster_balanced_ties_and_rerank():
+    """Integer data, duplicate centroids with equal sizes (exact ties: lowest index) and
+    with sizes one apart (the penalty alone decides): exercises the exact re-rank."""
+    B, H, N, d, K = 1, 1, 512, 64, 6
+    rng = np.random.default_rng(12)
+    V = synth.bf16_bits((rng.integers(-3, 4, (B, H, N, d)) * 0.5).astype(np.float32))
+    C0 = (rng.integers(-3, 4, (B, H, K, d)) * 0.5).astype(np.float32)
+    C0[0, 0, 4] = C0[0, 0, 1]
+    C0[0, 0, 5] = C0[0, 0, 2]
+    cnt0 = np.array([[[40, 70, 71, 30, 70, 70]]], np.int32)
+    for lam in (0.25, 0.0625):
+        lab, perm, C, cnt = _gpu_cluster_balanced(V, K, 2, False, lam, cnt0, C0)
+        l_or, p_or, c_or, n_or = oracle.kmeans_balanced(V[0, 0], K, 2, False, lam, cnt0[0, 0], C0[0, 0])
+        assert np.array_equal(lab[0, 0], l_or)
+        assert np.array_equal(perm[0, 0], p_or)
+        assert np.array_equal(C[0, 0], c_or)
+        assert np.array_equal(cnt[0, 0], n_or)
+
+
 @pytest.mark.parametrize("d,N,K", [(128, 1024, 8), (64, 2560, 37), (128, 3072, 300)])
 def test_cluster_cost_matches_oracle(d, N, K):
     """k-means objective under given (arbitrary) labels and centroids, several heads,
