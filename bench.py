@@ -7,7 +7,7 @@ resident in HBM before the timed region. `value` is attention-equivalent TFLOPS 
 whole step, 4*B*H*N^2*d / t_step; the per-stage times and the attention kernel's own
 TFLOPS (from HIP events on the launch stream) are reported beside it.
 
-Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule|oracle]
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload wan|sweepN|schedule|balance|oracle]
                        [--no-cpu-baseline] [--attention-only [--attn-mode vc|vc_e5m2|expcast|exp]]
 """
 from __future__ import annotations
@@ -337,6 +337,90 @@ def run_schedule(args):
     print(json.dumps(res), flush=True)
 
 
+def run_balance(args):
+    """Size-penalised (balanced) clustering against plain k-means on the Wan-shaped step:
+    from the same warm state (cold 4-iteration k-means on the previous step's values and
+    its cluster sizes), 2 warm iterations with lambda = kappa * J / (N/K), J the mean
+    squared assignment distance of the current values under the warm clustering. Reports
+    per kappa: k-means time, cluster-size spread, the share of 128-token key blocks that
+    hold one cluster only, the k-means objective, and the attention error (V-Smooth +
+    ExpCast) against binary64 exact attention on sampled rows of several heads."""
+    import numpy as np
+    import torch
+    import bit_attention_video_online_amd as vc
+
+    torch.cuda.set_device(0)
+    B, H, N, d, Kc, seed = 1, 40, 70400, 128, 550, 2
+    dev, _ = make_inputs("wan", B, H, N, d, seed)
+    Qd, Kd, Vd, Vpd = dev["Q"], dev["K"], dev["V"], dev["V_prev"]
+    Cw = torch.zeros((B, H, Kc, d), dtype=torch.float32, device="cuda")
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    ws_c = vc.workspace(vc.vc_cluster_workspace_bytes(B, H, N, d, Kc))
+    vc.vc_cluster(Vpd, Kc, 4, True, Cw, lab, perm, ws=ws_c)
+    cnt_w = torch.stack([torch.bincount(lab[0, h].long(), minlength=Kc) for h in range(H)]).int().view(B, H, Kc)
+    cost = torch.empty((B, H), dtype=torch.float64, device="cuda")
+    ws_cost = vc.workspace(int(vc.lib().vc_cluster_cost_workspace_bytes(B, H, N, d)))
+    vc.vc_cluster_cost(Vd, Cw, lab, cost, ws=ws_cost)
+    J = float(cost.mean())
+    q = vc.quantize_outputs(B, H, N, d)
+    ws_q = vc.workspace(vc.vc_quantize_workspace_bytes(B, H, N, d))
+    O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    heads = list(range(0, H, max(1, H // args.balance_heads)))[:args.balance_heads]
+    rows_t = torch.from_numpy(np.linspace(0, N - 1, args.schedule_rows).astype(np.int64)).cuda()
+    exact = {h: exact_attention_rows(Qd[0, h][rows_t].double(), Kd[0, h].double(), Vd[0, h].double()) for h in heads}
+    C = torch.empty_like(Cw)
+    cnt = torch.empty_like(cnt_w)
+    out = []
+    for kappa in [float(x) for x in args.kappas.split(",")]:
+        lam = kappa * J * Kc / N
+
+        def run():
+            C.copy_(Cw)
+            cnt.copy_(cnt_w)
+            if kappa == 0.0:
+                vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
+            else:
+                vc.vc_cluster_balanced(Vd, Kc, 2, False, lam, cnt, C, lab, perm, ws=ws_c)
+        run()
+        times = []
+        for _ in range(5):
+            C.copy_(Cw)
+            cnt.copy_(cnt_w)
+            e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if kappa == 0.0:
+                vc.vc_cluster(Vd, Kc, 2, False, C, lab, perm, ws=ws_c)
+            else:
+                vc.vc_cluster_balanced(Vd, Kc, 2, False, lam, cnt, C, lab, perm, ws=ws_c)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        sizes = torch.stack([torch.bincount(lab[0, h].long(), minlength=Kc) for h in range(H)]).double()
+        ls = torch.gather(lab, 2, perm.long()).view(B, H, N // 128, 128)
+        pure = float((ls.amin(-1) == ls.amax(-1)).double().mean())
+        vc.vc_cluster_cost(Vd, C, lab, cost, ws=ws_cost)
+        vc.vc_quantize(Qd, Kd, Vd, perm, vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH, q, ws=ws_q)
+        vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+        torch.cuda.synchronize()
+        num = den = 0.0
+        for h in heads:
+            diff = O[0, h][rows_t].double() - exact[h]
+            num += float((diff * diff).sum())
+            den += float((exact[h] * exact[h]).sum())
+        row = dict(kappa=kappa, lam=lam, kmeans_ms=round(min(times), 3),
+                   size_cv=round(float((sizes.std(1) / sizes.mean(1)).mean()), 4),
+                   size_max=int(sizes.max()), empty_clusters=int((sizes == 0).sum()),
+                   single_cluster_blocks=round(pure, 4), kmeans_objective=round(float(cost.mean()), 4),
+                   rmse=round((num / den) ** 0.5, 6))
+        log("[balance] %s" % row)
+        out.append(row)
+    res = {"workload": "balanced vs plain k-means on the wan2.2-shaped step, B=%d H=%d N=%d d=%d, %d clusters, "
+                       "2 warm iterations; error on %d rows x heads %s" % (B, H, N, d, Kc, args.schedule_rows, heads),
+           "J_warm": J, "rows": out}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +441,9 @@ def main():
                     help="schedule workload: fixed clustering steps 0-4, or drift-triggered refresh")
     ap.add_argument("--drift-threshold", type=float, default=0.05,
                     help="relative growth of the k-means objective that triggers a refresh")
+    ap.add_argument("--kappas", default="0,0.003,0.01,0.03,0.1",
+                    help="balance workload: penalty scales, lambda = kappa * J / (N/K)")
+    ap.add_argument("--balance-heads", type=int, default=8, help="balance workload: heads sampled for the error")
     ap.add_argument("--quant-prep", default="none", choices=["none", "rope", "hadamard", "rope_hadamard"],
                     help="preprocessing fused into the quantiser: RoPE on the video grid and/or the Q/K Hadamard "
                          "rotation")
@@ -379,6 +466,9 @@ def main():
 
     if args.workload == "schedule":
         run_schedule(args)
+        return
+    if args.workload == "balance":
+        run_balance(args)
         return
     if args.workload in ("oracle", "oracle-c0"):
         run_oracle_timing(args)
