@@ -111,6 +111,36 @@ def test_wan_cluster_cost_sampled_heads(run, oracle_heads):
     assert np.all(got > 0)
 
 
+def test_wan_balanced_kmeans_sampled_heads(run, oracle_heads):
+    """Size-penalised k-means at full size from the warm state (sizes of the warm labels),
+    lambda = 0.01 J / (N/K): all heads on the GPU, two heads bit-exact against the oracle."""
+    w = run["w"]
+    B, H, N, d = w["V"].shape
+    # inputs of the sampled heads come from the oracle (its warm state and the sizes of its
+    # warm-started labels); the other heads start from the GPU warm state with zero sizes
+    Cw = run["Cw"].copy()
+    cnt0 = np.zeros((B, H, KC), np.int32)
+    for h in HEADS:
+        Cw[0, h] = oracle_heads[h]["Cw"]
+        cnt0[0, h] = np.bincount(oracle_heads[h]["lab"], minlength=KC)
+    lam = float(np.float32(0.01 * 141.87 * KC / N))
+    C = torch.from_numpy(Cw).cuda()
+    cnt = torch.from_numpy(cnt0).cuda()
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    vc.vc_cluster_balanced(to_dev_bf16(w["V"]), KC, 2, False, lam, cnt, C, lab, perm)
+    torch.cuda.synchronize()
+    lab, perm, C, cnt = (x.cpu().numpy() for x in (lab, perm, C, cnt))
+    for h in HEADS:
+        l_or, p_or, c_or, n_or = oracle.kmeans_balanced(w["V"][0, h], KC, 2, False, lam, cnt0[0, h], Cw[0, h])
+        assert np.array_equal(lab[0, h], l_or), (h, np.count_nonzero(lab[0, h] != l_or))
+        assert np.array_equal(perm[0, h], p_or), h
+        assert np.array_equal(C[0, h], c_or), h
+        assert np.array_equal(cnt[0, h], n_or), h
+    for h in range(H):
+        assert np.array_equal(cnt[0, h], np.bincount(lab[0, h], minlength=KC)), h
+
+
 def test_wan_quantize_bitexact_sampled_heads(run, oracle_heads):
     g = run["q"]
     for h in HEADS:
