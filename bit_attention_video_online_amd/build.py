@@ -12,7 +12,10 @@ SOURCES = ["vc_api.hip", "vc_quantize.hip", "vc_attention.hip", "vc_cluster.hip"
 # Per-file extra flags. The attention kernel takes finite inputs by contract: without
 # NaN semantics (and with the shader's IEEE mode off) float max needs no operand
 # canonicalisation, which removes one VALU op per score element.
-EXTRA = {"vc_attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# The k-means assignment reads its matrix-core results once each: with the MFMAs in their
+# VGPR form it needs no accumulator-register read-back (one vector instruction per distance).
+EXTRA = {"vc_attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "vc_cluster.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -186,10 +186,10 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
         const float cnk = cn_s[kl];
         for (int g = 0; g < NG; g++) {
           const float dd = __builtin_fmaf(-2.0f, acc[g][i], cnk);  // exact scaling, one rounding
-          const bool better = dd < d1[g];
-          d2[g] = fminf(d2[g], better ? d1[g] : dd);
-          d1[g] = better ? dd : d1[g];
-          kbest[g] = better ? k0 + kl : kbest[g];
+          // d1 <= d2 always, so the new runner-up is the median of (d1, d2, dd)
+          kbest[g] = dd < d1[g] ? k0 + kl : kbest[g];
+          d2[g] = __builtin_amdgcn_fmed3f(d1[g], d2[g], dd);
+          d1[g] = fminf(d1[g], dd);
         }
       }
     }
