@@ -75,6 +75,8 @@ __device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte global -> LDS copy (global_load_lds_dwordx4): lane L of the wave writes
 // LDS[base + 16 L]. The builtin exists only for the device pass; seen by the host pass
@@ -292,20 +294,32 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   auto flush = [&](int nvalid) {
     float2 t[8];
     for (int k = 0; k < 8; k++) t[k] = rlog[k * 32 + r32];
-    bf16x8 w0, w1;
-    for (int k = 0; k < 8; k++) {
-      const float w = k < nvalid ? t[k].x * __builtin_amdgcn_exp2f(t[k].y - m) : 0.0f;
-      const __bf16 hi = (__bf16)w;
-      const __bf16 lo = (__bf16)(w - (float)hi);
-      w0[k] = h ? lo : hi;
-      w1[k] = h ? (__bf16)0.0f : hi;
+    // pairs of weights: hi = bf16(w) and lo = bf16(w - hi), two per conversion; lanes of
+    // the upper half supply the low parts (and zeros to the second MFMA)
+    v8i w0, w1;
+    for (int k2 = 0; k2 < 4; k2++) {
+      f32x2 w;
+      w.x = 2 * k2 < nvalid ? t[2 * k2].x * __builtin_amdgcn_exp2f(t[2 * k2].y - m) : 0.0f;
+      w.y = 2 * k2 + 1 < nvalid ? t[2 * k2 + 1].x * __builtin_amdgcn_exp2f(t[2 * k2 + 1].y - m) : 0.0f;
+      const bf16x2 hb = __builtin_convertvector(w, bf16x2);
+      uint32_t hp;
+      __builtin_memcpy(&hp, &hb, 4);
+      const f32x2 r = {w.x - __uint_as_float(hp << 16), w.y - __uint_as_float(hp & 0xffff0000u)};
+      const bf16x2 lb = __builtin_convertvector(r, bf16x2);
+      uint32_t lp;
+      __builtin_memcpy(&lp, &lb, 4);
+      w0[k2] = (int)(h ? lp : hp);
+      w1[k2] = h ? 0 : (int)hp;
     }
+    bf16x8 b0, b1;
+    __builtin_memcpy(&b0, &w0, 16);
+    __builtin_memcpy(&b1, &w1, 16);
     for (int db = 0; db < NDB; db++) {
       bf16x8 a0, a1;
       __builtin_memcpy(&a0, packs + (db * 2 + 0) * 1024 + lane * 16, 16);
       __builtin_memcpy(&a1, packs + (db * 2 + 1) * 1024 + lane * 16, 16);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, w0, oacc[db], 0, 0, 0);
-      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, w1, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, oacc[db], 0, 0, 0);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, oacc[db], 0, 0, 0);
     }
   };
 
