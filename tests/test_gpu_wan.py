@@ -189,6 +189,36 @@ def test_wan_attention_sampled_rows(run, oracle_heads):
     assert m["vc"] < m["expcast"]
 
 
+def test_wan_every_head_bitexact_and_rows(run):
+    """Every one of the 40 heads against the oracle: warm-start and warm k-means (centroids,
+    labels, pi), every quantiser output bit-exact, and the VC output on 32 seeded rows per
+    head within 2e-3 of the emulation (rows are independent given K and V)."""
+    w = run["w"]
+    g = run["q"]
+    B, H, N, d = w["Q"].shape
+    rng = np.random.default_rng(80)
+    worst = 0.0
+    t0 = time.time()
+    for h in range(H):
+        _, _, Cw = oracle.kmeans(w["V_prev"][0, h], KC, 4, cold=True)
+        lab, perm, C = oracle.kmeans(w["V"][0, h], KC, 2, cold=False, C=Cw)
+        assert np.array_equal(run["Cw"][0, h], Cw), h
+        assert np.array_equal(run["lab"][0, h], lab), h
+        assert np.array_equal(run["perm"][0, h], perm), h
+        assert np.array_equal(run["C"][0, h], C), h
+        o = oracle.quantize(w["Q"][0, h], w["K"][0, h], w["V"][0, h], perm, oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
+        for k in ("Qq", "sQ", "Kq", "sK", "sV", "mu", "mu_scaled"):
+            assert np.array_equal(g[k][0, h], o[k]), (h, k)
+        assert np.array_equal(vq_rowmajor(g["Vq"])[0, h], o["Vq"]), h
+        rows = np.sort(rng.choice(N, 32, replace=False)).astype(np.int32)
+        O_em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+        err = rel_l2(synth.bf16_to_f32(run["O"][0, h][rows]).astype(np.float64), O_em)
+        worst = max(worst, err)
+        assert err <= 2e-3, (h, err)
+        if h % 8 == 7:
+            print("[wan] heads 0-%d match (%.0fs, worst rel-L2 %.2e)" % (h, time.time() - t0, worst), flush=True)
+
+
 def test_wan_rope_hadamard_sampled_heads(run, oracle_heads):
     """RoPE on the video grid (22 x 40 x 80) and the Q/K Hadamard rotation inside the
     quantiser at full size: quantiser outputs of two heads bit-exact, attention on sampled
