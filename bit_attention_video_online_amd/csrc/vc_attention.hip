@@ -176,7 +176,10 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   // reads of one stage never alias the asynchronous copies into the other, and inserts no
   // wait for those copies before the reads.
   __shared__ __attribute__((aligned(16))) uint8_t kst0[TILE], kst1[TILE], vst0[TILE], vst1[TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t packs[RESTORE ? PACK + RLOG : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t packs[RESTORE ? PACK : 16];
+  // the row-sum log has an array of its own: written with ordinary LDS stores, it must not
+  // look to the compiler as if it could alias the mean operand's asynchronous copies
+  __shared__ __attribute__((aligned(16))) float2 rlog_all[RESTORE ? RLOG / 8 : 2];
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   // v_mfma_f32_32x32x16_bf16 per 32-channel block: K slots 0..7 (lanes 0-31) take
   // mu_hi x w_hi, slots 8..15 (lanes 32-63) mu_hi x w_lo, and the second MFMA mu_lo x w_hi.
   // Log layout per wave [slot][query]: 32 lanes touch 256 contiguous bytes.
-  float2* const rlog = reinterpret_cast<float2*>(packs + PACK) + wave * (8 * 32);
+  float2* const rlog = rlog_all + wave * (8 * 32);
   auto flush = [&](int nvalid) {
     float2 t[8];
     for (int k = 0; k < 8; k++) t[k] = rlog[k * 32 + r32];
@@ -367,6 +370,8 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   __syncthreads();
   s_part(S0{}, 0);
   s_part(S0{}, 2);
+  // iteration 0 copies K_2 into stage 0: every wave must have read K_0 from it first
+  wg_barrier();
 
   // iteration j; P = j & 1 is a compile-time stage number
   auto iteration = [&](int j, auto P) {
@@ -414,33 +419,41 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     // per-byte min fixes the operand before its MFMAs read it.
     const bool fix = EXPCAST && __ballot(fabsf(mp) >= 65536.0f);
     auto bytes_half = [&](int kh) {
+      if (EXPCAST) {
+        // All 32 FMAs of the half first (in place: the accumulators are dead afterwards),
+        // then the byte conversions with the eight packed words interleaved. Written one
+        // word at a time, each conversion waits on the FMA issued just before it and on
+        // the previous byte of the same word: one serial chain through the whole half.
+        const float bias = C0 - SLOPE * mp;
+        const float s8 = SLOPE * sigma;
+        for (int kb = 2 * kh; kb < 2 * kh + 2; kb++)
+          for (int i = 0; i < 16; i++) sacc[kb][i] = __builtin_fmaf(sacc[kb][i], s8, bias);
+        uint32_t w[8];
+        for (int k = 0; k < 8; k++) w[k] = __builtin_amdgcn_cvt_pk_u8_f32(sacc[2 * kh + (k >> 2)][4 * (k & 3)], 0, 0u);
+        for (int b = 1; b < 4; b++)
+          for (int k = 0; k < 8; k++) w[k] = __builtin_amdgcn_cvt_pk_u8_f32(sacc[2 * kh + (k >> 2)][4 * (k & 3) + b], b, w[k]);
+        for (int k = 0; k < 8; k++) pf[kh][k] = (int)w[k];
+        if (fix)
+          for (int k = 0; k < 8; k++) pf[kh][k] = (int)bytes_min120((uint32_t)pf[kh][k]);
+        return;
+      }
+      // exp-then-cast
       for (int kb = 2 * kh; kb < 2 * kh + 2; kb++)
         for (int qd = 0; qd < 4; qd++) {
-          uint32_t w = 0;
-          if (EXPCAST) {
-            const float bias = C0 - SLOPE * mp;
-            const float s8 = SLOPE * sigma;
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 0], s8, bias), 0, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 1], s8, bias), 1, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 2], s8, bias), 2, w);
-            w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sacc[kb][4 * qd + 3], s8, bias), 3, w);
-          } else {
-            const float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 0] - mp);
-            const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
-            const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
-            const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
-            // both conversions as one opaque step right after the exponentials: written
-            // with the builtins, the compiler keeps all 32 scaled values of the half live
-            // until the PV operand is needed and then spills with the MXFP4 value path;
-            // op_sel[3] writes the high word and keeps the low one
-            asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2\n\tv_cvt_pk_fp8_f32 %0, %3, %4 op_sel:[0,0,1]"
-                         : "=&v"(w) : "v"(p0), "v"(p1), "v"(p2), "v"(p3));
-            r += (p0 + p1) + (p2 + p3);
-          }
+          const float p0 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 0] - mp);
+          const float p1 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 1] - mp);
+          const float p2 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 2] - mp);
+          const float p3 = 256.0f * __builtin_amdgcn_exp2f(sigma * sacc[kb][4 * qd + 3] - mp);
+          // both conversions as one opaque step right after the exponentials: written
+          // with the builtins, the compiler keeps all 32 scaled values of the half live
+          // until the PV operand is needed and then spills with the MXFP4 value path;
+          // op_sel[3] writes the high word and keeps the low one
+          uint32_t w;
+          asm volatile("v_cvt_pk_fp8_f32 %0, %1, %2\n\tv_cvt_pk_fp8_f32 %0, %3, %4 op_sel:[0,0,1]"
+                       : "=&v"(w) : "v"(p0), "v"(p1), "v"(p2), "v"(p3));
+          r += (p0 + p1) + (p2 + p3);
           pf[kh][4 * (kb & 1) + qd] = (int)w;
         }
-      if (fix)
-        for (int k = 0; k < 8; k++) pf[kh][k] = (int)bytes_min120((uint32_t)pf[kh][k]);
     };
     bytes_half(0);
     pv_part(vt, 0, pf[0]);
