@@ -64,6 +64,15 @@ def run():
         vc.vc_attention(q, Or, beta=BETA, flags=vc.VC_F_EXPCAST)
         repeat_identical.append(bool(torch.equal(Or, O)))
         del Or
+    # k-means (warm, from the same start) and the quantiser repeated as well
+    C2 = Cw.clone()
+    lab2, perm2 = torch.empty_like(lab), torch.empty_like(perm)
+    vc.vc_cluster(V, KC, 2, False, C2, lab2, perm2)
+    repeat_identical.append(bool(torch.equal(C2, C) and torch.equal(lab2, lab) and torch.equal(perm2, perm)))
+    q2 = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(Q, K, V, perm, vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH, q2)
+    repeat_identical.append(all(bool(torch.equal(q2[k], q[k])) for k in q))
+    del C2, lab2, perm2, q2
     torch.cuda.synchronize()
     print("[wan] GPU path done in %.1fs" % (time.time() - t0), flush=True)
     res = dict(w=w, Cw=Cw.cpu().numpy(), C=C.cpu().numpy(), lab=lab.cpu().numpy(), perm=perm.cpu().numpy(),
@@ -76,9 +85,10 @@ def run():
 
 
 def test_wan_attention_repeatable(run):
-    """Four more launches of the VC attention on the same inputs give the same bytes: the
-    kernel's accumulation order is fixed, so any difference is a race (a tile stage copied
-    over while another wave of the work-group still reads it)."""
+    """Four more launches of the VC attention on the same inputs give the same bytes, and so
+    do a second warm k-means from the same centroids and a second quantiser call: every
+    accumulation order is fixed, so any difference is a race (for attention, a tile stage
+    copied over while another wave of the work-group still reads it)."""
     assert all(run["repeat_identical"]), run["repeat_identical"]
 
 
