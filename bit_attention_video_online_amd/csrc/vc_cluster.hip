@@ -372,16 +372,27 @@ __global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V,
   const int32_t* ph = perm + (size_t)bh * N + s0;
   const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int i = g; i < n; i += G) {
-    int row = ph[i];
-    row = ((unsigned)row < (unsigned)N) ? row : 0;
-    const uint4 raw = *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
+  auto add_row = [&](const uint4 raw) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     for (int e = 0; e < 4; e++) {
       acc[2 * e] += (double)__uint_as_float(w[e] << 16);
       acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
     }
+  };
+  auto load_row = [&](int i) {
+    int row = ph[i];
+    row = ((unsigned)row < (unsigned)N) ? row : 0;
+    return *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
+  };
+  // four member rows in flight per row group (the index and row loads of one member are
+  // dependent; members are independent); the binary64 sums are exact, so the order in
+  // which members are added does not change the result
+  int i = g;
+  for (; i + 3 * G < n; i += 4 * G) {
+    const uint4 r0 = load_row(i), r1 = load_row(i + G), r2 = load_row(i + 2 * G), r3 = load_row(i + 3 * G);
+    add_row(r0); add_row(r1); add_row(r2); add_row(r3);
   }
+  for (; i < n; i += G) add_row(load_row(i));
   for (int e = 0; e < 8; e++) part[g][8 * chunk + e] = acc[e];
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += 128) {
