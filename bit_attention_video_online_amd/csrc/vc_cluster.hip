@@ -161,18 +161,33 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   }
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
+  // centroid chunks of CCH bf16 rows go through registers into LDS; the next chunk's global
+  // loads are issued before the current chunk is ranked, so their latency is hidden
+  constexpr int SPT = CCH * (D / 8) / 256;  // 16-byte pieces per thread per chunk
+  uint4 pre[SPT];
+  float pre_cn = 3.0e38f;
+  auto load_chunk = [&](int k0) {
+    for (int p = 0; p < SPT; p++) {
+      const int i = tid + 256 * p;
+      const int k = i / (D / 8), c8 = (i % (D / 8)) * 8;
+      pre[p] = make_uint4(0, 0, 0, 0);
+      if (k0 + k < K) pre[p] = *reinterpret_cast<const uint4*>(Ch + (size_t)(k0 + k) * D + c8);
+    }
+    // padding past K gets zero rows and a huge finite norm, so its distance never wins
+    if (tid < CCH) pre_cn = (k0 + tid < K) ? Nh[k0 + tid] : 3.0e38f;
+  };
+  load_chunk(0);
   for (int k0 = 0; k0 < K; k0 += CCH) {
     __syncthreads();
     // stage chat rows [k0, k0+64) (bf16)
-    for (int i = tid; i < CCH * (D / 8); i += 256) {
+    for (int p = 0; p < SPT; p++) {
+      const int i = tid + 256 * p;
       const int k = i / (D / 8), c8 = (i % (D / 8)) * 8;
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (k0 + k < K) w = *reinterpret_cast<const uint4*>(Ch + (size_t)(k0 + k) * D + c8);
-      *reinterpret_cast<uint4*>(Cs + k * ROWB + 2 * c8) = w;
+      *reinterpret_cast<uint4*>(Cs + k * ROWB + 2 * c8) = pre[p];
     }
-    // padding past K gets zero rows and a huge finite norm, so its distance never wins
-    if (tid < CCH) cn_s[tid] = (k0 + tid < K) ? Nh[k0 + tid] : 3.0e38f;
+    if (tid < CCH) cn_s[tid] = pre_cn;
     __syncthreads();
+    if (k0 + CCH < K) load_chunk(k0 + CCH);
     for (int cb = 0; cb < CCH / 16; cb++) {
       v4f acc[NG];
       for (int g = 0; g < NG; g++) acc[g] = zero4;
