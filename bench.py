@@ -428,7 +428,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="wan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=12288,
+                    help="attention rows of the oracle sample (about 10 s of CPU work with the k-means and quantiser)")
     ap.add_argument("--attention-only", action="store_true", help="time only vc_attention (profiling aid)")
     ap.add_argument("--attn-mode", default="vc", choices=["vc", "vc_e5m2", "expcast", "exp", "vs_mx4", "vc_mx4"],
                     help="with --attention-only: vc = V-Smooth + ExpCast (the path); vc_e5m2 = the same with "
