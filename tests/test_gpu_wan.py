@@ -64,6 +64,13 @@ def run():
         vc.vc_attention(q, Or, beta=BETA, flags=vc.VC_F_EXPCAST)
         repeat_identical.append(bool(torch.equal(Or, O)))
         del Or
+    # one repeat of each other attention variant (exp-then-cast, plain FP8, E5M2 bytes)
+    for qq, ref, beta, flags, rm in ((q, Ovs, BETA, 0, True), (qp, Op, BETA, 0, False),
+                                     (q, O5, oracle.BETA_E5M2, vc.VC_F_EXPCAST | vc.VC_F_E5M2, True)):
+        Or = torch.empty_like(O)
+        vc.vc_attention(qq, Or, beta=beta, flags=flags, restore_mean=rm)
+        repeat_identical.append(bool(torch.equal(Or, ref)))
+        del Or
     # k-means (warm, from the same start) and the quantiser repeated as well
     C2 = Cw.clone()
     lab2, perm2 = torch.empty_like(lab), torch.empty_like(perm)
@@ -85,8 +92,9 @@ def run():
 
 
 def test_wan_attention_repeatable(run):
-    """Four more launches of the VC attention on the same inputs give the same bytes, and so
-    do a second warm k-means from the same centroids and a second quantiser call: every
+    """Four more launches of the VC attention on the same inputs give the same bytes, as do one
+    more launch of each other attention variant (exp-then-cast, plain FP8, E5M2 bytes), a second
+    warm k-means from the same centroids and a second quantiser call: every
     accumulation order is fixed, so any difference is a race (for attention, a tile stage
     copied over while another wave of the work-group still reads it)."""
     assert all(run["repeat_identical"]), run["repeat_identical"]
