@@ -59,6 +59,12 @@ struct Best {
   int k;
 };
 
+// exact distance (hi, lo) of a re-ranked token and its centroid index
+struct Exact {
+  double d, lo;
+  int k;
+};
+
 // Rigorous lower bound of d_k - e_k over every centroid whose computed distance' is >= x
 // (x = d2): with |c_k| <= |v| + sqrt(D_k) and D_k <= d_k + e_k + |v|^2, the bound
 // e_k <= F(e) = 2(2 gam |v| c(e) + u (c(e)^2 + |x|)), c(e) = |v| + sqrt(x + e + |v|^2),
@@ -109,9 +115,9 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   __shared__ float vn_s[kAssignTokens];
   __shared__ Best rec[kAssignTokens][4];
   __shared__ int unsure[kAssignTokens];
+  constexpr int RB = 64;  // uncertain tokens per re-rank batch
+  __shared__ Exact rr[RB][4];
   __shared__ int n_unsure;
-  __shared__ double red_d[256], red_lo[256];
-  __shared__ int red_k[256];
 
   const int bh = blockIdx.y, t0 = blockIdx.x * kAssignTokens;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -239,47 +245,82 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
     }
   }
   __syncthreads();
-  // exact re-rank (binary64) of the uncertain tokens, the whole group per token; with size
-  // penalties the distance is the exact pair (hi, lo) = TwoSum(s, b_k), ranked
-  // lexicographically (hi is the rounding of s + b_k, and rounding is monotone)
+  // exact re-rank (binary64) of the uncertain tokens, in batches of RB tokens with two
+  // barriers per batch: for each token the eight lanes of a lane group share one centroid
+  // row (D/8 features each, so a row is one coalesced read) and the work-group's 32 lane
+  // groups take centroids k = 32j + 8 wave + group. The partial sums are combined across the
+  // lane group, the groups' winners across the wave, and the four waves' winners through LDS.
+  // These sums of squared bf16 differences are exact in binary64 for inputs of moderate
+  // exponent span, so their order does not change them. With size penalties the distance is
+  // the exact pair (hi, lo) = TwoSum(s, b_k), ranked lexicographically (hi is the rounding
+  // of s + b_k, and rounding is monotone); ties go to the lowest index.
   const int nu = n_unsure;
   const int32_t* nkh = nk ? nk + (size_t)bh * K : nullptr;
-  for (int ui = 0; ui < nu; ui++) {
-    const int t = t0 + unsure[ui];
-    const uint16_t* vt = Vh + (size_t)t * D;
-    double best = __builtin_inf(), blo = 0.0;
-    int bk = 0x7fffffff;
-    for (int k = tid; k < K; k += 256) {
-      const uint16_t* ck = Ch + (size_t)k * D;
-      double s = 0.0;
-      for (int c = 0; c < D; c++) {
-        double df = (double)bf16_to_f32(vt[c]) - (double)bf16_to_f32(ck[c]);
-        s = fma(df, df, s);
+  constexpr int SL = D / 8;  // features per lane
+  const int sub = lane & 7, grp = lane >> 3;
+  auto load_slice = [&](const uint16_t* p, double* f) {
+    for (int q = 0; q < SL / 8; q++) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(p + 8 * q);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      for (int e = 0; e < 4; e++) {
+        f[8 * q + 2 * e] = (double)__uint_as_float(w[e] << 16);
+        f[8 * q + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
       }
-      double lo = 0.0;
-      if (nkh) {
-        const double b = (double)(lam * (float)nkh[k]);
-        const double hi = s + b, bb = hi - s;
-        lo = (s - (hi - bb)) + (b - bb);
-        s = hi;
-      }
-      if (s < best || (s == best && lo < blo)) { best = s; blo = lo; bk = k; }
     }
-    red_d[tid] = best;
-    red_lo[tid] = blo;
-    red_k[tid] = bk;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if (tid < o) {
-        const double d2 = red_d[tid + o], l2 = red_lo[tid + o];
-        const int k2 = red_k[tid + o];
-        if (d2 < red_d[tid] || (d2 == red_d[tid] && (l2 < red_lo[tid] || (l2 == red_lo[tid] && k2 < red_k[tid])))) {
-          red_d[tid] = d2; red_lo[tid] = l2; red_k[tid] = k2;
+  };
+  auto better = [](double d2, double l2, int k2, double d, double l, int k) {
+    return d2 < d || (d2 == d && (l2 < l || (l2 == l && k2 < k)));
+  };
+  for (int u0 = 0; u0 < nu; u0 += RB) {
+    const int nb = min(RB, nu - u0);
+    for (int j = 0; j < nb; j++) {
+      const int t = t0 + unsure[u0 + j];
+      double vf[SL];
+      load_slice(Vh + (size_t)t * D + sub * SL, vf);
+      double best = __builtin_inf(), blo = 0.0;
+      int bk = 0x7fffffff;
+      for (int kk = 0; kk < K; kk += 32) {
+        const int k = kk + 8 * wave + grp;
+        double s = 0.0;
+        if (k < K) {
+          double cf[SL];
+          load_slice(Ch + (size_t)k * D + sub * SL, cf);
+          for (int c = 0; c < SL; c++) {
+            const double df = vf[c] - cf[c];
+            s = fma(df, df, s);
+          }
+        }
+        // butterfly over the lane group: every lane of it ends with the same sum
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        if (k < K) {
+          double lo = 0.0;
+          if (nkh) {
+            const double b0 = (double)(lam * (float)nkh[k]);
+            const double hi = s + b0, bb = hi - s;
+            lo = (s - (hi - bb)) + (b0 - bb);
+            s = hi;
+          }
+          if (s < best || (s == best && lo < blo)) { best = s; blo = lo; bk = k; }
         }
       }
-      __syncthreads();
+      for (int o = 8; o < 64; o <<= 1) {
+        const double d2 = __shfl_xor(best, o), l2 = __shfl_xor(blo, o);
+        const int k2 = __shfl_xor(bk, o);
+        if (better(d2, l2, k2, best, blo, bk)) { best = d2; blo = l2; bk = k2; }
+      }
+      if (lane == 0) rr[j][wave] = Exact{best, blo, bk};
     }
-    if (tid == 0) labels[(size_t)bh * N + t] = ((unsigned)red_k[0] < (unsigned)K) ? red_k[0] : 0;
+    __syncthreads();
+    if (tid < nb) {
+      Exact a = rr[tid][0];
+      for (int w = 1; w < 4; w++) {
+        const Exact& o = rr[tid][w];
+        if (better(o.d, o.lo, o.k, a.d, a.lo, a.k)) a = o;
+      }
+      labels[(size_t)bh * N + t0 + unsure[u0 + tid]] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
+    }
     __syncthreads();
   }
 }
