@@ -231,6 +231,34 @@ def test_cluster_ties_duplicate_centroids():
     assert np.array_equal(C[0, 0], c_or)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_cluster_ties_reranked_in_batches(d):
+    """90 centroids in identical pairs (2i, 2i+1) and 10 single ones, tokens near them: a
+    token near a pair has an exact tie for its best distance and goes through the exact
+    re-rank, so every work-group re-ranks about 200 of its tokens, a count that is not a
+    multiple of the re-rank's batches (K = 100 is not a multiple of the centroids ranked per
+    step either; the last work-group holds 128 tokens). Tokens of a pair must get its even
+    index, as the oracle has it."""
+    B, H, N, NP, NS = 1, 2, 1152, 45, 10
+    K = 2 * NP + NS
+    rng = np.random.default_rng(21 + d)
+    base = (rng.integers(-6, 7, (B, H, NP + NS, d)) * 0.5).astype(np.float32)
+    C0 = np.concatenate([np.repeat(base[:, :, :NP], 2, axis=2), base[:, :, NP:]], axis=2)
+    pick = rng.integers(0, NP + NS, (B, H, N))
+    noise = (rng.integers(-1, 2, (B, H, N, d)) * 0.5).astype(np.float32)
+    noise *= rng.random((B, H, N, d)) < 0.1
+    Vf = np.take_along_axis(base, pick[..., None].repeat(d, -1), axis=2) + noise
+    V = synth.bf16_bits(Vf)
+    lab, perm, C = _gpu_cluster(V, K, 1, False, C0)
+    for h in range(H):
+        l_or, p_or, c_or = oracle.kmeans(V[0, h], K, 1, cold=False, C=C0[0, h])
+        paired = l_or < 2 * NP
+        assert np.all(l_or[paired] % 2 == 0) and 0.7 < paired.mean() < 0.9
+        assert np.array_equal(lab[0, h], l_or), (h, np.count_nonzero(lab[0, h] != l_or))
+        assert np.array_equal(perm[0, h], p_or)
+        assert np.array_equal(C[0, h], c_or)
+
+
 def _gpu_cluster_balanced(V, K, iters, cold, lam, counts, C0=None):
     B, H, N, d = V.shape
     C = torch.zeros((B, H, K, d), dtype=torch.float32, device="cuda") if C0 is None else to_dev(C0)
