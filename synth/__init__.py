@@ -20,6 +20,9 @@ which are not available):
   channels redrawn per head. ``V_prev`` is the previous denoising step's value
   tensor; ``V = bf16(V_prev + xi * |V_prev|)`` with xi ~ N(0, 0.05^2).
 * ``sweep``  -- the ``wan`` generator at other (H, N, d).
+* ``wan_tight`` -- B=1, H=2, N=70400, d=128: the ``wan`` recipe with tight value clusters
+  (centre norm sqrt(d), i.e. about one per element, noise std 0.25), a model of highly
+  redundant neighbouring video tokens; Q, K, outliers and drift as ``wan``.
 """
 from __future__ import annotations
 
@@ -57,13 +60,14 @@ def head_k_biased(seed, b, h, N, d):
     return bf16_bits(_normal(rng, (N, d)) + bias[None, :])
 
 
-def head_v_mixture(seed, b, h, N, d, n_centres, n_outliers, out_lo, out_hi, n_spike=8):
+def head_v_mixture(seed, b, h, N, d, n_centres, n_outliers, out_lo, out_hi, n_spike=8, centre_norm=4.0,
+                   noise=1.0):
     """Mixture of Gaussian centres with token outliers on a few spike channels."""
     rng = _rng(seed, TAG_V, b, h)
     g = _normal(rng, (n_centres, d))
-    centres = (4.0 * g / np.linalg.norm(g, axis=1, keepdims=True)).astype(np.float32)
+    centres = (centre_norm * g / np.linalg.norm(g, axis=1, keepdims=True)).astype(np.float32)
     z = rng.integers(0, n_centres, size=N)
-    V = centres[z] + _normal(rng, (N, d))
+    V = centres[z] + noise * _normal(rng, (N, d))
     toks = rng.choice(N, size=n_outliers, replace=False)
     chans = rng.choice(d, size=n_spike, replace=False)
     if out_lo == out_hi:
@@ -121,6 +125,7 @@ WORKLOADS = {
     "expcast": dict(seed=1, B=1, H=8, N=8192, d=128),
     "wan": dict(seed=2, B=1, H=40, N=70400, d=128, clusters=550, iters=2, cold=False),
     "schedule": dict(seed=3, B=1, H=40, N=70400, d=128, clusters=550, steps=20),
+    "wan_tight": dict(seed=5, B=1, H=2, N=70400, d=128, clusters=550, iters=2, cold=False),
 }
 SWEEP = [dict(seed=40 + i, B=1, H=24, N=n, d=128) for i, n in enumerate([16384, 32768, 65536, 131072])] + \
         [dict(seed=44, B=1, H=48, N=32768, d=64)]
@@ -144,6 +149,14 @@ def gen_head(kind: str, seed: int, b: int, h: int, N: int, d: int):
         K = head_k_biased(seed, b, h, N, d)
         n_out = int(round(0.01 * N))
         Vp, z, c, toks = head_v_mixture(seed, b, h, N, d, 64, n_out, 10.0, 30.0)
+        V = drift(Vp, seed, b, h, 0)
+        return dict(Q=Q, K=K, V=V, V_prev=Vp, z_true=z, centres=c, outliers=toks)
+    if kind == "wan_tight":
+        Q = head_q(seed, b, h, N, d)
+        K = head_k_biased(seed, b, h, N, d)
+        n_out = int(round(0.01 * N))
+        Vp, z, c, toks = head_v_mixture(seed, b, h, N, d, 64, n_out, 10.0, 30.0, centre_norm=float(np.sqrt(d)),
+                                        noise=0.25)
         V = drift(Vp, seed, b, h, 0)
         return dict(Q=Q, K=K, V=V, V_prev=Vp, z_true=z, centres=c, outliers=toks)
     raise ValueError(kind)

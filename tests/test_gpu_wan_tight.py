@@ -1,0 +1,74 @@
+"""Error of the VC path against plain FP8 on tight value clusters, at full Wan size.
+
+The workload is the Wan-shaped recipe with tight value clusters (``synth`` kind
+``wan_tight``: centre norm sqrt(d), noise std 0.25, the same outlier tokens and drift),
+a model of highly redundant neighbouring video tokens. There the tokens of a 128-token
+block share most of their value, block demeaning leaves a small residual, and the value
+term of the error shrinks by about half, so the VC output (V-Smooth + ExpCast) is closer
+to binary64 exact attention than plain FP8 (no V-Smooth, exp then cast), as the paper
+page's accuracy tables have it. The VC output is also checked against the oracle's
+emulation of the quantised pipeline (2e-3), on the GPU's own permutation.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+vc = pytest.importorskip("bit_attention_video_online_amd")
+from tests.gpu_util import bf16_bits, rel_l2, to_dev_bf16  # noqa: E402
+
+KC = 550
+BETA = oracle.BETA_E4M3
+
+
+@pytest.fixture(scope="module")
+def tight():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = synth.gen("wan_tight")
+    B, H, N, d = w["Q"].shape
+    print("\n[wan_tight] B=%d H=%d N=%d d=%d" % (B, H, N, d), flush=True)
+    Q, K, V, Vp = (to_dev_bf16(w[k]) for k in ("Q", "K", "V", "V_prev"))
+    C = torch.zeros((B, H, KC, d), dtype=torch.float32, device="cuda")
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    vc.vc_cluster(Vp, KC, 4, True, C, lab, perm)
+    vc.vc_cluster(V, KC, 2, False, C, lab, perm)
+    q = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(Q, K, V, perm, vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH, q)
+    O = torch.empty((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    vc.vc_attention(q, O, beta=BETA, flags=vc.VC_F_EXPCAST)
+    qp = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(Q, K, V, None, vc.VC_F_KSMOOTH, qp)
+    Op = torch.empty_like(O)
+    vc.vc_attention(qp, Op, beta=BETA, flags=0, restore_mean=False)
+    torch.cuda.synchronize()
+    print("[wan_tight] GPU path done", flush=True)
+    return dict(w=w, perm=perm.cpu().numpy(), O=bf16_bits(O), Op=bf16_bits(Op))
+
+
+def test_wan_tight_vc_below_plain_fp8(tight):
+    w = tight["w"]
+    N = w["Q"].shape[2]
+    rng = np.random.default_rng(77)
+    e_vc, e_plain = [], []
+    for h in range(w["Q"].shape[1]):
+        rows = np.sort(rng.choice(N, 64, replace=False)).astype(np.int32)
+        Qh, Kh, Vh = w["Q"][0, h], w["K"][0, h], w["V"][0, h]
+        Oex = oracle.attention_exact(Qh, Kh, Vh, rows)
+        O = synth.bf16_to_f32(tight["O"][0, h][rows]).astype(np.float64)
+        Op = synth.bf16_to_f32(tight["Op"][0, h][rows]).astype(np.float64)
+        e_vc.append(rel_l2(O, Oex))
+        e_plain.append(rel_l2(Op, Oex))
+        # parity of the VC output with the oracle's emulation on the GPU's permutation
+        o = oracle.quantize(Qh, Kh, Vh, tight["perm"][0, h], oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
+        em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+        err = rel_l2(O, em)
+        print("[wan_tight] head %d: VC %.3f%%  plain FP8 %.3f%%  VC vs emulation %.2e"
+              % (h, 100 * e_vc[-1], 100 * e_plain[-1], err), flush=True)
+        assert err <= 2e-3
+    assert np.mean(e_vc) < np.mean(e_plain)
