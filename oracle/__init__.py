@@ -64,7 +64,7 @@ def build(force: bool = False) -> str:
     """Compile vc_oracle.c into liboracle.so (gcc, OpenMP, no FP contraction)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+        cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
                "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
@@ -109,7 +109,11 @@ def lib() -> ctypes.CDLL:
         _lib.or_quantize_ex.argtypes = [P, P, P, P, P, P, I, I, I, F, P, P, P, P, P, P, P, P, P, P]
         _lib.or_rope.argtypes = [P, P, P, I, I, P]
         _lib.or_fwht_rows.argtypes = [P, I, I]
-        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P, P]
+        _lib.or_attention_emul.argtypes = [P, P, P, P, P, P, P, I, I, F, I, I, P, P, I, P, P, P, P, I]
+        _lib.or_mfma_f8_dot64.restype = F
+        _lib.or_mfma_f8_dot64.argtypes = [P, P, F]
+        _lib.or_mfma_f8_dot64_array.argtypes = [P, P, P, P, L]
+        _lib.or_bf16_from_f64_array.argtypes = [P, P, L]
         _lib.or_attention_exact.argtypes = [P, P, P, I, I, I, P, P]
         _lib.or_exact_mean.restype = ctypes.c_double
         _lib.or_exact_mean.argtypes = [P, L, I]
@@ -182,6 +186,26 @@ def expcast(acc, scale8, bias) -> np.ndarray:
     a, s, b = _c(acc, np.float32), _c(scale8, np.float32), _c(bias, np.float32)
     out = np.empty(a.shape, np.uint8)
     lib().or_expcast_array(_p(a), _p(s), _p(b), _p(out), a.size)
+    return out
+
+
+def mfma_f8_dot64(a, b, c) -> np.ndarray:
+    """D = C + sum_k a_k b_k per row, as gfx950's FP8 32x32x64 matrix-core instruction
+    accumulates it: a, b uint8 E4M3 codes [..., 64], c binary32 [...]."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    assert a.shape == b.shape and a.shape[-1] == 64
+    cc = _c(np.broadcast_to(np.asarray(c, np.float32), a.shape[:-1]), np.float32)
+    out = np.empty(a.shape[:-1], np.float32)
+    lib().or_mfma_f8_dot64_array(_p(a), _p(b), _p(cc), _p(out), out.size)
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """binary64 -> bfloat16 bit patterns, one rounding to nearest even."""
+    a = _c(x, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    lib().or_bf16_from_f64_array(_p(a), _p(out), a.size)
     return out
 
 
@@ -309,12 +333,19 @@ def quantize(Q_bits, K_bits, V_bits, perm=None, flags=FLAG_KSMOOTH | FLAG_VSMOOT
 
 # ---------------------------------------------------------------- attention
 def attention_emul(q: dict, rows, beta: float = -0.35, mode: int = MODE_EXPCAST, restore_mean: bool = True,
-                   dump_block: int = -1, want_m: bool = False, want_weights: bool = False):
+                   dump_block: int = -1, want_m: bool = False, want_weights: bool = False, score: str = "exact",
+                   out_bf16: bool = False):
     """Online-softmax emulation on the given query rows. Returns O [rows, d] (binary64)
     and, when dump_block >= 0, the probability bytes of that key block [rows, 128]; with
     want_m the running max after each key block [rows, N/128]; with want_weights the
     effective weight of every key in the output [rows, N] (keys in the quantised order):
-    the decoded probability times 2^(m'_j - m'_final) / l, binary64."""
+    the decoded probability times 2^(m'_j - m'_final) / l, binary64.
+
+    score: "exact" takes every score as fl32 of the exact dot product of the codes (the
+    plain definition); "gfx950" takes it in the precision of the gfx950 FP8 matrix core
+    (see or_mfma_f8_dot64 in vc_oracle.c), the precision the attention kernel decides
+    its bytes in. out_bf16 rounds O once to bfloat16 (nearest even), the output format,
+    and returns it as binary64 values."""
     rows = _c(rows, np.int32)
     N, d = q["Qq"].shape
     O = np.empty((rows.size, d), np.float64)
@@ -326,7 +357,10 @@ def attention_emul(q: dict, rows, beta: float = -0.35, mode: int = MODE_EXPCAST,
                             None if mu is None else _p(_c(mu, np.float32)), N, d, float(np.float32(beta)),
                             int(mode), rows.size, _p(rows), _p(O), int(dump_block),
                             None if dump is None else _p(dump), None if mm is None else _p(mm),
-                            None if W is None else _p(W), _p(q["Vs"]) if "Vs" in q else None)
+                            None if W is None else _p(W), _p(q["Vs"]) if "Vs" in q else None,
+                            {"exact": 0, "gfx950": 1}[score])
+    if out_bf16:
+        O = bf16_bits_to_f32(bf16_round(O)).astype(np.float64)
     res = [O]
     if dump is not None:
         res.append(dump)

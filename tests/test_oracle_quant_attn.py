@@ -134,3 +134,70 @@ def test_vsmooth_beats_plain_on_tiny_workload():
     e_plain, e_vs, e_vc = _rel_l2(O_plain, Oex), _rel_l2(O_vs, Oex), _rel_l2(O_vc, Oex)
     assert e_vs < e_plain
     assert e_vc < 0.1
+
+
+def _pow2_f32(u: np.float32) -> np.float32:
+    """fl32(2^u) for a binary32 u, from a 60-digit decimal evaluation (correctly rounded unless
+    2^u lies within 1e-50 relative of a binary32 midpoint)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    v = (Decimal(float(u)) * Decimal(2).ln()).exp()
+    return round_to_f32(Fraction(v))
+
+
+def _e4m3_nearest_even(x: Fraction) -> int:
+    """RNE of a nonnegative rational to an E4M3 code (saturating), by brute force over the table."""
+    best = None
+    for c in range(0x7F):
+        v = e4m3_value(c)
+        key = (abs(v - x), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def test_exp_then_cast_codes_rowsums_and_output_match_exact_recomputation():
+    """Exp-then-cast probabilities (the plain-FP8 and V-Smooth-only paths): for every key,
+    p = fl32(2^u) with u = fl32(fl32(sigma acc) - m'), byte = e4m3(256 p), and the row sum is
+    256 sum p while the values are weighted by the decoded bytes (study notes 2-3: the row
+    sum the kernel already keeps). Recomputed from scratch with decimals and rationals: every
+    byte equals the oracle's, and the output agrees to 1e-12 relative. An e-based
+    exponential, a different probability scale or a row sum taken from the bytes fails."""
+    rng = np.random.default_rng(33)
+    N, d = 256, 16
+    Q = synth.bf16_bits((rng.standard_normal((N, d)) * 2).astype(np.float32))
+    K = synth.bf16_bits((rng.standard_normal((N, d)) * 2).astype(np.float32))
+    V = synth.bf16_bits(rng.standard_normal((N, d)).astype(np.float32))
+    q = oracle.quantize(Q, K, V, None, oracle.FLAG_KSMOOTH)
+    rows = np.array([3, 130, 255], np.int32)
+    nb = N // 128
+    dec = {c: e4m3_value(c) for c in range(256) if (c & 0x7F) != 0x7F}
+    O_or = oracle.attention_emul(q, rows, mode=oracle.MODE_EXP_THEN_CAST, restore_mean=False)
+    dumps = [oracle.attention_emul(q, rows, mode=oracle.MODE_EXP_THEN_CAST, restore_mean=False, dump_block=j)[1]
+             for j in range(nb)]
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    for ri, i in enumerate(rows):
+        I = i // 128
+        m, A, l = None, [Fraction(0)] * d, Fraction(0)
+        for j in range(nb):
+            sigma = np.float32(q["sQ"][I] * q["sK"][j])
+            accs = [round_to_f32(sum(dec[int(q["Qq"][i, c])] * dec[int(q["Kq"][j * 128 + t, c])] for c in range(d)))
+                    for t in range(128)]
+            mnew = np.float32(sigma * max(accs))
+            mp = mnew if m is None else max(m, mnew)
+            alpha = Fraction(0) if m is None else Fraction((Decimal(float(m) - float(mp)) * Decimal(2).ln()).exp())
+            r, pv = Fraction(0), [Fraction(0)] * d
+            for t in range(128):
+                u = np.float32(np.float32(sigma * accs[t]) - mp)
+                P = _pow2_f32(u)
+                code = _e4m3_nearest_even(Fraction(float(np.float32(256.0) * P)))
+                assert dumps[j][ri, t] == code, (i, j, t)
+                r += 256 * Fraction(float(P))
+                for c in range(d):
+                    pv[c] += dec[code] * dec[int(q["Vq"][j * 128 + t, c])]
+            l = alpha * l + r
+            A = [alpha * a + x for a, x in zip(A, pv)]
+            m = mp
+        want = [float(Fraction(float(q["sV"][c])) * A[c] / l) for c in range(d)]
+        assert np.allclose(O_or[ri], want, rtol=1e-12, atol=1e-14 * max(abs(x) for x in want)), (i, O_or[ri], want)
