@@ -8,6 +8,7 @@ built, importing the functions raises.
 
 Entry points (same names as the C ABI):
   vc_cluster, vc_quantize, vc_attention, vc_attention_dump, vc_debug_expcast,
+  vc_debug_expcast_unclamped (as vc_debug_expcast(..., clamp=False)), vc_debug_mfma_f8,
   vc_cluster_workspace_bytes, vc_quantize_workspace_bytes, vc_mu_pack_size, vc_status_string.
 """
 from __future__ import annotations
@@ -77,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.vc_attention_dump.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, F, U, P, I, P, P]
         L.vc_debug_expcast.restype = I
         L.vc_debug_expcast.argtypes = [P, P, P, P, S, P]
+        L.vc_debug_expcast_unclamped.restype = I
+        L.vc_debug_expcast_unclamped.argtypes = [P, P, P, P, S, P]
+        L.vc_debug_mfma_f8.restype = I
+        L.vc_debug_mfma_f8.argtypes = [P, P, P, P, I, P]
         L.vc_debug_mfma_peak.restype = I
         L.vc_debug_mfma_peak.argtypes = [I, I, I, P, P]
         _lib = L
@@ -255,11 +260,26 @@ def vc_debug_mfma_peak(grid, iters, random_bits, out, stream=None):
     return out
 
 
-def vc_debug_expcast(acc, scale8, bias, codes, stream=None):
+def vc_debug_expcast(acc, scale8, bias, codes, stream=None, clamp=True):
+    """The attention kernel's ExpCast byte sequence elementwise: with clamp (default) its
+    clamped path (vc_debug_expcast), else its unclamped path (vc_debug_expcast_unclamped)."""
     n = acc.numel()
     for t, name in ((acc, "acc"), (scale8, "scale8"), (bias, "bias")):
         _need(t, torch.float32, tuple(acc.shape), name)
     _need(codes, torch.uint8, tuple(acc.shape), "codes")
-    st = lib().vc_debug_expcast(_ptr(acc), _ptr(scale8), _ptr(bias), _ptr(codes), n, _stream(stream))
+    fn = lib().vc_debug_expcast if clamp else lib().vc_debug_expcast_unclamped
+    st = fn(_ptr(acc), _ptr(scale8), _ptr(bias), _ptr(codes), n, _stream(stream))
     _check(st)
     return codes
+
+
+def vc_debug_mfma_f8(A, B, C, D, stream=None):
+    """D = C + A B^T per 32x32x64 tile on the attention kernel's FP8 matrix-core instruction:
+    A, B uint8 [n, 32, 64], C, D float32 [n, 32, 32] on the device."""
+    n = int(A.shape[0])
+    _need(A, torch.uint8, (n, 32, 64), "A")
+    _need(B, torch.uint8, (n, 32, 64), "B")
+    _need(C, torch.float32, (n, 32, 32), "C")
+    _need(D, torch.float32, (n, 32, 32), "D")
+    _check(lib().vc_debug_mfma_f8(_ptr(A), _ptr(B), _ptr(C), _ptr(D), n, _stream(stream)))
+    return D

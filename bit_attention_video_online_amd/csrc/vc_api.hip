@@ -1,6 +1,7 @@
-// vc_api.hip -- the C ABI declared in include/vc.h: argument validation on the host,
-// then asynchronous launches on the caller's stream. Nothing here allocates,
-// synchronises or keeps state.
+// vc_api.hip -- the C ABI declared in include/vc.h: argument validation on the host, a check
+// that the current device is a gfx950, then asynchronous launches on the caller's stream.
+// Nothing here allocates or synchronises; the only state is a per-device record of the
+// architecture check.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -22,7 +23,9 @@ extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uin
                                    float beta, int pmode, int mx, uint16_t* O, int dump_block, uint8_t* dump,
                                    hipStream_t st);
 extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
-                                 hipStream_t st);
+                                 int clamp, hipStream_t st);
+extern "C" int vc_launch_mfma_f8_tiles(const uint8_t* A, const uint8_t* B, const float* C, float* D, int n,
+                                       hipStream_t st);
 extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
 extern "C" int vc_launch_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold, float* C,
                                  int32_t* labels, int32_t* perm, void* ws, hipStream_t st, float lam, int32_t* nk_io);
@@ -57,6 +60,26 @@ struct Range {
 bool overlaps(Range x, Range y) {
   if (!x.a || !y.a || x.n == 0 || y.n == 0) return false;
   return x.a < y.a + y.n && y.a < x.a + x.n;
+}
+
+// The current device must be a gfx950 (the kernels are built for it alone). The answer is
+// kept per device ordinal; concurrent first calls may both query, and write the same value.
+vc_status device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();  // leave no sticky error behind for the caller
+    return VC_E_UNSUPPORTED;
+  }
+  static int known[64];  // 0 unknown, 1 gfx950, 2 other
+  if (dev < 64 && known[dev]) return known[dev] == 1 ? VC_OK : VC_E_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return VC_E_UNSUPPORTED;
+  }
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) known[dev] = ok ? 1 : 2;
+  return ok ? VC_OK : VC_E_UNSUPPORTED;
 }
 
 }  // namespace
@@ -96,6 +119,7 @@ extern "C" vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K
   if (overlaps(in, {(const char*)centroids, (size_t)B * H * K * d * 4}) || overlaps(in, {(const char*)labels, el * 4}) ||
       overlaps(in, {(const char*)perm, el * 4}) || overlaps({(const char*)labels, el * 4}, {(const char*)perm, el * 4}))
     return VC_E_ALIAS;
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
                         (hipStream_t)stream, 0.0f, nullptr) != 0)
     return VC_E_HIP;
@@ -123,6 +147,7 @@ extern "C" vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int
     for (int j = i + 1; j < 5; j++)
       if (overlaps(outs[i], outs[j])) return VC_E_ALIAS;
   }
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
                         (hipStream_t)stream, lambda, counts) != 0)
     return VC_E_HIP;
@@ -151,6 +176,7 @@ extern "C" vc_status vc_cluster_cost(const void* V, const float* centroids, cons
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_cluster_cost(V, centroids, labels, B, H, N, d, K, cost, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
@@ -191,6 +217,7 @@ static vc_status quantize_common(const void* Q, const void* K, const void* V, co
   for (const Range& o : outs)
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_quantize(Q, K, V, perm, rope_cos, rope_sin, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK,
                          Vq, sV, mu, mu_scaled, mu_pack, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
@@ -238,6 +265,7 @@ static vc_status attention_common(const uint8_t* Qq, const float* sQ, const uint
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (overlaps(outs[0], outs[1])) return VC_E_ALIAS;
   const int pmode = (flags & VC_F_EXPCAST) ? ((flags & VC_F_E5M2) ? 2 : 1) : 0;
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_attention(Qq, sQ, Kq, sK, Vq, sV, mu_pack, B, H, N, d, beta, pmode, (flags & VC_F_MXFP4) ? 1 : 0,
                           (uint16_t*)O, dump_block, codes, (hipStream_t)stream) != 0)
     return VC_E_HIP;
@@ -263,14 +291,43 @@ extern "C" vc_status vc_attention_dump(const uint8_t* Qq, const float* sQ, const
 extern "C" vc_status vc_debug_mfma_peak(int grid, int iters, int random_bits, float* out, void* stream) {
   if (!out) return VC_E_NULLPTR;
   if (grid < 1 || iters < 1) return VC_E_PARAM;
+  if (const vc_status dc = device_check()) return dc;
   if (vc_launch_mfma_peak(grid, iters, random_bits ? 1 : 0, out, (hipStream_t)stream) != 0) return VC_E_HIP;
+  return VC_OK;
+}
+
+static vc_status debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes, size_t n,
+                               int clamp, void* stream) {
+  if (n == 0) return VC_OK;
+  if (!acc || !scale8 || !bias || !codes) return VC_E_NULLPTR;
+  if (n > ((size_t)1 << 34)) return VC_E_PARAM;
+  if (const vc_status dc = device_check()) return dc;
+  if (vc_launch_expcast(acc, scale8, bias, codes, n, clamp, (hipStream_t)stream) != 0) return VC_E_HIP;
   return VC_OK;
 }
 
 extern "C" vc_status vc_debug_expcast(const float* acc, const float* scale8, const float* bias, uint8_t* codes, size_t n,
                                       void* stream) {
-  if (n == 0) return VC_OK;
-  if (!acc || !scale8 || !bias || !codes) return VC_E_NULLPTR;
-  if (vc_launch_expcast(acc, scale8, bias, codes, n, (hipStream_t)stream) != 0) return VC_E_HIP;
+  return debug_expcast(acc, scale8, bias, codes, n, 1, stream);
+}
+
+extern "C" vc_status vc_debug_expcast_unclamped(const float* acc, const float* scale8, const float* bias,
+                                                uint8_t* codes, size_t n, void* stream) {
+  return debug_expcast(acc, scale8, bias, codes, n, 0, stream);
+}
+
+extern "C" vc_status vc_debug_mfma_f8(const uint8_t* A, const uint8_t* B, const float* C, float* D, int ntiles,
+                                      void* stream) {
+  if (ntiles == 0) return VC_OK;
+  if (!A || !B || !C || !D) return VC_E_NULLPTR;
+  if (ntiles < 0 || ntiles > (1 << 20)) return VC_E_PARAM;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D)) return VC_E_UNSUPPORTED;
+  const size_t n = (size_t)ntiles;
+  const Range outs{(const char*)D, n * 4096};
+  if (overlaps(outs, {(const char*)A, n * 2048}) || overlaps(outs, {(const char*)B, n * 2048}) ||
+      overlaps(outs, {(const char*)C, n * 4096}))
+    return VC_E_ALIAS;
+  if (const vc_status dc = device_check()) return dc;
+  if (vc_launch_mfma_f8_tiles(A, B, C, D, ntiles, (hipStream_t)stream) != 0) return VC_E_HIP;
   return VC_OK;
 }

@@ -24,14 +24,6 @@ constexpr int kWaves = 4;                 // waves per work-group (32 query rows
 constexpr int kAThreads = 64 * kWaves;
 constexpr int kQB = kWaves / 4;           // 128-row query blocks per work-group
 
-// per-byte min(b, 120) of a packed dword (two bytes per 16-bit half at a time)
-__device__ __forceinline__ uint32_t bytes_min120(uint32_t w) {
-  uint32_t lo = w & 0x00ff00ffu, hi = (w >> 8) & 0x00ff00ffu;
-  lo = min(lo & 0xffffu, 120u) | (min(lo >> 16, 120u) << 16);
-  hi = min(hi & 0xffffu, 120u) | (min(hi >> 16, 120u) << 16);
-  return lo | (hi << 8);
-}
-
 // lanes l and l^32 hold the same query: combine them with one v_permlane32_swap
 __device__ __forceinline__ float lane_max2(float v) {
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -412,12 +404,9 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     v8i pf[2];
     float r = 0.0f;
     v4f rs;
-    // ExpCast bytes: cvt_pk_u8_f32 rounds half-even and saturates to [0, 255] (NaN -> 0), so
-    // clamp(rne(t), 0, 120) = min(cvt(t), 120). For |m'| < 2^16 every t = fma(S, SLOPE sigma,
-    // bias) stays below 120.5 (for either slope, C0 <= 120 and the roundings of m' and of the
-    // bias add less than 0.05) and the min is idle; otherwise (uniform per wave, rare) a packed
-    // per-byte min fixes the operand before its MFMAs read it.
-    const bool fix = EXPCAST && __ballot(fabsf(mp) >= 65536.0f);
+    // ExpCast bytes (the helpers in vc_device.h): FMA, cvt_pk_u8_f32, and the per-byte min with
+    // 120 only when some byte can exceed it (beta above ~0.45, or |m'| >= 2^16; uniform per wave)
+    const bool fix = EXPCAST && __ballot(expcast_needs_clamp(C0, mp));
     auto bytes_half = [&](int kh) {
       if (EXPCAST) {
         // All 32 FMAs of the half first (in place: the accumulators are dead afterwards),
@@ -427,14 +416,15 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
         const float bias = C0 - SLOPE * mp;
         const float s8 = SLOPE * sigma;
         for (int kb = 2 * kh; kb < 2 * kh + 2; kb++)
-          for (int i = 0; i < 16; i++) sacc[kb][i] = __builtin_fmaf(sacc[kb][i], s8, bias);
+          for (int i = 0; i < 16; i++) sacc[kb][i] = expcast_t(sacc[kb][i], s8, bias);
         uint32_t w[8];
-        for (int k = 0; k < 8; k++) w[k] = __builtin_amdgcn_cvt_pk_u8_f32(sacc[2 * kh + (k >> 2)][4 * (k & 3)], 0, 0u);
-        for (int b = 1; b < 4; b++)
-          for (int k = 0; k < 8; k++) w[k] = __builtin_amdgcn_cvt_pk_u8_f32(sacc[2 * kh + (k >> 2)][4 * (k & 3) + b], b, w[k]);
+        for (int k = 0; k < 8; k++) w[k] = expcast_cvt<0>(sacc[2 * kh + (k >> 2)][4 * (k & 3)], 0u);
+        for (int k = 0; k < 8; k++) w[k] = expcast_cvt<1>(sacc[2 * kh + (k >> 2)][4 * (k & 3) + 1], w[k]);
+        for (int k = 0; k < 8; k++) w[k] = expcast_cvt<2>(sacc[2 * kh + (k >> 2)][4 * (k & 3) + 2], w[k]);
+        for (int k = 0; k < 8; k++) w[k] = expcast_cvt<3>(sacc[2 * kh + (k >> 2)][4 * (k & 3) + 3], w[k]);
         for (int k = 0; k < 8; k++) pf[kh][k] = (int)w[k];
         if (fix)
-          for (int k = 0; k < 8; k++) pf[kh][k] = (int)bytes_min120((uint32_t)pf[kh][k]);
+          for (int k = 0; k < 8; k++) pf[kh][k] = (int)expcast_min120((uint32_t)pf[kh][k]);
         return;
       }
       // exp-then-cast
@@ -515,10 +505,23 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     }
 }
 
+// The hot loop's byte sequence on elementwise inputs, four per thread (one packed dword, as
+// the kernel forms them): FMA, cvt_pk_u8_f32 into byte 0..3, then the per-byte min with 120
+// when `clamp` (the kernel's rare path) -- without it, inputs must keep every FMA result
+// below 120.5, as the kernel guarantees before it skips the min.
 __global__ void expcast_kernel(const float* __restrict__ acc, const float* __restrict__ s8, const float* __restrict__ bias,
-                               uint8_t* __restrict__ out, size_t n) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) out[i] = (uint8_t)expcast_byte(acc[i], s8[i], bias[i], 0u, 0);
+                               uint8_t* __restrict__ out, size_t n, int clamp) {
+  const size_t i0 = 4 * ((size_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i0 >= n) return;
+  float t[4];
+  for (int e = 0; e < 4; e++) t[e] = i0 + e < n ? expcast_t(acc[i0 + e], s8[i0 + e], bias[i0 + e]) : 0.0f;
+  uint32_t w = expcast_cvt<0>(t[0], 0u);
+  w = expcast_cvt<1>(t[1], w);
+  w = expcast_cvt<2>(t[2], w);
+  w = expcast_cvt<3>(t[3], w);
+  if (clamp) w = expcast_min120(w);
+  for (int e = 0; e < 4; e++)
+    if (i0 + e < n) out[i0 + e] = (uint8_t)(w >> (8 * e));
 }
 
 template <int D, int PM, bool R, bool DU, bool MX>
@@ -574,9 +577,9 @@ extern "C" int vc_launch_attention(const uint8_t* Qq, const float* sQ, const uin
 }
 
 extern "C" int vc_launch_expcast(const float* acc, const float* s8, const float* bias, uint8_t* out, size_t n,
-                                 hipStream_t st) {
+                                 int clamp, hipStream_t st) {
   if (n == 0) return 0;
-  const size_t blocks = (n + 255) / 256;
-  expcast_kernel<<<(unsigned)blocks, 256, 0, st>>>(acc, s8, bias, out, n);
+  const size_t blocks = (n + 1023) / 1024;   // 256 threads x 4 elements
+  expcast_kernel<<<(unsigned)blocks, 256, 0, st>>>(acc, s8, bias, out, n, clamp);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -70,24 +70,36 @@ __device__ __forceinline__ uint32_t e4m3x4_from_f32(float a, float b, float c, f
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// ExpCast-FP8 byte (paper page, method step (4)): the score enters as the raw
-// accumulator; t = fma(acc, 8*sigma, fl32(fl32(120+beta) - 8 m')) is one binary32
-// FMA, then round half to even and clamp to [0, 120]. med3 clamps in the float
-// domain (clamping to integer bounds commutes with rounding) and cvt_pk_u8_f32
-// rounds to nearest even; the byte lands in position `sel` of `old`.
-// The FMA is written as the instruction itself: the attention kernel also evaluates the
-// same FMA on its unclamped fast path, and an opaque instruction keeps the compiler from
-// hoisting both into one shared set of 32 live temporaries.
-__device__ __forceinline__ uint32_t expcast_byte(float acc, float scale8, float bias, uint32_t old, int sel) {
-  float t;
-  asm("v_fma_f32 %0, %1, %2, %3" : "=v"(t) : "v"(acc), "v"(scale8), "v"(bias));
-  t = __builtin_amdgcn_fmed3f(t, 0.0f, 120.0f);
-  switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_pk_u8_f32(t, 0, old);
-    case 1: return __builtin_amdgcn_cvt_pk_u8_f32(t, 1, old);
-    case 2: return __builtin_amdgcn_cvt_pk_u8_f32(t, 2, old);
-    default: return __builtin_amdgcn_cvt_pk_u8_f32(t, 3, old);
-  }
+// ExpCast-FP8 bytes (paper page, method step (4)), the exact instruction sequence of the
+// attention kernel's hot loop; the elementwise test entry points run these same helpers.
+//   t = fma(acc, slope * sigma, fl32(fl32(120 + beta) - slope * m')): one binary32 FMA on the
+//       raw score accumulator (slope 8 for E4M3 bytes, 4 for E5M2);
+//   byte = cvt_pk_u8_f32(t): round half to even, saturate to [0, 255] (NaN -> 0); four
+//       bytes are packed into one dword, byte `sel` replacing that byte of `w`;
+//   clamp: a packed per-byte min with 120. It is needed only when some t can reach 120.5,
+//       i.e. when fl32(120 + beta) > 120 or |m'| >= 2^16 (the kernel tests this per wave and
+//       per key block); below that every byte is already <= 120 and the min is idle.
+// Together: clamp(rne(t), 0, 120), since clamping to integer bounds commutes with rounding.
+__device__ __forceinline__ float expcast_t(float acc, float slope_sigma, float bias) {
+  return __builtin_fmaf(acc, slope_sigma, bias);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t expcast_cvt(float t, uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(t, SEL, w);
+}
+__device__ __forceinline__ uint32_t expcast_min120(uint32_t w) {  // per-byte min(b, 120)
+  uint32_t lo = w & 0x00ff00ffu, hi = (w >> 8) & 0x00ff00ffu;
+  lo = min(lo & 0xffffu, 120u) | (min(lo >> 16, 120u) << 16);
+  hi = min(hi & 0xffffu, 120u) | (min(hi >> 16, 120u) << 16);
+  return lo | (hi << 8);
+}
+// whether the clamp must run: C0 = fl32(120 + beta), mp the running maximum m' (wave-uniform
+// in the kernel). For C0 <= 120 and |m'| < 2^16, t = fma(S, slope sigma, fl32(C0 - slope m'))
+// stays below 120.5: S <= max S and m' >= fl32(sigma max S), so slope (sigma S - m') <=
+// slope 2^-24 |m'| <= 2^-5 (slope <= 8); fl32(C0 - slope m') is off by at most half an ulp of
+// a value below 2^19 + 120, i.e. 2^-5; the FMA's own rounding is below 2^-17.
+__device__ __forceinline__ bool expcast_needs_clamp(float C0, float mp) {
+  return C0 > 120.0f || fabsf(mp) >= 65536.0f;
 }
 
 // Work-group index remap so that consecutive logical tiles share an XCD: the

@@ -38,9 +38,39 @@ __global__ __launch_bounds__(256) void mfma_peak(int iters, int random_bits, flo
   out[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// The matrix-core instruction of the attention kernel's score and PV products on caller
+// operands, one 32x32x64 tile per wave: D = C + A B^T with A [32 rows][64] and B [32 columns]
+// [64] E4M3 codes (both row-major, K fastest) and C, D [32][32] binary32 row-major. Lane l
+// supplies row / column l % 32 and K bytes [32 (l / 32), +32) of A and B -- the operand layout
+// attn_fwd uses (keys as A rows, queries as B columns) -- and holds accumulator element i at
+// row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32.
+__global__ __launch_bounds__(256) void mfma_f8_tiles(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                                     const float* __restrict__ C, float* __restrict__ D, int n) {
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= n) return;
+  const int l = threadIdx.x & 63, r = l & 31, h = l >> 5;
+  const uint4* pa = reinterpret_cast<const uint4*>(A + (size_t)w * 2048 + r * 64 + 32 * h);
+  const uint4* pb = reinterpret_cast<const uint4*>(B + (size_t)w * 2048 + r * 64 + 32 * h);
+  const uint4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  v8i a, b;
+  a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+  b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+  v16f c;
+  for (int i = 0; i < 16; i++) c[i] = C[(size_t)w * 1024 + (8 * (i >> 2) + 4 * h + (i & 3)) * 32 + r];
+  const v16f d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  for (int i = 0; i < 16; i++) D[(size_t)w * 1024 + (8 * (i >> 2) + 4 * h + (i & 3)) * 32 + r] = d[i];
+}
+
 }  // namespace vc
 
 using namespace vc;
+
+extern "C" int vc_launch_mfma_f8_tiles(const uint8_t* A, const uint8_t* B, const float* C, float* D, int n,
+                                       hipStream_t st) {
+  if (n <= 0) return 0;
+  mfma_f8_tiles<<<(n + 3) / 4, 256, 0, st>>>(A, B, C, D, n);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
 
 extern "C" int vc_launch_mfma_peak(int grid, int iters, int random_bits, float* out, hipStream_t st) {
   mfma_peak<<<grid, 256, 0, st>>>(iters, random_bits, out);

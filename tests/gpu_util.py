@@ -4,6 +4,17 @@ import numpy as np
 import torch
 
 import bit_attention_video_online_amd as vc
+import oracle
+
+# The parity contract for the attention output: the oracle's emulation with every score taken in
+# the precision of the gfx950 FP8 matrix core (the precision the kernel decides its bytes in) and
+# the output rounded once to bfloat16 (the output format).
+PARITY = dict(score="gfx950", out_bf16=True)
+
+
+def emul(q_or, rows, **kw):
+    """oracle.attention_emul under the parity contract."""
+    return oracle.attention_emul(q_or, rows, **PARITY, **kw)
 
 
 def to_dev_bf16(bits: np.ndarray) -> torch.Tensor:

@@ -177,3 +177,30 @@ def test_debug_mfma_peak_rejects_bad_sizes(L):
     assert L.vc_debug_mfma_peak(1, 1, 0, None, None) == 1
     assert L.vc_debug_mfma_peak(0, 1, 0, ctypes.c_void_p(1 << 20), None) == 3
     assert L.vc_debug_mfma_peak(1, 0, 0, ctypes.c_void_p(1 << 20), None) == 3
+
+
+def test_debug_expcast_unclamped_and_mfma_tiles_reject_bad_arguments(L):
+    assert L.vc_debug_expcast_unclamped(None, None, None, None, 0, None) == 0
+    assert L.vc_debug_expcast_unclamped(None, None, None, None, 5, None) == 1
+    A, B, C, D = (ctypes.c_void_p(k << 20) for k in (1, 2, 3, 4))
+    assert L.vc_debug_mfma_f8(None, None, None, None, 0, None) == 0
+    assert L.vc_debug_mfma_f8(None, B, C, D, 1, None) == 1
+    assert L.vc_debug_mfma_f8(A, B, C, D, -1, None) == 3
+    assert L.vc_debug_mfma_f8(A, B, C, D, (1 << 20) + 1, None) == 3
+    assert L.vc_debug_mfma_f8(A, B, C, ctypes.c_void_p((4 << 20) + 4), 1, None) == 5
+    assert L.vc_debug_mfma_f8(A, B, C, ctypes.c_void_p((3 << 20) + 1024), 1, None) == 7   # D inside C
+
+
+def test_valid_calls_need_a_gfx950_device(L):
+    """After validation every entry point that would launch checks the current device: with no
+    GPU present, valid arguments give VC_E_UNSUPPORTED and nothing runs (this host check is
+    skipped where a GPU exists, since there it would launch on the placeholder pointers)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _quant(L) == 5
+    assert _attn(L) == 5
+    A, B, C, D = (ctypes.c_void_p(k << 20) for k in (1, 2, 3, 4))
+    assert L.vc_debug_mfma_f8(A, B, C, D, 1, None) == 5
+    assert L.vc_debug_expcast(A, B, C, D, 4, None) == 5
+    assert L.vc_debug_mfma_peak(1, 1, 0, ctypes.c_void_p(1 << 20), None) == 5

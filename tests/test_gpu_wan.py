@@ -4,7 +4,8 @@ in the launch configuration that bench.py times.
 The GPU runs the whole batch; the oracle recomputes two sampled heads completely
 (k-means warm start and both iterations, quantiser) and 64 query rows per sampled head
 for attention (rows are independent given K and V). Properties that hold at any size
-(pi is a stable sort of the labels) are checked on every head. The error of the VC path
+(pi is a stable sort of the labels) are checked on every head. In-kernel ExpCast bytes of the
+first and the last key block are bit-exact on sampled rows. The error of the VC path
 against binary64 exact attention is compared with the plain FP8 path.
 """
 import time
@@ -19,7 +20,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 vc = pytest.importorskip("bit_attention_video_online_amd")
-from tests.gpu_util import bf16_bits, mu_pack_expected, rel_l2, to_dev_bf16, vq_rowmajor  # noqa: E402
+from tests.gpu_util import bf16_bits, emul, mu_pack_expected, rel_l2, to_dev_bf16, vq_rowmajor  # noqa: E402
 
 HEADS = (0, 23)
 KC = 550
@@ -54,6 +55,15 @@ def run():
     vc.vc_attention(qp, Op, beta=BETA, flags=0, restore_mean=False)
     Oe = torch.empty_like(O)
     vc.vc_attention(qp, Oe, beta=BETA, flags=vc.VC_F_EXPCAST, restore_mean=False)
+    dumps = {}
+    codes = torch.empty((B, H, N, 128), dtype=torch.uint8, device="cuda")
+    for blk in (0, N // 128 - 1):
+        Od = torch.empty_like(O)
+        vc.vc_attention_dump(q, Od, blk, codes, beta=BETA, flags=vc.VC_F_EXPCAST)
+        torch.cuda.synchronize()
+        dumps[blk] = (codes[:, list(HEADS)].cpu().numpy(), bool(torch.equal(Od, O)))
+        del Od
+    del codes
     O5 = torch.empty_like(O)  # the VC path with E5M2 ExpCast bytes
     vc.vc_attention(q, O5, beta=oracle.BETA_E5M2, flags=vc.VC_F_EXPCAST | vc.VC_F_E5M2)
     # the same launch repeated on the same inputs: any race between the waves of a
@@ -85,7 +95,7 @@ def run():
     res = dict(w=w, Cw=Cw.cpu().numpy(), C=C.cpu().numpy(), lab=lab.cpu().numpy(), perm=perm.cpu().numpy(),
                q={k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in q.items()},
                O=bf16_bits(O), Ovs=bf16_bits(Ovs), Op=bf16_bits(Op), Oe=bf16_bits(Oe), O5=bf16_bits(O5),
-               repeat_identical=repeat_identical)
+               repeat_identical=repeat_identical, dumps=dumps)
     del Q, K, V, Vp, q, qp, O, Op, Ovs, Oe, O5
     torch.cuda.empty_cache()
     return res
@@ -190,37 +200,66 @@ def test_wan_quantize_bitexact_sampled_heads(run, oracle_heads):
         assert np.array_equal(g["mu_pack"][0, h], mu_pack_expected(o["mu_scaled"]))
 
 
-def test_wan_attention_sampled_rows(run, oracle_heads):
-    """Output within rel-L2 2e-3 of the emulation; error vs binary64 exact attention per path.
-
-    V-Smooth must lower the error of the path it is added to (same probability quantiser
-    on both sides). On this synthetic workload the FP8 score error dominates, and
-    ExpCast's approximation costs about as much as V-Smooth saves; the VC-vs-plain
-    figure is printed and recorded, not asserted."""
+@pytest.fixture(scope="module")
+def sampled_errors(run, oracle_heads):
+    """Output of every path on 64 seeded rows of the sampled heads: against the emulation, and
+    against binary64 exact attention (rMSE = ||O - O_exact|| / ||O_exact||)."""
     w = run["w"]
     N = w["Q"].shape[2]
     rng = np.random.default_rng(77)
-    errs, errs5 = [], []
+    errs, errs5, errs_x = [], [], []
     e = {k: [] for k in ("vc", "vsmooth", "plain", "expcast", "vc_e5m2")}
     for h in HEADS:
         rows = np.sort(rng.choice(N, 64, replace=False)).astype(np.int32)
-        O_em = oracle.attention_emul(oracle_heads[h]["q"], rows, beta=BETA, mode=oracle.MODE_EXPCAST)
-        O_em5 = oracle.attention_emul(oracle_heads[h]["q"], rows, beta=oracle.BETA_E5M2,
-                                      mode=oracle.MODE_EXPCAST_E5M2)
         got = lambda key: synth.bf16_to_f32(run[key][0, h][rows]).astype(np.float64)
-        errs.append(rel_l2(got("O"), O_em))
-        errs5.append(rel_l2(got("O5"), O_em5))
+        errs.append(rel_l2(got("O"), emul(oracle_heads[h]["q"], rows, beta=BETA, mode=oracle.MODE_EXPCAST)))
+        errs5.append(rel_l2(got("O5"), emul(oracle_heads[h]["q"], rows, beta=oracle.BETA_E5M2,
+                                              mode=oracle.MODE_EXPCAST_E5M2)))
+        errs_x.append(rel_l2(got("O"), oracle.attention_emul(oracle_heads[h]["q"], rows, beta=BETA,
+                                                              mode=oracle.MODE_EXPCAST)))
         O_ex = oracle.attention_exact(w["Q"][0, h], w["K"][0, h], w["V"][0, h], rows)
         for k, key in (("vc", "O"), ("vsmooth", "Ovs"), ("plain", "Op"), ("expcast", "Oe"), ("vc_e5m2", "O5")):
             e[k].append(rel_l2(got(key), O_ex))
     m = {k: float(np.mean(v)) for k, v in e.items()}
-    print("[wan] rel-L2 vs emulation %s (E5M2 %s); rMSE vs exact %s" % (errs, errs5, m), flush=True)
-    assert max(errs) <= 2e-3
-    # E5M2 bytes: one code step is 2^(1/4), so a byte moved by the matrix core's score
-    # rounding weighs (2^(1/4) - 1) / (2^(1/8) - 1) = 2.09 times as much as with E4M3
-    assert max(errs5) <= 2e-3 * (2 ** 0.25 - 1) / (2 ** 0.125 - 1)
-    assert m["vsmooth"] < m["plain"]
-    assert m["vc"] < m["expcast"]
+    print("[wan] rel-L2 vs emulation %s (E5M2 %s; exactly rounded scores, unrounded output %s); rMSE vs exact %s"
+          % (errs, errs5, errs_x, m), flush=True)
+    return dict(errs=errs, errs5=errs5, rmse=m)
+
+
+def test_wan_attention_sampled_rows(sampled_errors):
+    """Output within rel-L2 2e-3 of the emulation for E4M3 and E5M2 bytes; V-Smooth lowers the
+    error of each probability quantiser it is added to."""
+    s = sampled_errors
+    assert max(s["errs"]) <= 2e-3
+    assert max(s["errs5"]) <= 2e-3
+    assert s["rmse"]["vsmooth"] < s["rmse"]["plain"]
+    assert s["rmse"]["vc"] < s["rmse"]["expcast"]
+
+
+@pytest.mark.xfail(reason="on this generator (64 value centres of norm 4 under per-element noise of std 1, so a "
+                          "128-token block shares little of its value) the probability term dominates the error and "
+                          "ExpCast's code costs about as much as V-Smooth saves: VC 0.852 %, plain FP8 0.836 % "
+                          "measured (64 rows x 2 heads); with tight value clusters VC is below plain FP8 "
+                          "(test_gpu_wan_tight)", strict=False)
+def test_wan_vc_error_below_plain_fp8(sampled_errors):
+    """The VC path (V-Smooth + ExpCast) against plain FP8 (exp then cast, no V-Smooth), error
+    against binary64 exact attention on the sampled rows."""
+    m = sampled_errors["rmse"]
+    assert m["vc"] < m["plain"], (m["vc"], m["plain"])
+
+
+def test_wan_inkernel_bytes_first_and_last_block(run, oracle_heads):
+    """ExpCast bytes inside the attention loop at full size, key blocks 0 and 549 (after the
+    running maximum has evolved over all of them), 128 sampled rows of two heads: bit-exact."""
+    N = run["w"]["Q"].shape[2]
+    rng = np.random.default_rng(81)
+    for blk, (codes, same_output) in run["dumps"].items():
+        assert same_output
+        for i, h in enumerate(HEADS):
+            rows = np.sort(rng.choice(N, 128, replace=False)).astype(np.int32)
+            _, c_or = emul(oracle_heads[h]["q"], rows, beta=BETA, mode=oracle.MODE_EXPCAST, dump_block=blk)
+            got = codes[0, i][rows]
+            assert np.array_equal(got, c_or), (blk, h, np.count_nonzero(got != c_or))
 
 
 def test_wan_every_head_bitexact_and_rows(run):
@@ -245,7 +284,7 @@ def test_wan_every_head_bitexact_and_rows(run):
             assert np.array_equal(g[k][0, h], o[k]), (h, k)
         assert np.array_equal(vq_rowmajor(g["Vq"])[0, h], o["Vq"]), h
         rows = np.sort(rng.choice(N, 32, replace=False)).astype(np.int32)
-        O_em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+        O_em = emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
         err = rel_l2(synth.bf16_to_f32(run["O"][0, h][rows]).astype(np.float64), O_em)
         worst = max(worst, err)
         assert err <= 2e-3, (h, err)
@@ -292,7 +331,7 @@ def test_wan_rope_hadamard_sampled_heads(run, oracle_heads):
                 assert np.array_equal(g[k][0, h], o[k]), (had, h, k)
             assert np.array_equal(vq_rowmajor(g["Vq"])[0, h], o["Vq"])
             got = synth.bf16_to_f32(O[0, h][rows]).astype(np.float64)
-            O_em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+            O_em = emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
             assert rel_l2(got, O_em) <= 2e-3, (had, h)
             err_ex[had].append(rel_l2(got, O_ex))
     print("[wan rope] rMSE vs exact on the RoPE'd inputs: without rotation %.4f, with Hadamard %.4f"
@@ -330,7 +369,7 @@ def test_wan_mxfp4_sampled_rows(run, oracle_heads):
         O_ex = oracle.attention_exact(w["Q"][0, h], w["K"][0, h], w["V"][0, h], rows)
         for name, mode in (("exp", oracle.MODE_EXP_THEN_CAST), ("vc", oracle.MODE_EXPCAST)):
             got = synth.bf16_to_f32(O[name][0, h][rows]).astype(np.float64)
-            assert rel_l2(got, oracle.attention_emul(o, rows, beta=BETA, mode=mode)) <= 2e-3, (name, h)
+            assert rel_l2(got, emul(o, rows, beta=BETA, mode=mode)) <= 2e-3, (name, h)
             err_ex[name].append(rel_l2(got, O_ex))
     print("[wan mxfp4] rMSE vs exact: exp-then-cast + V-Smooth %.4f, ExpCast + V-Smooth %.4f"
           % (np.mean(err_ex["exp"]), np.mean(err_ex["vc"])), flush=True)

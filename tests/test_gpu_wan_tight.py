@@ -19,7 +19,7 @@ import oracle  # noqa: E402
 import synth  # noqa: E402
 
 vc = pytest.importorskip("bit_attention_video_online_amd")
-from tests.gpu_util import bf16_bits, rel_l2, to_dev_bf16  # noqa: E402
+from tests.gpu_util import bf16_bits, emul, rel_l2, to_dev_bf16  # noqa: E402
 
 KC = 550
 BETA = oracle.BETA_E4M3
@@ -66,7 +66,7 @@ def test_wan_tight_vc_below_plain_fp8(tight):
         e_plain.append(rel_l2(Op, Oex))
         # parity of the VC output with the oracle's emulation on the GPU's permutation
         o = oracle.quantize(Qh, Kh, Vh, tight["perm"][0, h], oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
-        em = oracle.attention_emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
+        em = emul(o, rows, beta=BETA, mode=oracle.MODE_EXPCAST)
         err = rel_l2(O, em)
         print("[wan_tight] head %d: VC %.3f%%  plain FP8 %.3f%%  VC vs emulation %.2e"
               % (h, 100 * e_vc[-1], 100 * e_plain[-1], err), flush=True)
