@@ -129,6 +129,11 @@ def test_mfma_tiles_match_the_oracles_score_model():
     D = torch.empty_like(Z)
     vc.vc_debug_mfma_f8(dev(A), dev(B), dev(C), D)
     got, want = D.cpu().numpy(), oracle.mfma_f8_dot64(*pair(A, B), C)
+    for t, r, c in np.argwhere(got != want)[:8]:
+        ks = np.nonzero(A[t, r])[0]
+        print("[mfma model] mismatch tile %d row %d col %d: slots %s a %s b %s C %r got %r model %r"
+              % (t, r, c, ks.tolist(), [hex(x) for x in A[t, r, ks]], [hex(x) for x in B[t, c, ks]],
+                 float(C[t, r, c]), float(got[t, r, c]), float(want[t, r, c])))
     assert np.array_equal(got, want), np.count_nonzero(got != want)
     # adversarial: every group one product of random exponent, C of comparable size (not modelled)
     A = np.zeros((n, 32, 64), np.uint8)

@@ -30,7 +30,7 @@ def _operands(slots):
 
 def test_worked_examples():
     cases = json.load(open(os.path.join(HERE, "golden", "mfma_score_cases.json")))["cases"]
-    assert len(cases) == 10
+    assert len(cases) == 13
     for c in cases:
         a, b = _operands(c["slots"])
         got = float(oracle.mfma_f8_dot64(a[None], b[None], np.float32(c["c"]))[0])
