@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.vc_debug_expcast.argtypes = [P, P, P, P, S, P]
         L.vc_debug_expcast_unclamped.restype = I
         L.vc_debug_expcast_unclamped.argtypes = [P, P, P, P, S, P]
+        L.vc_quantize_noalloc.restype = I
+        L.vc_quantize_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P]
         L.vc_debug_mfma_f8.restype = I
         L.vc_debug_mfma_f8.argtypes = [P, P, P, P, I, P]
         L.vc_debug_mfma_peak.restype = I
@@ -212,6 +214,22 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK, ro
         _need(rope_sin, torch.float32, (N, d // 2), "rope_sin")
         st = lib().vc_quantize_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), _ptr(rope_cos), _ptr(rope_sin), B, H, N,
                                     d, int(block), int(flags), *outs)
+    _check(st)
+    return out
+
+
+def vc_quantize_noalloc(Q, K, V, perm, flags, out, stream=None, block=BLOCK):
+    """vc_quantize without a workspace: the library's own device scratch serves instead (no
+    allocation in the call; calls overlapping on one device race)."""
+    B, H, N, d = _dims(Q)
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, (B, H, N, d), n)
+    if perm is not None:
+        _need(perm, torch.int32, (B, H, N), "perm")
+    st = lib().vc_quantize_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(perm), B, H, N, d, int(block), int(flags),
+                                   _ptr(out["Qq"]), _ptr(out["sQ"]), _ptr(out["Kq"]), _ptr(out["sK"]),
+                                   _ptr(out["Vq"]), _ptr(out["sV"]), _ptr(out.get("mu")), _ptr(out.get("mu_scaled")),
+                                   _ptr(out.get("mu_pack")), _stream(stream))
     _check(st)
     return out
 

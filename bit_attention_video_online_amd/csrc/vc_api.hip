@@ -192,16 +192,42 @@ extern "C" size_t vc_quantize_workspace_bytes(int B, int H, int N, int d, int bl
   return vc_quantize_ws_bytes(B, H, N, d);
 }
 
+// ---- the allocation-free quantiser: the workspace that vc_quantize takes from its caller lives
+// in a file-scope device array instead. Every device that runs it holds its own copy until the
+// process ends; the host-side name is only a stand-in, so the array is always addressed through
+// the device address hipGetSymbolAddress returns for the current device (kept per ordinal).
+static __device__ __align__(256) unsigned char scratch[VC_QUANTIZE_NOALLOC_SCRATCH_BYTES];
+static void* scratch_dev[64];
+
+static vc_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return VC_E_UNSUPPORTED;
+  }
+  if (!scratch_dev[dev]) {  // first call on this device (concurrent first calls store the same value)
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return VC_E_HIP;
+    }
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return VC_OK;
+}
+
 static vc_status quantize_common(const void* Q, const void* K, const void* V, const int32_t* perm,
                                  const float* rope_cos, const float* rope_sin, int B, int H, int N, int d, int block,
                                  uint32_t flags, uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq,
                                  float* sV, void* mu, float* mu_scaled, void* mu_pack, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || !workspace) return VC_E_NULLPTR;
+                                 size_t workspace_bytes, void* stream, bool noalloc = false) {
+  if (!Q || !K || !V || !Qq || !sQ || !Kq || !sK || !Vq || !sV || (!workspace && !noalloc)) return VC_E_NULLPTR;
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return VC_E_NULLPTR;
   if (!shape_ok(B, H, N, d) || block != 128) return VC_E_SHAPE;
   if (flags & ~(uint32_t)(VC_F_KSMOOTH | VC_F_VSMOOTH | VC_F_EXPCAST | VC_F_HADAMARD | VC_F_MXFP4)) return VC_E_PARAM;
-  if (workspace_bytes < vc_quantize_ws_bytes(B, H, N, d)) return VC_E_WORKSPACE;
+  const size_t need = vc_quantize_ws_bytes(B, H, N, d);
+  if (noalloc ? need > (size_t)VC_QUANTIZE_NOALLOC_SCRATCH_BYTES : workspace_bytes < need) return VC_E_WORKSPACE;
   const void* ptrs[] = {Q, K, V, perm, rope_cos, rope_sin, Qq, sQ, Kq, sK, Vq, sV, mu, mu_scaled, mu_pack, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return VC_E_UNSUPPORTED;
@@ -218,8 +244,11 @@ static vc_status quantize_common(const void* Q, const void* K, const void* V, co
     for (const Range& i : ins)
       if (overlaps(o, i)) return VC_E_ALIAS;
   if (const vc_status dc = device_check()) return dc;
+  void* ws = workspace;
+  if (noalloc)
+    if (const vc_status sp = scratch_ptr(&ws)) return sp;
   if (vc_launch_quantize(Q, K, V, perm, rope_cos, rope_sin, B, H, N, d, flags, log2e_over_sqrt_d(d), Qq, sQ, Kq, sK,
-                         Vq, sV, mu, mu_scaled, mu_pack, workspace, (hipStream_t)stream) != 0)
+                         Vq, sV, mu, mu_scaled, mu_pack, ws, (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
 }
@@ -230,6 +259,14 @@ extern "C" vc_status vc_quantize(const void* Q, const void* K, const void* V, co
                                  size_t workspace_bytes, void* stream) {
   return quantize_common(Q, K, V, perm, nullptr, nullptr, B, H, N, d, block, flags, Qq, sQ, Kq, sK, Vq, sV, mu,
                          mu_scaled, mu_pack, workspace, workspace_bytes, stream);
+}
+
+extern "C" vc_status vc_quantize_noalloc(const void* Q, const void* K, const void* V, const int32_t* perm, int B,
+                                         int H, int N, int d, int block, uint32_t flags, uint8_t* Qq, float* sQ,
+                                         uint8_t* Kq, float* sK, uint8_t* Vq, float* sV, void* mu, float* mu_scaled,
+                                         void* mu_pack, void* stream) {
+  return quantize_common(Q, K, V, perm, nullptr, nullptr, B, H, N, d, block, flags, Qq, sQ, Kq, sK, Vq, sV, mu,
+                         mu_scaled, mu_pack, nullptr, 0, stream, true);
 }
 
 extern "C" vc_status vc_quantize_rope(const void* Q, const void* K, const void* V, const int32_t* perm,

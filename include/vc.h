@@ -197,6 +197,28 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
                       size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * vc_quantize_noalloc -- vc_quantize for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and outputs, with no workspace argument. Its scratch is a
+ * file-scope device array of VC_QUANTIZE_NOALLOC_SCRATCH_BYTES (64 MiB) that every device
+ * the library runs on holds until the process ends; the call itself allocates nothing.
+ *
+ *   a shape whose vc_quantize_workspace_bytes exceeds VC_QUANTIZE_NOALLOC_SCRATCH_BYTES is
+ *   rejected with VC_E_WORKSPACE before anything is launched (B*H*(N/128)*d up to about
+ *   4.79 M elements, e.g. B=1, H=40, N=70,400, d=128 fits);
+ *   every call on one device shares that device's array, which keeps the last call's
+ *   contents (nothing in it needs clearing: each call writes all it reads): calls that
+ *   overlap in time on one device, on any streams, race and must be serialised by the
+ *   caller.
+ * Other arguments, outputs and errors as vc_quantize.
+ * ------------------------------------------------------------------------ */
+#define VC_QUANTIZE_NOALLOC_SCRATCH_BYTES (64u << 20)
+vc_status vc_quantize_noalloc(const void* Q, const void* K, const void* V, const int32_t* perm,
+                              int B, int H, int N, int d, int block, uint32_t flags,
+                              uint8_t* Qq, float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV,
+                              void* mu, float* mu_scaled, void* mu_pack, void* stream);
+
+/* ------------------------------------------------------------------------
  * vc_quantize_rope -- vc_quantize with rotary position embedding applied to Q and K
  * first (the pages' fused preprocessing absorbs RoPE into the quantiser).
  *

@@ -204,3 +204,22 @@ def test_valid_calls_need_a_gfx950_device(L):
     assert L.vc_debug_mfma_f8(A, B, C, D, 1, None) == 5
     assert L.vc_debug_expcast(A, B, C, D, 4, None) == 5
     assert L.vc_debug_mfma_peak(1, 1, 0, ctypes.c_void_p(1 << 20), None) == 5
+
+
+def test_quantize_noalloc_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, perm=None, B=1, H=1, N=256, d=128, block=128, flags=3,
+                 Qq=ctypes.c_void_p(1 << 20), sQ=ctypes.c_void_p(2 << 20), Kq=ctypes.c_void_p(3 << 20),
+                 sK=ctypes.c_void_p(4 << 20), Vq=ctypes.c_void_p(5 << 20), sV=ctypes.c_void_p(6 << 20),
+                 mu=ctypes.c_void_p(7 << 20), mus=ctypes.c_void_p(8 << 20), mup=ctypes.c_void_p(10 << 20))
+        a.update(kw)
+        return L.vc_quantize_noalloc(a["Q"], a["K"], a["V"], a["perm"], a["B"], a["H"], a["N"], a["d"], a["block"],
+                                     a["flags"], a["Qq"], a["sQ"], a["Kq"], a["sK"], a["Vq"], a["sV"], a["mu"],
+                                     a["mus"], a["mup"], None)
+    assert call(Q=None) == 1
+    assert call(N=200) == 2
+    assert call(flags=64) == 3
+    # beyond the 64 MiB scratch: B*H*(N/128)*d = 40 * 1024 * 128 elements need 70 MiB
+    assert call(B=1, H=40, N=131072) == 4
+    assert call(Qq=ctypes.c_void_p((1 << 20) + 4)) == 5
+    assert call(Qq=FAKE) == 7
