@@ -62,16 +62,20 @@ def profiled_traffic():
     return round((rec["fetch_bytes"] + rec["write_bytes"]) / 1e9, 3)
 
 
-def cpu_baseline(host, K_clusters, sample_rows, threads):
-    """Time the oracle on a bounded sample of the same workload (head 0)."""
+def cpu_baseline(host, K_clusters, sample_rows, threads, gpu=None):
+    """Time the oracle on a bounded sample of the same workload (head 0), and compare the GPU's
+    head 0 with what the oracle computed: mismatch counts of every bit-exact output (k-means
+    centroids, labels and permutation; quantiser codes, scales and means; the in-kernel ExpCast
+    bytes of the last key block on sampled rows) and the output's relative L2 distance from the
+    emulation on those rows (scores in the matrix core's precision, output rounded to bf16)."""
     import numpy as np
     import oracle
     Q, K, V, Vp = (host[k][0, 0] for k in ("Q", "K", "V", "V_prev"))
     N, d = Q.shape
     t0 = time.time()
-    _, _, Cw = oracle.kmeans(Vp, K_clusters, 1, cold=True)          # warm-start state (not timed)
+    _, _, Cw = oracle.kmeans(Vp, K_clusters, 4, cold=True)          # warm-start state (not timed)
     t1 = time.time()
-    labels, perm, _ = oracle.kmeans(V, K_clusters, 2, cold=False, C=Cw)
+    labels, perm, C = oracle.kmeans(V, K_clusters, 2, cold=False, C=Cw)
     t2 = time.time()
     q = oracle.quantize(Q, K, V, perm, oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
     t3 = time.time()
@@ -80,12 +84,41 @@ def cpu_baseline(host, K_clusters, sample_rows, threads):
     t4 = time.time()
     t_head = (t2 - t1) + (t3 - t2) + (t4 - t3) * N / sample_rows
     flops_head = 4.0 * N * N * d
-    return dict(value=flops_head / t_head / 1e12, unit="TFLOPS", cores=threads, kind="oracle",
-                sample="head 0 of the workload: k-means (2 warm iterations, 550 clusters) and quantiser in full, "
-                       "attention emulation on %d of %d query rows extrapolated x%.0f; per-head time %.1f s "
-                       "(kmeans %.1f s, quantise %.1f s, attention %.1f s measured)"
-                       % (sample_rows, N, N / sample_rows, t_head, t2 - t1, t3 - t2, t4 - t3),
-                seconds_measured=round(t4 - t1, 2), warm_start_seconds=round(t1 - t0, 2))
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    res = dict(value=flops_head / t_head / 1e12, unit="TFLOPS", cores=threads, kind="oracle", cpu=cpu,
+               sample="head 0 of the workload: k-means (2 warm iterations, 550 clusters) and quantiser in full, "
+                      "attention emulation on %d of %d query rows extrapolated x%.0f; per-head time %.1f s "
+                      "(kmeans %.1f s, quantise %.1f s, attention %.1f s measured)"
+                      % (sample_rows, N, N / sample_rows, t_head, t2 - t1, t3 - t2, t4 - t3),
+               seconds_measured=round(t4 - t1, 2), warm_start_seconds=round(t1 - t0, 2))
+    if gpu is not None:
+        nb = N // 128
+        g = gpu["q"]
+        vq = g["Vq"].reshape(nb, d, 128).transpose(0, 2, 1).reshape(N, d)   # block-transposed -> row-major
+        mis = {"centroids": int(np.count_nonzero(gpu["C"] != C)), "labels": int(np.count_nonzero(gpu["labels"] != labels)),
+               "perm": int(np.count_nonzero(gpu["perm"] != perm))}
+        for k in ("Qq", "sQ", "Kq", "sK", "sV", "mu", "mu_scaled"):
+            mis[k] = int(np.count_nonzero(g[k] != q[k]))
+        mis["Vq"] = int(np.count_nonzero(vq != q["Vq"]))
+        prow = gpu["rows"]
+        O_em, codes = oracle.attention_emul(q, prow, beta=BETA, mode=oracle.MODE_EXPCAST, dump_block=nb - 1,
+                                            score="gfx950", out_bf16=True)
+        mis["expcast_bytes_block_%d" % (nb - 1)] = int(np.count_nonzero(gpu["codes"] != codes))
+        Og = gpu["O"].astype(np.float64)
+        res["parity"] = {"mismatches": mis,
+                         "elements_compared": {"centroids": int(C.size), "labels": int(N), "codes_per_tensor": int(N * d),
+                                               "expcast_bytes": int(codes.size)},
+                         "attention_rows": int(prow.size),
+                         "attention_rel_l2_vs_emulation": float(np.linalg.norm(Og - O_em) / np.linalg.norm(O_em)),
+                         "tolerance": 2e-3}
+    return res
 
 
 def exact_attention_rows(Qr, K, V):
@@ -94,6 +127,53 @@ def exact_attention_rows(Qr, K, V):
     s = torch.mm(Qr, K.t().contiguous()) / (Qr.shape[1] ** 0.5)
     p = torch.softmax(s, dim=1)
     return p @ V
+
+
+def error_columns(args, vc, torch, B, H, N, d, Kc, Qd, Kd, Vd, lab, perm, C, q, O, flags_q):
+    """After the timed steps (the buffers hold the last step's results): the error of every path
+    against binary64 exact attention (softmax(Q K^T / sqrt(d)) V from the bf16 inputs, torch on
+    the device) on sampled rows of two heads, rMSE = ||O - O_exact||_F / ||O_exact||_F over the
+    sampled rows. Paths: vc (V-Smooth + ExpCast, the timed output), vsmooth (V-Smooth, exp then
+    cast), plain (no V-Smooth, exp then cast), expcast (no V-Smooth, ExpCast). Also returns the
+    GPU's head-0 results for the oracle comparison of the CPU-baseline leg."""
+    import numpy as np
+    heads = (0, min(23, H - 1))
+    rows = np.linspace(0, N - 1, args.error_rows).astype(np.int64)
+    rows_t = torch.from_numpy(rows).cuda()
+    Ovs = torch.empty_like(O)
+    vc.vc_attention(q, Ovs, beta=BETA, flags=0)
+    qp = vc.quantize_outputs(B, H, N, d)
+    vc.vc_quantize(Qd, Kd, Vd, None, vc.VC_F_KSMOOTH, qp)
+    Op = torch.empty_like(O)
+    vc.vc_attention(qp, Op, beta=BETA, flags=0, restore_mean=False)
+    Oe = torch.empty_like(O)
+    vc.vc_attention(qp, Oe, beta=BETA, flags=vc.VC_F_EXPCAST, restore_mean=False)
+    codes = torch.empty((B, H, N, 128), dtype=torch.uint8, device="cuda")
+    Od = torch.empty_like(O)
+    vc.vc_attention_dump(q, Od, N // 128 - 1, codes, beta=BETA, flags=vc.VC_F_EXPCAST)
+    torch.cuda.synchronize()
+    err = {k: [0.0, 0.0] for k in ("vc", "vsmooth", "plain", "expcast")}
+    for h in heads:
+        ex = exact_attention_rows(Qd[0, h][rows_t].double(), Kd[0, h].double(), Vd[0, h].double())
+        for k, X in (("vc", O), ("vsmooth", Ovs), ("plain", Op), ("expcast", Oe)):
+            diff = X[0, h][rows_t].double() - ex
+            err[k][0] += float((diff * diff).sum())
+            err[k][1] += float((ex * ex).sum())
+    rmse = {k: round((a / b) ** 0.5, 6) for k, (a, b) in err.items()}
+    errors = {"rmse_vs_fp64": rmse, "vc_below_plain_fp8": rmse["vc"] < rmse["plain"],
+              "rows": "%d evenly spaced rows x heads %s, binary64 softmax(Q K^T / sqrt(d)) V from the bf16 inputs"
+                      % (rows.size, list(heads)),
+              "dump_output_identical": bool(torch.equal(Od, O))}
+    prow = np.linspace(0, N - 1, 128).astype(np.int32)
+    gpu = {"labels": lab[0, 0].cpu().numpy(), "perm": perm[0, 0].cpu().numpy(), "C": C[0, 0].cpu().numpy(),
+           "q": {k: (v[0, 0].contiguous().view(torch.int16).cpu().numpy().view(np.uint16) if v.dtype == torch.bfloat16
+                     else v[0, 0].cpu().numpy()) for k, v in q.items() if k != "mu_pack"},
+           "rows": prow, "codes": codes[0, 0][torch.from_numpy(prow).long().cuda()].cpu().numpy(),
+           "O": O[0, 0][torch.from_numpy(prow).long().cuda()].float().cpu().numpy()}
+    del Ovs, qp, Op, Oe, codes, Od
+    torch.cuda.empty_cache()
+    log("[bench] rMSE vs binary64 exact attention: %s" % rmse)
+    return errors, gpu
 
 
 def device_info():
@@ -438,6 +518,8 @@ def main():
                          "the probability stage); vs_mx4 / vc_mx4 = the 4-bit (MXFP4) value residual with V-Smooth "
                          "and exp-then-cast / ExpCast probabilities")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
+    ap.add_argument("--error-rows", type=int, default=64,
+                    help="rows per head (two heads) for the error columns of the default workload")
     ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift"],
                     help="schedule workload: fixed clustering steps 0-4, or drift-triggered refresh")
     ap.add_argument("--drift-threshold", type=float, default=0.05,
@@ -563,6 +645,10 @@ def main():
     mfma = measure_mfma_peak()
     log("[bench] sustained FP8 matrix-core rate (TFLOP/s): %s" % mfma)
 
+    errors = gpu_head0 = None
+    if not args.attention_only:
+        errors, gpu_head0 = error_columns(args, vc, torch, B, H, N, d, Kc, Qd, Kd, Vd, lab, perm, C, q, O, flags_q)
+
     flops = 4.0 * B * H * N * N * d
     t_att = avg["attention"] / 1e3
     att_tflops = flops / t_att / 1e12
@@ -589,6 +675,8 @@ def main():
                      "traffic_unit": "GB per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
                      "kernel": "attn_fwd<128,ExpCast,restore>", "algorithmic_flops_per_launch": flops},
     }
+    if errors is not None:
+        res["errors"] = errors
     if args.quant_prep != "none":
         res["config"]["workload"] += " (quantiser with %s%s)" % (
             {"rope": "RoPE", "hadamard": "the Q/K Hadamard rotation",
@@ -607,7 +695,7 @@ def main():
     if not args.no_cpu_baseline and not args.attention_only:
         import oracle
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        res["cpu_baseline"] = cpu_baseline(host, Kc, args.cpu_rows, oracle.num_threads())
+        res["cpu_baseline"] = cpu_baseline(host, Kc, args.cpu_rows, oracle.num_threads(), gpu=gpu_head0)
     print(json.dumps(res), flush=True)
 
 
