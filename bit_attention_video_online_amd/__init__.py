@@ -19,7 +19,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libvc.so")
+# VC_LIB_PATH selects another build of the same library (the CPU suite's host-sanitizer run uses it)
+LIB_PATH = os.environ.get("VC_LIB_PATH") or os.path.join(HERE, "libvc.so")
 
 VC_F_KSMOOTH = 1
 VC_F_VSMOOTH = 2

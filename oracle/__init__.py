@@ -60,8 +60,16 @@ PINS = {
 }
 
 
-def build(force: bool = False) -> str:
-    """Compile vc_oracle.c into liboracle.so (gcc, OpenMP, no FP contraction)."""
+def build(force: bool = False, sanitize_to: str | None = None) -> str:
+    """Compile vc_oracle.c into liboracle.so (gcc, OpenMP, no FP contraction). With
+    sanitize_to, build an AddressSanitizer + UndefinedBehaviorSanitizer copy at that path
+    instead (loaded through VC_ORACLE_LIB with the gcc ASan runtime preloaded)."""
+    if sanitize_to:
+        cmd = ["gcc", "-O1", "-g", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-o", sanitize_to, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        return sanitize_to
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
@@ -77,7 +85,7 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        _lib = ctypes.CDLL(os.environ.get("VC_ORACLE_LIB") or build())
         P = ctypes.c_void_p
         I = ctypes.c_int
         L = ctypes.c_int64
