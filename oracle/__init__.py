@@ -110,6 +110,7 @@ def lib() -> ctypes.CDLL:
         _lib.or_kmeans.argtypes = [P, I, I, I, I, I, P, P, P]
         _lib.or_kmeans_assign_biased.argtypes = [P, I, I, P, I, P, P]
         _lib.or_kmeans_balanced.argtypes = [P, I, I, I, I, I, ctypes.c_float, P, P, P, P]
+        _lib.or_kmeans_incremental.argtypes = [P, I, I, I, F, I, P, P, P, P]
         _lib.or_kmeans_cost.restype = ctypes.c_double
         _lib.or_kmeans_cost.argtypes = [P, I, I, P, I, P]
         _lib.or_quantize.restype = I
@@ -296,6 +297,24 @@ def fwht_rows(x) -> np.ndarray:
     rows, d = a.shape
     lib().or_fwht_rows(_p(a), rows, d)
     return a
+
+
+def kmeans_incremental(V_bits, C, M, decay: float, assign: bool, labels=None):
+    """One cross-step incremental centroid update (see or_kmeans_incremental): returns
+    (labels, perm, centroids, masses). Without `assign` the given labels are kept."""
+    V = _c(V_bits, np.uint16)
+    N, d = V.shape
+    Cn = np.array(C, dtype=np.float32, copy=True, order="C")
+    Mn = np.array(M, dtype=np.float32, copy=True, order="C")
+    K = Cn.shape[0]
+    assert Mn.shape == (K,)
+    lab = np.zeros(N, np.int32) if labels is None else np.array(labels, dtype=np.int32, copy=True, order="C")
+    if not assign and labels is None:
+        raise ValueError("kmeans_incremental: labels are required without assign")
+    perm = np.empty(N, np.int32)
+    lib().or_kmeans_incremental(_p(V), N, d, K, ctypes.c_float(decay), 1 if assign else 0, _p(Cn), _p(Mn),
+                                _p(lab), _p(perm))
+    return lab, perm, Cn, Mn
 
 
 def kmeans_cost(V_bits, C, labels) -> float:

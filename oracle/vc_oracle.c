@@ -392,6 +392,93 @@ void or_kmeans(const uint16_t* V, int N, int d, int K, int iters, int cold,
   free(chat);
 }
 
+/* a += x*y exactly, for any finite doubles x, y (significands split into     */
+/* 18-bit pieces so that every partial product stays below 2^36)             */
+static void xa_add_prod_dd(xacc* a, double x, double y) {
+  int64_t mx, my; int ex, ey;
+  dbl_me(x, &mx, &ex);
+  dbl_me(y, &my, &ey);
+  if (mx == 0 || my == 0) return;
+  const int neg = (mx < 0) != (my < 0);
+  const uint64_t ax = mx < 0 ? (uint64_t)(-mx) : (uint64_t)mx, ay = my < 0 ? (uint64_t)(-my) : (uint64_t)my;
+  for (int i = 0; i < 3; i++)
+    for (int j = 0; j < 3; j++) {
+      const int64_t pp = (int64_t)(((ax >> (18 * i)) & 0x3ffff) * ((ay >> (18 * j)) & 0x3ffff));
+      xa_add_me(a, neg ? -pp : pp, ex + ey + 18 * (i + j));
+    }
+}
+
+/* nearest binary32 (ties to even) of the exact quotient num/den, den > 0 */
+static float f32_of_quotient(double num, double den) {
+  const double q = num / den;
+  const float f = (float)q;
+  if ((double)f == q) return f; /* then num/den is within half a binary64 ulp of f */
+  const float lo = (double)f < q ? f : nextafterf(f, -INFINITY);
+  const float hi = (double)f < q ? nextafterf(f, INFINITY) : f;
+  const double mid = ((double)lo + (double)hi) / 2; /* exact */
+  xacc s;
+  xa_zero(&s);
+  xa_add_double(&s, num);
+  xa_add_prod_dd(&s, -mid, den);
+  uint32_t mag[XA_LIMBS];
+  const int sg = xa_normalize(&s, mag);
+  if (sg > 0) return hi;
+  if (sg < 0) return lo;
+  uint32_t bl;
+  memcpy(&bl, &lo, 4);
+  return (bl & 1) ? hi : lo;
+}
+
+/* Cross-step incremental centroid update (the paper page's weakness list:   */
+/* clustering runs per step and per head and leaves the redundancy between    */
+/* denoising steps unused; update the centroids incrementally across steps).  */
+/* Each cluster keeps a decayed member mass M_k beside its centroid C_k, and  */
+/* one step folds the current values of its members into a running mean:     */
+/*   A = decay * M_k (binary64, exact),  S_k = exact member sum (to binary64), */
+/*   num = A * C_k + S_k, den = A + n_k (binary64, rounded op by op),         */
+/*   C_k = nearest binary32 of num / den,  M_k = fl32(den);                   */
+/* an empty cluster keeps C_k and decays its mass, M_k = fl32(decay * M_k).    */
+/* decay = 0 is one Lloyd update; decay = 1 the mean over all steps so far.   */
+/* With `assign` the members are first re-assigned to the nearest bf16(C_k)   */
+/* (the k-means assignment); otherwise the given labels are kept (a label     */
+/* outside [0, K) is read as 0). perm = stable argsort of the labels.        */
+void or_kmeans_incremental(const uint16_t* V, int N, int d, int K, float decay, int assign, float* C, float* M,
+                           int32_t* labels, int32_t* perm) {
+  if (assign) {
+    float* chat = (float*)malloc(sizeof(float) * (size_t)K * d);
+    for (int64_t i = 0; i < (int64_t)K * d; i++) chat[i] = bf16_val(f32_to_bf16(C[i]));
+    or_kmeans_assign(V, N, d, chat, K, labels);
+    free(chat);
+  } else {
+    for (int t = 0; t < N; t++)
+      if (labels[t] < 0 || labels[t] >= K) labels[t] = 0;
+  }
+  or_stable_argsort(labels, N, K, perm);
+  int64_t* start = (int64_t*)calloc((size_t)K + 1, sizeof(int64_t));
+  for (int t = 0; t < N; t++) start[labels[t] + 1]++;
+  for (int k = 0; k < K; k++) start[k + 1] += start[k];
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int k = 0; k < K; k++) {
+    const int64_t a = start[k], b = start[k + 1];
+    const double A = (double)decay * (double)M[k];
+    if (b == a) {
+      M[k] = (float)A;
+      continue;
+    }
+    const double den = A + (double)(b - a);
+    for (int j = 0; j < d; j++) {
+      xacc s;
+      xa_zero(&s);
+      for (int64_t i = a; i < b; i++) xa_add_double(&s, bf16_val(V[(int64_t)perm[i] * d + j]));
+      const double S = xa_round_div(&s, 1, 53);
+      const double num = A * (double)C[(int64_t)k * d + j] + S;
+      C[(int64_t)k * d + j] = f32_of_quotient(num, den);
+    }
+    M[k] = (float)den;
+  }
+  free(start);
+}
+
 /* Size-penalised Lloyd iterations: a cheap form of the balanced clustering   */
 /* the paper page measures and sets aside for its cost (ablation on balanced  */
 /* k-means; the weakness list). Each assignment minimises                    */
