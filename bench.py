@@ -352,6 +352,7 @@ def run_schedule(args):
     cost = torch.empty((B, H), dtype=torch.float64, device="cuda")
     ws_cost = vc.workspace(int(vc.lib().vc_cluster_cost_workspace_bytes(B, H, N, d)))
     cost_ref = None
+    mass = torch.zeros((B, H, Kc), dtype=torch.float32, device="cuda")
     steps = []
     for s in range(S):
         if s > 0:
@@ -363,7 +364,18 @@ def run_schedule(args):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         ev[0].record()
         clustered, drift = False, None
-        if args.refresh == "fixed":
+        if args.refresh == "incremental":
+            # cross-step incremental centroids: step 0 is the fixed schedule's cold 4-iteration
+            # k-means (3 iterations, then a decay-0 incremental step = the 4th iteration, which
+            # also sets every cluster's mass to its size); every later step re-assigns once
+            # and folds the new members into the decayed running mean
+            if s == 0:
+                vc.vc_cluster(V, Kc, 3, True, C, lab, perm, ws=ws_c)
+                vc.vc_cluster_incremental(V, 0.0, True, C, mass, lab, perm, ws=ws_c)
+            else:
+                vc.vc_cluster_incremental(V, args.decay, True, C, mass, lab, perm, ws=ws_c)
+            clustered = True
+        elif args.refresh == "fixed":
             if s == 0:
                 vc.vc_cluster(V, Kc, 4, True, C, lab, perm, ws=ws_c)
             elif s <= 4:
@@ -402,11 +414,13 @@ def run_schedule(args):
                "" if drift is None else ", drift %.4f" % drift))
     t_c = sum(x["cluster_ms"] for x in steps)
     t_qa = sum(x["quantize_ms"] + x["attention_ms"] for x in steps)
-    sched = ("cluster at steps 0-4 (cold x4, then warm x2), permutation of step 4 reused for steps 5-19"
-             if args.refresh == "fixed" else
-             "cluster cold x4 at step 0; afterwards re-cluster (warm x2) whenever the mean over heads of the "
-             "k-means objective under the kept clustering exceeds its post-clustering value by more than %g"
-             % args.drift_threshold)
+    sched = {"fixed": "cluster at steps 0-4 (cold x4, then warm x2), permutation of step 4 reused for steps 5-19",
+             "drift": "cluster cold x4 at step 0; afterwards re-cluster (warm x2) whenever the mean over heads of "
+                      "the k-means objective under the kept clustering exceeds its post-clustering value by more "
+                      "than %g" % args.drift_threshold,
+             "incremental": "cluster cold x4 at step 0; every later step one cross-step incremental update "
+                            "(re-assignment, then centroids = decayed running member mean, decay %g)" % args.decay
+             }[args.refresh]
     res = {"workload": "20-step amortised schedule, B=%d H=%d N=%d d=%d, %d clusters; %s" % (B, H, N, d, Kc, sched),
            "clusterings": sum(1 for x in steps if x["clustered"]),
            "clustering_share": round(t_c / t_qa, 5), "cluster_ms_total": round(t_c, 3),
@@ -520,8 +534,11 @@ def main():
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--error-rows", type=int, default=64,
                     help="rows per head (two heads) for the error columns of the default workload")
-    ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift"],
-                    help="schedule workload: fixed clustering steps 0-4, or drift-triggered refresh")
+    ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift", "incremental"],
+                    help="schedule workload: fixed clustering steps 0-4, drift-triggered refresh, or a cross-step "
+                         "incremental centroid update at every step")
+    ap.add_argument("--decay", type=float, default=0.5,
+                    help="schedule workload with --refresh incremental: weight of a cluster's past members")
     ap.add_argument("--drift-threshold", type=float, default=0.05,
                     help="relative growth of the k-means objective that triggers a refresh")
     ap.add_argument("--kappas", default="0,0.003,0.01,0.03,0.1",

@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.vc_debug_expcast.argtypes = [P, P, P, P, S, P]
         L.vc_debug_expcast_unclamped.restype = I
         L.vc_debug_expcast_unclamped.argtypes = [P, P, P, P, S, P]
+        L.vc_cluster_incremental.restype = I
+        L.vc_cluster_incremental.argtypes = [P, I, I, I, I, I, F, I, P, P, P, P, P, S, P]
         L.vc_quantize_noalloc.restype = I
         L.vc_quantize_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, U, P, P, P, P, P, P, P, P, P, P]
         L.vc_debug_mfma_f8.restype = I
@@ -217,6 +219,23 @@ def vc_quantize(Q, K, V, perm, flags, out, ws=None, stream=None, block=BLOCK, ro
                                     d, int(block), int(flags), *outs)
     _check(st)
     return out
+
+
+def vc_cluster_incremental(V, decay, assign, C, M, labels, perm, ws=None, stream=None):
+    """One cross-step incremental centroid update: C float32 [B,H,K,d] and M float32 [B,H,K]
+    in/out; labels int32 [B,H,N] out with `assign`, else in; perm int32 [B,H,N] out."""
+    B, H, N, d = _dims(V)
+    K = C.shape[2]
+    _need(V, torch.bfloat16, (B, H, N, d), "V")
+    _need(C, torch.float32, (B, H, K, d), "centroids")
+    _need(M, torch.float32, (B, H, K), "mass")
+    _need(labels, torch.int32, (B, H, N), "labels")
+    _need(perm, torch.int32, (B, H, N), "perm")
+    if ws is None:
+        ws = workspace(vc_cluster_workspace_bytes(B, H, N, d, K), V.device)
+    _check(lib().vc_cluster_incremental(_ptr(V), B, H, N, d, K, float(decay), int(bool(assign)), _ptr(C), _ptr(M),
+                                        _ptr(labels), _ptr(perm), _ptr(ws), ws.numel(), _stream(stream)))
+    return C, M, labels, perm
 
 
 def vc_quantize_noalloc(Q, K, V, perm, flags, out, stream=None, block=BLOCK):

@@ -30,6 +30,8 @@ extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
 extern "C" int vc_launch_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold, float* C,
                                  int32_t* labels, int32_t* perm, void* ws, hipStream_t st, float lam, int32_t* nk_io);
 extern "C" int vc_max_clusters(void);
+extern "C" int vc_launch_cluster_inc(const void* V, int B, int H, int N, int d, int K, float decay, int assign,
+                                     float* C, float* M, int32_t* labels, int32_t* perm, void* ws, hipStream_t st);
 
 namespace {
 
@@ -150,6 +152,34 @@ extern "C" vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int
   if (const vc_status dc = device_check()) return dc;
   if (vc_launch_cluster(V, B, H, N, d, K, iters, cold_start ? 1 : 0, centroids, labels, perm, workspace,
                         (hipStream_t)stream, lambda, counts) != 0)
+    return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" vc_status vc_cluster_incremental(const void* V, int B, int H, int N, int d, int K, float decay, int assign,
+                                            float* centroids, float* mass, int32_t* labels, int32_t* perm,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!V || !centroids || !mass || !labels || !perm || !workspace) return VC_E_NULLPTR;
+  if (!shape_ok(B, H, N, d)) return VC_E_SHAPE;
+  if (K < 1 || K > N || K > vc_max_clusters()) return VC_E_PARAM;
+  if (!(decay >= 0.0f && decay <= 1.0f)) return VC_E_PARAM;  // also rejects NaN
+  if (workspace_bytes < vc_cluster_ws_bytes(B, H, N, d, K)) return VC_E_WORKSPACE;
+  const void* ptrs[] = {V, centroids, mass, labels, perm, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return VC_E_UNSUPPORTED;
+  const size_t el = (size_t)B * H * N;
+  const Range in{(const char*)V, el * d * 2};
+  const Range bufs[] = {{(const char*)centroids, (size_t)B * H * K * d * 4}, {(const char*)mass, (size_t)B * H * K * 4},
+                        {(const char*)labels, el * 4}, {(const char*)perm, el * 4},
+                        {(const char*)workspace, workspace_bytes}};
+  for (int i = 0; i < 5; i++) {
+    if (overlaps(in, bufs[i])) return VC_E_ALIAS;
+    for (int j = i + 1; j < 5; j++)
+      if (overlaps(bufs[i], bufs[j])) return VC_E_ALIAS;
+  }
+  if (const vc_status dc = device_check()) return dc;
+  if (vc_launch_cluster_inc(V, B, H, N, d, K, decay, assign ? 1 : 0, centroids, mass, labels, perm, workspace,
+                            (hipStream_t)stream) != 0)
     return VC_E_HIP;
   return VC_OK;
 }

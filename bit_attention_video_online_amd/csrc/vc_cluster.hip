@@ -463,6 +463,62 @@ __global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V,
 // clustering early). Partial sums of ||V_t - bf16(C_{z_t})||^2 over kCostTokens tokens per
 // work-group: the difference of two bf16 values is exact in binary64, its square and the
 // sums are binary64 roundings (relative error ~1e-13 over a head).
+// Cross-step incremental update (the paper page's weakness list: centroids updated
+// incrementally across denoising steps). Cluster k keeps a decayed member mass M_k; with A =
+// decay * M_k (binary64, exact) and S_k the exact member sum (binary64 partial sums, exact for
+// values of moderate exponent span, combined in LDS), C_k = nearest binary32 of
+// (A * C_k + S_k) / (A + n_k) with the product, the sum and the denominator rounded in
+// binary64 op by op, and M_k = fl32(A + n_k). An empty cluster keeps C_k, M_k = fl32(A).
+template <int D>
+__global__ __launch_bounds__(128) void cl_update_inc(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                     const int32_t* __restrict__ cstart,
+                                                     const int32_t* __restrict__ csize, int N, int K, float decay,
+                                                     float* __restrict__ C, float* __restrict__ M) {
+  constexpr int CH = D / 8, G = 128 / CH;
+  __shared__ double part[G][D];
+  const int k = blockIdx.x, bh = blockIdx.y;
+  const size_t ck = (size_t)bh * K + k;
+  const int n = csize[ck];
+  const double A = (double)decay * (double)M[ck];
+  if (n == 0) {
+    if (threadIdx.x == 0) M[ck] = (float)A;
+    return;
+  }
+  const int s0 = cstart[ck];
+  const uint16_t* Vh = V + (size_t)bh * N * D;
+  const int32_t* ph = perm + (size_t)bh * N + s0;
+  const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  auto add_row = [&](const uint4 raw) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int e = 0; e < 4; e++) {
+      acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+      acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+    }
+  };
+  auto load_row = [&](int i) {
+    int row = ph[i];
+    row = ((unsigned)row < (unsigned)N) ? row : 0;
+    return *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
+  };
+  int i = g;
+  for (; i + 3 * G < n; i += 4 * G) {
+    const uint4 r0 = load_row(i), r1 = load_row(i + G), r2 = load_row(i + 2 * G), r3 = load_row(i + 3 * G);
+    add_row(r0); add_row(r1); add_row(r2); add_row(r3);
+  }
+  for (; i < n; i += G) add_row(load_row(i));
+  for (int e = 0; e < 8; e++) part[g][8 * chunk + e] = acc[e];
+  __syncthreads();  // every thread has read M[ck] before thread 0 writes it below
+  const double den = A + (double)n;
+  for (int c = threadIdx.x; c < D; c += 128) {
+    double s = 0.0;
+    for (int q = 0; q < G; q++) s += part[q][c];
+    const double num = A * (double)C[ck * D + c] + s;
+    C[ck * D + c] = div_to_f32(num, den);
+  }
+  if (threadIdx.x == 0) M[ck] = (float)den;
+}
+
 constexpr int kCostTokens = 1024;
 
 template <int D>
@@ -566,6 +622,35 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
     else cl_update<64><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
   }
   if (nk_io && iters > 0) cl_copy_sizes<<<(BH * K + 255) / 256, 256, 0, st>>>(csize, nk_io, BH * K);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// One incremental step: optional assignment to bf16(C) (plain, no size penalty), the stable
+// counting sort of the labels, then the decayed update. Labels outside [0, K) read as 0.
+extern "C" int vc_launch_cluster_inc(const void* Vv, int B, int H, int N, int d, int K, float decay, int assign,
+                                     float* C, float* M, int32_t* labels, int32_t* perm, void* ws, hipStream_t st) {
+  const uint16_t* V = (const uint16_t*)Vv;
+  const int BH = B * H, nch = (N + kChunk - 1) / kChunk;
+  char* w = (char*)ws;
+  uint16_t* chat = (uint16_t*)w; w += (size_t)BH * K * d * sizeof(float);
+  float* cnorm = (float*)w; w += (size_t)BH * K * sizeof(float);
+  int32_t* counts = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
+  int32_t* offs = (int32_t*)w; w += (size_t)BH * K * nch * sizeof(int32_t);
+  int32_t* cstart = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
+  int32_t* csize = (int32_t*)w; w += (size_t)BH * K * sizeof(int32_t);
+  int32_t* ctotal = (int32_t*)w;
+  const dim3 gmf((N + kAssignTokens - 1) / kAssignTokens, BH), gch(nch, BH), gk(K, BH);
+  if (assign) {
+    cl_prep<<<gk, d, 0, st>>>(C, chat, cnorm, K, d, nullptr, 0.0f);
+    if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nullptr, 0.0f);
+    else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nullptr, 0.0f);
+  }
+  cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
+  cl_scan_k<<<dim3((K + 3) / 4, BH), 256, 0, st>>>(counts, K, nch, offs, ctotal);
+  cl_scan_c<<<BH, 1024, 0, st>>>(ctotal, K, cstart, csize);
+  cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, cstart, perm);
+  if (d == 128) cl_update_inc<128><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, decay, C, M);
+  else cl_update_inc<64><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, decay, C, M);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -129,6 +129,31 @@ vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int d, int K, 
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * vc_cluster_incremental -- one cross-step incremental centroid update (the paper
+ * page's weakness list: clustering runs per denoising step and per head and leaves the
+ * redundancy between steps unused; update centroids incrementally across steps).
+ *
+ * Every cluster carries a decayed member mass M_k beside its centroid. With the members
+ * n_k of cluster k under the labels (re-assigned first when `assign` != 0: nearest
+ * bf16(C_k), as vc_cluster assigns; else the given labels, read-only, a label outside
+ * [0,K) read as 0), S_k their exact value sum, and A = decay * M_k (binary64):
+ *   C_k = nearest binary32 of (A * C_k + S_k) / (A + n_k), the product, the sum and the
+ *         denominator rounded in binary64 one operation at a time;
+ *   M_k = fl32(A + n_k); an empty cluster keeps C_k and gets M_k = fl32(A).
+ * decay 0 is one Lloyd update (with assign: one vc_cluster iteration, bit for bit);
+ * decay 1 pools every step so far. perm = stable argsort of the labels.
+ *
+ *   decay      in [0, 1] (else VC_E_PARAM)
+ *   centroids  float [B,H,K,d] in/out;  mass float [B,H,K] in/out (zeros: no history)
+ *   labels     int32 [B,H,N]  out with assign, else in;  perm int32 [B,H,N] out
+ *   workspace  >= vc_cluster_workspace_bytes(B,H,N,d,K)
+ * Other arguments, exactness and errors as vc_cluster; no buffer may overlap another.
+ * ------------------------------------------------------------------------ */
+vc_status vc_cluster_incremental(const void* V, int B, int H, int N, int d, int K, float decay, int assign,
+                                 float* centroids, float* mass, int32_t* labels, int32_t* perm,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * vc_cluster_cost -- the k-means objective of the current values under a kept
  * clustering, a drift statistic for refreshing the permutation early (the paper
  * page's weakness list: the reused permutation loses accuracy when the layout

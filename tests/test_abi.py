@@ -223,3 +223,22 @@ def test_quantize_noalloc_rejects_bad_arguments(L):
     assert call(B=1, H=40, N=131072) == 4
     assert call(Qq=ctypes.c_void_p((1 << 20) + 4)) == 5
     assert call(Qq=FAKE) == 7
+
+
+def test_cluster_incremental_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(V=FAKE, B=1, H=1, N=256, d=128, K=8, decay=0.5, assign=1, C=ctypes.c_void_p(1 << 20),
+                 M=ctypes.c_void_p(5 << 20), lab=ctypes.c_void_p(2 << 20), perm=ctypes.c_void_p(3 << 20),
+                 ws=ctypes.c_void_p(4 << 20), wsb=1 << 19)
+        a.update(kw)
+        return L.vc_cluster_incremental(a["V"], a["B"], a["H"], a["N"], a["d"], a["K"], ctypes.c_float(a["decay"]),
+                                        a["assign"], a["C"], a["M"], a["lab"], a["perm"], a["ws"], a["wsb"], None)
+    assert call(M=None) == 1
+    assert call(N=100) == 2
+    assert call(K=0) == 3
+    assert call(decay=-0.1) == 3
+    assert call(decay=1.5) == 3
+    assert call(decay=float("nan")) == 3
+    assert call(wsb=8) == 4
+    assert call(M=ctypes.c_void_p((5 << 20) + 4)) == 5
+    assert call(M=ctypes.c_void_p(2 << 20)) == 7        # mass aliases labels

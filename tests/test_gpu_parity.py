@@ -637,3 +637,34 @@ def test_attention_d64_long_sequence_sampled_rows():
         err = rel_l2(_o_f64(O[0, h][rows]), emul(q_or, rows, beta=BETA, mode=oracle.MODE_EXPCAST))
         print("[d=64 N=32768] head %d rel-L2 %.3e" % (h, err))
         assert err <= TOL, (h, err)
+
+
+@pytest.mark.parametrize("d,N,K", [(128, 1024, 8), (64, 2560, 37), (128, 3072, 300)])
+@pytest.mark.parametrize("decay,assign", [(0.0, True), (0.5, True), (1.0, False), (0.9, False)])
+def test_cluster_incremental_bitexact(d, N, K, decay, assign):
+    """Cross-step incremental centroid update, two steps in a row (the second on drifted
+    values, carrying the first step's centroids and masses): centroids, masses, labels and
+    permutation bit-exact against the oracle on two heads, ragged last work-group included."""
+    B, H = 1, 2
+    w = synth.gen("wan", seed=33, B=B, H=H, N=N, d=d)
+    V1 = w["V"]
+    V2 = np.stack([np.stack([synth.drift(w["V"][0, h], 33, 0, h, 1) for h in range(H)])])
+    rng = np.random.default_rng(N + K)
+    C = (rng.standard_normal((B, H, K, d)) * 2).astype(np.float32)
+    M = rng.uniform(0, 3 * N / K, (B, H, K)).astype(np.float32)
+    M[0, :, :3] = 0.0                                                    # clusters with no history
+    lab = rng.integers(0, K, (B, H, N)).astype(np.int32)
+    Cd, Md, ld = to_dev(C), to_dev(M), to_dev(lab)
+    pd = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    oc, om, ol = C.copy(), M.copy(), lab.copy()
+    for step, V in enumerate((V1, V2)):
+        vc.vc_cluster_incremental(to_dev_bf16(V), decay, assign, Cd, Md, ld, pd)
+        torch.cuda.synchronize()
+        for h in range(H):
+            l_or, p_or, c_or, m_or = oracle.kmeans_incremental(V[0, h], oc[0, h], om[0, h], decay, assign,
+                                                               labels=ol[0, h])
+            oc[0, h], om[0, h], ol[0, h] = c_or, m_or, l_or
+            assert np.array_equal(ld.cpu().numpy()[0, h], l_or), (step, h)
+            assert np.array_equal(pd.cpu().numpy()[0, h], p_or), (step, h)
+            assert np.array_equal(Cd.cpu().numpy()[0, h], c_or), (step, h)
+            assert np.array_equal(Md.cpu().numpy()[0, h], m_or), (step, h)

@@ -185,6 +185,30 @@ def test_wan_balanced_kmeans_sampled_heads(run, oracle_heads):
         assert np.array_equal(cnt[0, h], np.bincount(lab[0, h], minlength=KC)), h
 
 
+def test_wan_incremental_update_sampled_heads(run, oracle_heads):
+    """One cross-step incremental step at full size (decay 1/2, re-assignment) from the warm
+    state, with masses from the warm labels: all heads on the GPU, two heads bit-exact."""
+    w = run["w"]
+    B, H, N, d = w["V"].shape
+    C = run["Cw"].copy()
+    M = np.zeros((B, H, KC), np.float32)
+    for h in HEADS:
+        C[0, h] = oracle_heads[h]["Cw"]
+        M[0, h] = np.bincount(oracle_heads[h]["lab"], minlength=KC)
+    Cd, Md = torch.from_numpy(C).cuda(), torch.from_numpy(M).cuda()
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    vc.vc_cluster_incremental(to_dev_bf16(w["V"]), 0.5, True, Cd, Md, lab, perm)
+    torch.cuda.synchronize()
+    lab, perm, Cd, Md = (x.cpu().numpy() for x in (lab, perm, Cd, Md))
+    for h in HEADS:
+        l_or, p_or, c_or, m_or = oracle.kmeans_incremental(w["V"][0, h], C[0, h], M[0, h], 0.5, True)
+        assert np.array_equal(lab[0, h], l_or), (h, np.count_nonzero(lab[0, h] != l_or))
+        assert np.array_equal(perm[0, h], p_or), h
+        assert np.array_equal(Cd[0, h], c_or), h
+        assert np.array_equal(Md[0, h], m_or), h
+
+
 def test_wan_quantize_bitexact_sampled_heads(run, oracle_heads):
     g = run["q"]
     for h in HEADS:
