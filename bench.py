@@ -533,7 +533,7 @@ def main():
                          "and exp-then-cast / ExpCast probabilities")
     ap.add_argument("--schedule-rows", type=int, default=64, help="sampled rows of head 0 for the schedule's rMSE")
     ap.add_argument("--error-rows", type=int, default=64,
-                    help="rows per head (two heads) for the error columns of the default workload")
+                    help="rows per head (two heads) for the error columns of the default workload (0: no error columns)")
     ap.add_argument("--refresh", default="fixed", choices=["fixed", "drift", "incremental"],
                     help="schedule workload: fixed clustering steps 0-4, drift-triggered refresh, or a cross-step "
                          "incremental centroid update at every step")
@@ -663,7 +663,7 @@ def main():
     log("[bench] sustained FP8 matrix-core rate (TFLOP/s): %s" % mfma)
 
     errors = gpu_head0 = None
-    if not args.attention_only:
+    if not args.attention_only and args.error_rows > 0:
         errors, gpu_head0 = error_columns(args, vc, torch, B, H, N, d, Kc, Qd, Kd, Vd, lab, perm, C, q, O, flags_q)
 
     flops = 4.0 * B * H * N * N * d

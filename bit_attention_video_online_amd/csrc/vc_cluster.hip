@@ -207,10 +207,12 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
         const float cnk = cn_s[kl];
         for (int g = 0; g < NG; g++) {
           const float dd = __builtin_fmaf(-2.0f, acc[g][i], cnk);  // exact scaling, one rounding
-          // d1 <= d2 always, so the new runner-up is the median of (d1, d2, dd)
-          kbest[g] = dd < d1[g] ? k0 + kl : kbest[g];
+          // d1 <= d2 always, so the new runner-up is the median of (d1, d2, dd); the best moves
+          // on one compare, which selects both the index and the distance
+          const bool lt = dd < d1[g];
+          kbest[g] = lt ? k0 + kl : kbest[g];
           d2[g] = __builtin_amdgcn_fmed3f(d1[g], d2[g], dd);
-          d1[g] = fminf(d1[g], dd);
+          d1[g] = lt ? dd : d1[g];
         }
       }
     }
@@ -325,7 +327,8 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   }
 }
 
-// counts[bh][k][chunk]
+// Per-chunk label counts, counts[bh][chunk][k]: each work-group writes its K counts as one
+// contiguous row.
 __global__ __launch_bounds__(256) void cl_hist(const int32_t* __restrict__ labels, int N, int K, int nch,
                                                int32_t* __restrict__ counts) {
   extern __shared__ int hist[];
@@ -338,33 +341,40 @@ __global__ __launch_bounds__(256) void cl_hist(const int32_t* __restrict__ label
     atomicAdd(&hist[((unsigned)z < (unsigned)K) ? z : 0], 1);
   }
   __syncthreads();
-  for (int k = threadIdx.x; k < K; k += 256) counts[((size_t)bh * K + k) * nch + ch] = hist[k];
+  int32_t* row = counts + ((size_t)bh * nch + ch) * K;
+  for (int k = threadIdx.x; k < K; k += 256) row[k] = hist[k];
 }
 
-// Stable counting sort, scan part 1: one wave per cluster k scans the per-chunk counts of
-// k (chunk order) into offsets relative to the start of cluster k and writes the total.
-__global__ __launch_bounds__(256) void cl_scan_k(const int32_t* __restrict__ counts, int K, int nch,
-                                                 int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
-  const int bh = blockIdx.y, lane = threadIdx.x & 63;
-  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (k >= K) return;
-  const int32_t* cnt = counts + ((size_t)bh * K + k) * nch;
-  int32_t* off = offsets + ((size_t)bh * K + k) * nch;
-  const int per = (nch + 63) / 64;
-  const int a = min(nch, lane * per), b = min(nch, a + per);
+// Stable counting sort, scan part 1: offsets[bh][chunk][k] = number of tokens labelled k in
+// the chunks before `chunk` (chunk order), total[bh][k] = all of them. Work-group = 64
+// clusters (lane = cluster) x 16 waves; wave w takes a contiguous range of chunks, so every
+// access is a 256-byte row segment. Two passes over the wave's range: its sum, then (after
+// an exclusive scan of the 16 sums through LDS) the running offsets.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(64 * kScanWaves) void cl_scan_k(const int32_t* __restrict__ counts, int K, int nch,
+                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ total) {
+  __shared__ int part[kScanWaves][64];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + lane;
+  const bool on = k < K;
+  const int per = (nch + kScanWaves - 1) / kScanWaves;
+  const int a = min(nch, w * per), b = min(nch, a + per);
+  const int32_t* cnt = counts + (size_t)bh * nch * K + k;
+  int32_t* off = offsets + (size_t)bh * nch * K + k;
   int s = 0;
-  for (int i = a; i < b; i++) s += cnt[i];
-  int inc = s;  // inclusive wave scan of the per-lane sums
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o);
-    if (lane >= o) inc += v;
+  if (on)
+    for (int c = a; c < b; c++) s += cnt[(size_t)c * K];
+  part[w][lane] = s;
+  __syncthreads();
+  int run = 0;
+  for (int v = 0; v < w; v++) run += part[v][lane];
+  if (on) {
+    for (int c = a; c < b; c++) {
+      off[(size_t)c * K] = run;
+      run += cnt[(size_t)c * K];
+    }
+    if (w == kScanWaves - 1) total[(size_t)bh * K + k] = run;
   }
-  int run = inc - s;
-  for (int i = a; i < b; i++) {
-    off[i] = run;
-    run += cnt[i];
-  }
-  if (lane == 63) total[(size_t)bh * K + k] = inc;
 }
 
 // Scan part 2: cluster starts = exclusive scan of the totals (k order), sizes = totals.
@@ -407,7 +417,7 @@ __global__ __launch_bounds__(256) void cl_scatter(const int32_t* __restrict__ la
     const int z = lab[tid];
     int rank = 0;
     for (int i = 0; i < tid; i++) rank += (lab[i] == z);
-    perm[(size_t)bh * N + cstart[(size_t)bh * K + z] + offsets[((size_t)bh * K + z) * nch + ch] + rank] = t;
+    perm[(size_t)bh * N + cstart[(size_t)bh * K + z] + offsets[((size_t)bh * nch + ch) * K + z] + rank] = t;
   }
 }
 
@@ -615,7 +625,7 @@ extern "C" int vc_launch_cluster(const void* Vv, int B, int H, int N, int d, int
     if (d == 128) cl_assign_mfma<128><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nk, lam);
     else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nk, lam);
     cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
-    cl_scan_k<<<dim3((K + 3) / 4, BH), 256, 0, st>>>(counts, K, nch, offs, ctotal);
+    cl_scan_k<<<dim3((K + 63) / 64, BH), 64 * kScanWaves, 0, st>>>(counts, K, nch, offs, ctotal);
     cl_scan_c<<<BH, 1024, 0, st>>>(ctotal, K, cstart, csize);
     cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, cstart, perm);
     if (d == 128) cl_update<128><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, C);
@@ -646,7 +656,7 @@ extern "C" int vc_launch_cluster_inc(const void* Vv, int B, int H, int N, int d,
     else cl_assign_mfma<64><<<gmf, 256, 0, st>>>(V, chat, cnorm, N, K, labels, nullptr, 0.0f);
   }
   cl_hist<<<gch, 256, K * sizeof(int), st>>>(labels, N, K, nch, counts);
-  cl_scan_k<<<dim3((K + 3) / 4, BH), 256, 0, st>>>(counts, K, nch, offs, ctotal);
+  cl_scan_k<<<dim3((K + 63) / 64, BH), 64 * kScanWaves, 0, st>>>(counts, K, nch, offs, ctotal);
   cl_scan_c<<<BH, 1024, 0, st>>>(ctotal, K, cstart, csize);
   cl_scatter<<<gch, 256, 0, st>>>(labels, N, K, nch, offs, cstart, perm);
   if (d == 128) cl_update_inc<128><<<gk, 128, 0, st>>>(V, perm, cstart, csize, N, K, decay, C, M);
