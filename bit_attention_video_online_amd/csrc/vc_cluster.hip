@@ -52,11 +52,10 @@ __global__ void cl_prep(const float* __restrict__ C, uint16_t* __restrict__ chat
   }
 }
 
-// per-token record of one lane group: best distance' d1, the smallest distance' d2 of its
-// other centroids, and the best index
+// per-token record of one lane group: its three smallest keys, d1 <= d2 <= d3 (the low bits of
+// a key are its centroid index)
 struct Best {
-  float d1, d2;
-  int k;
+  float d1, d2, d3;
 };
 
 // exact distance (hi, lo) of a re-ranked token and its centroid index
@@ -154,16 +153,26 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   const float gam = (float)D * u / (1.0f - (float)D * u);
   // Every computed distance' d_k is within e_k = 2(2 gamma |v||c_k| + u(|c_k|^2 + |d_k|))
   // of its exact value (bf16 products are exact; the accumulation error is inside the
-  // binary32 bound). Per token and lane group the loop tracks, branch-free, only the best
-  // d1 with its index and the smallest distance' d2 of the other centroids; at the end
-  // others_lower_bound(d2) > d1 + e1 proves the best index exact. A lane group meets its
-  // centroids in increasing index order, so only a strictly smaller distance replaces the
-  // best (a tie leaves d2 = d1 and goes to the exact re-rank).
-  float d1[NG], d2[NG];
-  int kbest[NG];
+  // binary32 bound). Keys: d_k with the low kbits bits of its binary32 pattern replaced by k
+  // (the centroid count rounded up to whole chunks fits in kbits), so |key_k - d_k| <=
+  // 2^(kbits-23) |d_k| + 2^(kbits-149) (the exponent field is untouched) and the keys of
+  // different centroids differ. Per token and lane group the loop keeps, branch-free, the
+  // three smallest keys (three medians of three per distance). At the end, with x1 >= the
+  // best centroid's d and x2 (x3) <= every d_k whose key is at least the second (third)
+  // smallest: others_lower_bound(x2) > x1 + e1 proves the best index exact; otherwise
+  // others_lower_bound(x3) > x1 + e1 proves the exact argmin is one of the two smallest keys,
+  // whose two exact distances decide; otherwise the token goes to the full exact re-rank.
+  // Near ties (within the key perturbation) always fall to an exact comparison.
+  const int kpad = (K + 63) / 64 * 64;
+  const int kbits = 32 - __clz(kpad - 1);
+  const uint32_t kmask = (1u << kbits) - 1u;
+  // -inf as an operand the compiler cannot see: median(d1, key, -inf) is min(d1, key), which
+  // it would otherwise rewrite into a NaN-canonicalising max and a min (two instructions)
+  float ninf;
+  asm volatile("s_mov_b32 %0, 0xff800000" : "=s"(ninf));
+  float d1[NG], d2[NG], d3[NG];
   for (int g = 0; g < NG; g++) {
-    d1[g] = __builtin_inff(); d2[g] = __builtin_inff();
-    kbest[g] = 0x7fffffff;
+    d1[g] = __builtin_inff(); d2[g] = __builtin_inff(); d3[g] = __builtin_inff();
   }
   const v4f zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -205,46 +214,84 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
       for (int i = 0; i < 4; i++) {
         const int kl = 16 * cb + 4 * lg + i;
         const float cnk = cn_s[kl];
+        const uint32_t kk = (uint32_t)(k0 + kl);
         for (int g = 0; g < NG; g++) {
           const float dd = __builtin_fmaf(-2.0f, acc[g][i], cnk);  // exact scaling, one rounding
-          // d1 <= d2 always, so the new runner-up is the median of (d1, d2, dd); the best moves
-          // on one compare, which selects both the index and the distance
-          const bool lt = dd < d1[g];
-          kbest[g] = lt ? k0 + kl : kbest[g];
-          d2[g] = __builtin_amdgcn_fmed3f(d1[g], d2[g], dd);
-          d1[g] = lt ? dd : d1[g];
+          float key;  // (bits(dd) & ~kmask) | k as one v_and_or_b32 (the compiler splits it in two)
+          asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(key) : "v"(dd), "s"(~kmask), "v"(kk));
+          // d1 <= d2 <= d3 always: the new third is the median of (d2, d3, key), the new second
+          // that of (d1, d2, key), the new best that of (d1, key, -inf)
+          d3[g] = __builtin_amdgcn_fmed3f(d2[g], d3[g], key);
+          d2[g] = __builtin_amdgcn_fmed3f(d1[g], d2[g], key);
+          d1[g] = __builtin_amdgcn_fmed3f(d1[g], key, ninf);
         }
       }
     }
   }
   // merge the four lane groups of each token through LDS
   if (tid == 0) n_unsure = 0;
-  for (int g = 0; g < NG; g++) rec[wave * 16 * NG + g * 16 + r16][lg] = Best{d1[g], d2[g], kbest[g]};
+  for (int g = 0; g < NG; g++) rec[wave * 16 * NG + g * 16 + r16][lg] = Best{d1[g], d2[g], d3[g]};
   __syncthreads();
+  const int32_t* nkh = nk ? nk + (size_t)bh * K : nullptr;
+  auto better = [](double d2, double l2, int k2, double d, double l, int k) {
+    return d2 < d || (d2 == d && (l2 < l || (l2 == l && k2 < k)));
+  };
   if (tid < kAssignTokens && t0 + tid < N) {
-    Best a = rec[tid][0];
-    for (int x = 1; x < 4; x++) {
-      const Best& o = rec[tid][x];
-      if (o.d1 < a.d1 || (o.d1 == a.d1 && o.k < a.k)) {
-        a.d2 = fminf(fminf(a.d2, o.d2), a.d1);
-        a.d1 = o.d1; a.k = o.k;
-      } else {
-        a.d2 = fminf(fminf(a.d2, o.d2), o.d1);
+    float a1 = rec[tid][0].d1, a2 = rec[tid][0].d2, a3 = rec[tid][0].d3;  // the three smallest keys
+    auto insert = [&](float x) {  // keys are distinct, so the sorted triple stays exact
+      a3 = __builtin_amdgcn_fmed3f(a2, a3, x);
+      a2 = __builtin_amdgcn_fmed3f(a1, a2, x);
+      a1 = fminf(a1, x);
+    };
+    for (int x = 1; x < 4; x++) { insert(rec[tid][x].d1); insert(rec[tid][x].d2); insert(rec[tid][x].d3); }
+    const int k1 = (int)(__float_as_uint(a1) & kmask), k2 = (int)(__float_as_uint(a2) & kmask);
+    int label = -1;  // -1: full re-rank
+    if ((unsigned)k1 < (unsigned)K) {
+      const double vn = vn_s[tid], dg = (double)gam, du = (double)u;
+      const double delta = ldexp(1.0, kbits - 23), eta = ldexp(1.0, kbits - 149);
+      const double y1 = a1, y2 = a2, y3 = a3;
+      const double x1 = y1 + delta * fabs(y1) + eta;  // >= the best centroid's distance'
+      const double x2 = y2 - delta * fabs(y2) - eta;  // <= the distance' of every other centroid
+      const double x3 = y3 - delta * fabs(y3) - eta;  // <= that of every centroid but the first two
+      const double cnk = Nh[k1], ck = sqrt(cnk) * 1.0001;
+      const double e1 = 2.0 * (2.0 * dg * vn * ck + du * (cnk + fabs(y1) * (1.0 + delta) + eta)) * (1.0 + 1e-6);
+      const bool biased = nk != nullptr;
+      if (!(a2 < __builtin_inff()) || others_lower_bound(x2, vn, dg, du, biased) > x1 + e1) {
+        label = k1;
+      } else if ((unsigned)k2 < (unsigned)K &&
+                 (!(a3 < __builtin_inff()) || others_lower_bound(x3, vn, dg, du, biased) > x1 + e1)) {
+        // the exact argmin is k1 or k2: their exact distances (the re-rank's arithmetic)
+        const uint16_t* vr = Vh + (size_t)(t0 + tid) * D;
+        auto exact = [&](int k, double& dk, double& lk) {
+          const uint16_t* cr = Ch + (size_t)k * D;
+          double sum = 0.0;
+          for (int c8 = 0; c8 < D; c8 += 8) {
+            const uint4 va = *reinterpret_cast<const uint4*>(vr + c8), ca = *reinterpret_cast<const uint4*>(cr + c8);
+            const uint32_t wv[4] = {va.x, va.y, va.z, va.w}, wc[4] = {ca.x, ca.y, ca.z, ca.w};
+            for (int e = 0; e < 4; e++) {
+              const double dl = (double)__uint_as_float(wv[e] << 16) - (double)__uint_as_float(wc[e] << 16);
+              const double dh = (double)__uint_as_float(wv[e] & 0xffff0000u) - (double)__uint_as_float(wc[e] & 0xffff0000u);
+              sum = fma(dl, dl, sum);
+              sum = fma(dh, dh, sum);
+            }
+          }
+          double lo = 0.0;
+          if (nkh) {
+            const double b0 = (double)(lam * (float)nkh[k]);
+            const double hi = sum + b0, bb = hi - sum;
+            lo = (sum - (hi - bb)) + (b0 - bb);
+            sum = hi;
+          }
+          dk = sum; lk = lo;
+        };
+        double dA, lA, dB, lB;
+        exact(k1, dA, lA);
+        exact(k2, dB, lB);
+        label = better(dB, lB, k2, dA, lA, k1) ? k2 : k1;
       }
     }
-    bool certain = false;
-    if ((unsigned)a.k < (unsigned)K) {
-      const double vn = vn_s[tid], dg = (double)gam, du = (double)u;
-      const double cnk = Nh[a.k], ck = sqrt(cnk) * 1.0001;
-      const double e1 = 2.0 * (2.0 * dg * vn * ck + du * (cnk + fabs((double)a.d1))) * (1.0 + 1e-6);
-      certain = !(a.d2 < __builtin_inff()) ||
-                others_lower_bound((double)a.d2, vn, dg, du, nk != nullptr) > (double)a.d1 + e1;
-    }
-    if (certain) {
-      labels[(size_t)bh * N + t0 + tid] = ((unsigned)a.k < (unsigned)K) ? a.k : 0;
-    } else {
-      unsure[atomicAdd(&n_unsure, 1)] = tid;
-    }
+    if (label >= 0) labels[(size_t)bh * N + t0 + tid] = label;
+    else unsure[atomicAdd(&n_unsure, 1)] = tid;
   }
   __syncthreads();
   // exact re-rank (binary64) of the uncertain tokens, in batches of RB tokens with two
@@ -257,7 +304,6 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   // the exact pair (hi, lo) = TwoSum(s, b_k), ranked lexicographically (hi is the rounding
   // of s + b_k, and rounding is monotone); ties go to the lowest index.
   const int nu = n_unsure;
-  const int32_t* nkh = nk ? nk + (size_t)bh * K : nullptr;
   constexpr int SL = D / 8;  // features per lane
   const int sub = lane & 7, grp = lane >> 3;
   auto load_slice = [&](const uint16_t* p, double* f) {
@@ -269,9 +315,6 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
         f[8 * q + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xffff0000u);
       }
     }
-  };
-  auto better = [](double d2, double l2, int k2, double d, double l, int k) {
-    return d2 < d || (d2 == d && (l2 < l || (l2 == l && k2 < k)));
   };
   for (int u0 = 0; u0 < nu; u0 += RB) {
     const int nb = min(RB, nu - u0);

@@ -323,19 +323,23 @@ def test_cluster_ties_duplicate_centroids():
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_cluster_ties_reranked_in_batches(d):
-    """90 centroids in identical pairs (2i, 2i+1) and 10 single ones, tokens near them: a
-    token near a pair has an exact tie for its best distance and goes through the exact
-    re-rank, so every work-group re-ranks about 200 of its tokens, a count that is not a
-    multiple of the re-rank's batches (K = 100 is not a multiple of the centroids ranked per
-    step either; the last work-group holds 128 tokens). Tokens of a pair must get its even
-    index, as the oracle has it."""
-    B, H, N, NP, NS = 1, 2, 1152, 45, 10
-    K = 2 * NP + NS
-    rng = np.random.default_rng(21 + d)
-    base = (rng.integers(-6, 7, (B, H, NP + NS, d)) * 0.5).astype(np.float32)
-    C0 = np.concatenate([np.repeat(base[:, :, :NP], 2, axis=2), base[:, :, NP:]], axis=2)
-    pick = rng.integers(0, NP + NS, (B, H, N))
+@pytest.mark.parametrize("m", [2, 3])
+def test_cluster_ties_reranked_in_batches(d, m):
+    """Centroids in groups of m identical copies (45 pairs, or 30 triples) plus 10 single ones,
+    tokens near them: a token near a group has an exact tie for its best distance. With
+    pairs, the third smallest distance is clearly larger and the two tied centroids' exact
+    distances decide; with triples, the three-way tie goes through the batched exact re-rank,
+    so every work-group re-ranks about 200 of its tokens, a count that is not a multiple of
+    the re-rank's batches (K is not a multiple of the centroids ranked per step either; the
+    last work-group holds 128 tokens). Tokens of a group must get its first index, as the
+    oracle has it."""
+    B, H, N, NS = 1, 2, 1152, 10
+    NG = 90 // m
+    K = m * NG + NS
+    rng = np.random.default_rng(21 + d + 100 * m)
+    base = (rng.integers(-6, 7, (B, H, NG + NS, d)) * 0.5).astype(np.float32)
+    C0 = np.concatenate([np.repeat(base[:, :, :NG], m, axis=2), base[:, :, NG:]], axis=2)
+    pick = rng.integers(0, NG + NS, (B, H, N))
     noise = (rng.integers(-1, 2, (B, H, N, d)) * 0.5).astype(np.float32)
     noise *= rng.random((B, H, N, d)) < 0.1
     Vf = np.take_along_axis(base, pick[..., None].repeat(d, -1), axis=2) + noise
@@ -343,8 +347,8 @@ def test_cluster_ties_reranked_in_batches(d):
     lab, perm, C = _gpu_cluster(V, K, 1, False, C0)
     for h in range(H):
         l_or, p_or, c_or = oracle.kmeans(V[0, h], K, 1, cold=False, C=C0[0, h])
-        paired = l_or < 2 * NP
-        assert np.all(l_or[paired] % 2 == 0) and 0.7 < paired.mean() < 0.9
+        grouped = l_or < m * NG
+        assert np.all(l_or[grouped] % m == 0) and 0.7 < grouped.mean() < 0.95
         assert np.array_equal(lab[0, h], l_or), (h, np.count_nonzero(lab[0, h] != l_or))
         assert np.array_equal(perm[0, h], p_or)
         assert np.array_equal(C[0, h], c_or)
