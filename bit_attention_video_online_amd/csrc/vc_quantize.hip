@@ -398,27 +398,32 @@ __global__ __launch_bounds__(kQThreads) void quant_apply(const uint16_t* __restr
   // ---- mu / sV, and the packed mean operand of the attention kernel
   if (threadIdx.x < D) {
     const int c = threadIdx.x;
+    const float sv = sV[(size_t)bh * D + c];
     const float m = (flags & 2u) ? bf16_to_f32(mu[((size_t)bh * nb + j) * D + c]) : 0.0f;
-    const float ms = (flags & 2u) ? m / sV[(size_t)bh * D + c] : 0.0f;
-    if (mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = ms;
-    if (mu_pack) {
-      // mean-restoration operand, laid out as the A operands of two v_mfma_f32_32x32x16_bf16
-      // per 32-channel block: [chunk of 8 key blocks][d-block][MFMA t][lane][8]. MFMA 0:
-      // lanes 0-31 and 32-63 hold bf16(ms); MFMA 1: lanes 0-31 bf16(ms - bf16(ms)), lanes
-      // 32-63 zero; lane l carries channel 32*d-block + l%32, element s key block 8*chunk + s.
-      const int nc = (nb + 7) / 8, ch = j / 8, s8 = j % 8, db = c / 32, r = c % 32;
-      const uint16_t hi = f32_to_bf16(ms);
-      const uint16_t lo = f32_to_bf16(ms - bf16_to_f32(hi));
-      uint16_t* base = mu_pack + ((((size_t)bh * nc + ch) * (D / 32) + db) * 2 * 64) * 8;
-      base[(r) * 8 + s8] = hi;
-      base[(32 + r) * 8 + s8] = hi;
-      base[(64 + r) * 8 + s8] = lo;
-      base[(96 + r) * 8 + s8] = 0;
-      if (j == nb - 1) {  // key blocks past the end of the last chunk contribute nothing
-        for (int t = s8 + 1; t < 8; t++) {
-          base[(r) * 8 + t] = 0; base[(32 + r) * 8 + t] = 0; base[(64 + r) * 8 + t] = 0; base[(96 + r) * 8 + t] = 0;
-        }
+    if (mu_scaled) mu_scaled[((size_t)bh * nb + j) * D + c] = (flags & 2u) ? m / sv : 0.0f;
+    // mean-restoration operand, laid out as the A operands of two v_mfma_f32_32x32x16_bf16
+    // per 32-channel block: [chunk of 8 key blocks][d-block][MFMA t][lane][8]. MFMA 0:
+    // lanes 0-31 and 32-63 hold bf16(ms); MFMA 1: lanes 0-31 bf16(ms - bf16(ms)), lanes
+    // 32-63 zero; lane l carries channel 32*d-block + l%32, element s key block 8*chunk + s
+    // (zero past the last key block). The last block of each chunk writes the whole chunk,
+    // from the chunk's block means, as four 16-byte stores per channel.
+    const int s8 = j % 8;
+    if (mu_pack && (s8 == 7 || j == nb - 1)) {
+      const int nc = (nb + 7) / 8, ch = j / 8, db = c / 32, r = c % 32;
+      uint32_t hw[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+      for (int t = 0; t <= s8; t++) {
+        const float mt = (flags & 2u) ? bf16_to_f32(mu[((size_t)bh * nb + 8 * ch + t) * D + c]) : 0.0f;
+        const float ms = (flags & 2u) ? mt / sv : 0.0f;
+        const uint32_t hi = f32_to_bf16(ms);
+        const uint32_t lo = f32_to_bf16(ms - bf16_to_f32((uint16_t)hi));
+        hw[t / 2] |= hi << (16 * (t & 1));
+        lw[t / 2] |= lo << (16 * (t & 1));
       }
+      uint4* base = reinterpret_cast<uint4*>(mu_pack + ((((size_t)bh * nc + ch) * (D / 32) + db) * 2 * 64) * 8);
+      base[r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      base[32 + r] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      base[64 + r] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      base[96 + r] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
 }
