@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.vc_cluster_workspace_bytes.argtypes = [I, I, I, I, I]
         L.vc_cluster.restype = I
         L.vc_cluster.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, S, P]
+        L.vc_exponent_span.restype = I
+        L.vc_exponent_span.argtypes = [P, I, I, I, I, I, P, P]
         L.vc_cluster_balanced.restype = I
         L.vc_cluster_balanced.argtypes = [P, I, I, I, I, I, I, I, ctypes.c_float, P, P, P, P, P, S, P]
         L.vc_quantize_workspace_bytes.restype = S
@@ -267,6 +269,26 @@ def vc_cluster_cost(V, C, labels, cost, ws=None, stream=None):
     _check(lib().vc_cluster_cost(_ptr(V), _ptr(C), _ptr(labels), B, H, N, d, K, _ptr(cost), _ptr(ws), ws.numel(),
                                  _stream(stream)))
     return cost
+
+
+def vc_exponent_span(X, as_bf16=False, stream=None):
+    """Exponent range per (b,h) of X ([B,H,rows,d] bf16 or float32; float32 read as the bf16
+    value it rounds to with as_bf16): int32 [B,H,2] = (largest exponent, lowest significand
+    bit exponent) over the nonzero finite elements; (INT32_MIN, INT32_MAX) for an all-zero head."""
+    if X.dim() != 4:
+        raise ValueError("X must be [B,H,rows,d]")
+    B, H, R, d = X.shape
+    if X.dtype == torch.bfloat16:
+        kind = 0
+    elif X.dtype == torch.float32:
+        kind = 2 if as_bf16 else 1
+    else:
+        raise ValueError("X must be bfloat16 or float32")
+    if not X.is_contiguous():
+        raise ValueError("X must be contiguous")
+    out = torch.empty((B, H, 2), dtype=torch.int32, device=X.device)
+    _check(lib().vc_exponent_span(_ptr(X), kind, B, H, R, d, _ptr(out), _stream(stream)))
+    return out
 
 
 def vc_attention(q, O, beta=-0.35, flags=VC_F_EXPCAST, restore_mean=True, stream=None, block=BLOCK):

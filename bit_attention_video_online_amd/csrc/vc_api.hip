@@ -30,6 +30,8 @@ extern "C" size_t vc_cluster_ws_bytes(int B, int H, int N, int d, int K);
 extern "C" int vc_launch_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold, float* C,
                                  int32_t* labels, int32_t* perm, void* ws, hipStream_t st, float lam, int32_t* nk_io);
 extern "C" int vc_max_clusters(void);
+extern "C" int vc_launch_exponent_span(const void* X, int kind, int BH, long long per_head, int32_t* out,
+                                       hipStream_t st);
 extern "C" int vc_launch_cluster_inc(const void* V, int B, int H, int N, int d, int K, float decay, int assign,
                                      float* C, float* M, int32_t* labels, int32_t* perm, void* ws, hipStream_t st);
 
@@ -209,6 +211,23 @@ extern "C" vc_status vc_cluster_cost(const void* V, const float* centroids, cons
   if (const vc_status dc = device_check()) return dc;
   if (vc_launch_cluster_cost(V, centroids, labels, B, H, N, d, K, cost, workspace, (hipStream_t)stream) != 0)
     return VC_E_HIP;
+  return VC_OK;
+}
+
+extern "C" vc_status vc_exponent_span(const void* X, int kind, int B, int H, int rows, int d, int32_t* out,
+                                      void* stream) {
+  if (!X || !out) return VC_E_NULLPTR;
+  if (kind < 0 || kind > 2) return VC_E_PARAM;
+  if (B < 1 || H < 1 || rows < 1 || d < 1) return VC_E_SHAPE;
+  const long long per_head = (long long)rows * d;
+  if ((long long)B * H * per_head >= (1LL << 31)) return VC_E_SHAPE;
+  const size_t esz = kind == 0 ? 2 : 4;
+  if ((((uintptr_t)X) & (esz - 1)) || (((uintptr_t)out) & 3u)) return VC_E_UNSUPPORTED;
+  const Range o{(const char*)out, (size_t)B * H * 2 * sizeof(int32_t)};
+  const Range i{(const char*)X, (size_t)(B * (long long)H * per_head) * esz};
+  if (overlaps(o, i)) return VC_E_ALIAS;
+  if (const vc_status dc = device_check()) return dc;
+  if (vc_launch_exponent_span(X, kind, B * H, per_head, out, (hipStream_t)stream) != 0) return VC_E_HIP;
   return VC_OK;
 }
 

@@ -708,3 +708,92 @@ extern "C" int vc_launch_cluster_inc(const void* Vv, int B, int H, int N, int d,
 }
 
 extern "C" int vc_max_clusters(void) { return kMaxClusters; }
+
+// ---------------------------------------------------------------------------
+// Exponent range of a tensor per (b,h), the quantity the exactness conditions of the binary64
+// sums and distances are stated in: over the nonzero finite elements, the largest exponent
+// e = floor(log2|x|) and the smallest exponent of a lowest set significand bit (every element
+// is an integer multiple of 2^that). kind 0: bf16 bit patterns; 1: binary32; 2: binary32 taken
+// as the bf16 value it rounds to (nearest even), as the assignment reads centroids.
+namespace vc {
+
+__global__ void span_init(int32_t* __restrict__ out, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    out[2 * i] = INT32_MIN;
+    out[2 * i + 1] = INT32_MAX;
+  }
+}
+
+// e and q of one element given its biased exponent field, significand field and format widths;
+// returns false for zero, infinity and NaN
+__device__ __forceinline__ bool elem_exponents(uint32_t ef, uint32_t mant, int mbits, int& e, int& q) {
+  const uint32_t emaxf = 0xFFu;
+  if (ef == emaxf) return false;
+  if (ef == 0 && mant == 0) return false;
+  const int qsub = -126 - mbits;  // exponent of the last bit of a subnormal
+  if (ef == 0) {
+    e = (31 - __clz(mant)) + qsub;
+    q = qsub + __ffs(mant) - 1;
+  } else {
+    const uint32_t sig = mant | (1u << mbits);
+    e = (int)ef - 127;
+    q = e - mbits + __ffs(sig) - 1;
+  }
+  return true;
+}
+
+__global__ __launch_bounds__(256) void span_kernel(const void* __restrict__ X, int kind, long long per_head,
+                                                   int32_t* __restrict__ out) {
+  __shared__ int red[2][4];
+  const int bh = blockIdx.y;
+  int emax = INT32_MIN, qmin = INT32_MAX;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < per_head; i += stride) {
+    uint32_t ef, mant;
+    int mbits;
+    if (kind == 0) {
+      const uint32_t h = reinterpret_cast<const uint16_t*>(X)[(size_t)bh * per_head + i];
+      ef = (h >> 7) & 0xFFu; mant = h & 0x7Fu; mbits = 7;
+    } else {
+      uint32_t f = __float_as_uint(reinterpret_cast<const float*>(X)[(size_t)bh * per_head + i]);
+      if (kind == 2) {
+        if (((f >> 23) & 0xFFu) == 0xFFu) continue;  // infinity or NaN
+        f = (uint32_t)f32_to_bf16(__uint_as_float(f)) << 16;
+        ef = (f >> 23) & 0xFFu; mant = (f >> 16) & 0x7Fu; mbits = 7;
+      } else {
+        ef = (f >> 23) & 0xFFu; mant = f & 0x7FFFFFu; mbits = 23;
+      }
+    }
+    int e, q;
+    if (elem_exponents(ef, mant, mbits, e, q)) {
+      emax = max(emax, e);
+      qmin = min(qmin, q);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    emax = max(emax, __shfl_xor(emax, o));
+    qmin = min(qmin, __shfl_xor(qmin, o));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { red[0][w] = emax; red[1][w] = qmin; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; k++) { emax = max(emax, red[0][k]); qmin = min(qmin, red[1][k]); }
+    if (emax != INT32_MIN) {  // max and min are order-free: the result is deterministic
+      atomicMax(&out[2 * bh], emax);
+      atomicMin(&out[2 * bh + 1], qmin);
+    }
+  }
+}
+
+}  // namespace vc
+
+extern "C" int vc_launch_exponent_span(const void* X, int kind, int BH, long long per_head, int32_t* out,
+                                       hipStream_t st) {
+  vc::span_init<<<(BH + 255) / 256, 256, 0, st>>>(out, BH);
+  const long long blocks = (per_head + 256LL * 16 - 1) / (256LL * 16);
+  const int gx = (int)(blocks < 1024 ? (blocks < 1 ? 1 : blocks) : 1024);
+  vc::span_kernel<<<dim3(gx, BH), 256, 0, st>>>(X, kind, per_head, out);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

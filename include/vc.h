@@ -66,6 +66,56 @@ enum {
 /* Static description of a status code (host function, never NULL). */
 const char* vc_status_string(vc_status s);
 
+/* ------------------------------------------------------------------------
+ * Exactness of the binary64 arithmetic. The k-means re-rank and pair decision, the
+ * centroid, block-mean and key-mean sums are binary64 sums of bf16 values; the readings
+ * they implement (exact argmin, exact means rounded once) hold whenever those sums are
+ * exact. In terms of vc_exponent_span below -- E(X) the largest exponent and q(X) the
+ * lowest significand bit over the nonzero elements of a (b,h), s(X) = E(X) - q(X) --
+ * sufficient conditions per (b,h) are:
+ *   - sums of n elements of X are exact when s(X) <= 52 - ceil(log2 n) (every partial
+ *     sum is a multiple of 2^q(X) below n 2^(E(X)+1) <= 2^(q(X)+53)). vc_quantize: the
+ *     key mean needs s(K) <= 52 - ceil(log2 N) (of the rotated keys when RoPE tables are
+ *     given), the block means s(V) <= 45. vc_cluster, vc_cluster_balanced,
+ *     vc_cluster_incremental: the member sums need s(V) <= 52 - ceil(log2 N) (35 at
+ *     N = 70 400).
+ *   - the exact squared distances sum_c (v_c - c_c)^2 (d terms) of the k-means ranking
+ *     are exact when the span of V together with the bf16-rounded centroids the
+ *     assignment reads (vc_exponent_span kind 2) is at most (49 - ceil(log2 d)) / 2,
+ *     i.e. 21 for d = 64 and 128 (each difference is a multiple of 2^q below 2^(E+2));
+ *     and the binary32 error bound that proves most labels without them assumes every
+ *     nonzero |v| and |c| in [2^-56, 2^56) (no overflow or underflow in the products and
+ *     norms): E <= 55 and q >= -56. With iters > 1 the centroids an assignment reads are
+ *     the previous update's; run one iteration per call to check each.
+ * Outside these conditions the kernels still terminate and the binary64 values are
+ * within n 2^-53 (relative to the sum of magnitudes) of the exact ones: a label can then
+ * differ from the exact argmin only where the two best exact squared distances of a
+ * token differ by less than about 2^-45 of their size, and a mean only where its exact
+ * value lies that close to a rounding boundary. Real-valued data usually exceeds these
+ * sufficient conditions (a few elements near zero widen the span) while such near ties
+ * stay rare: two Wan-shaped test heads have V spans of 35 and 36 and K spans of 29 and
+ * 30, and every Wan head matches the oracle bit for bit. The oracle is exact for every
+ * finite input.
+ * ------------------------------------------------------------------------ */
+
+/* ------------------------------------------------------------------------
+ * vc_exponent_span -- the exponent range of a tensor per (batch, head), for the
+ * conditions above.
+ *
+ *   X     device, [B,H,rows,d] contiguous; kind 0: bf16 bit patterns, kind 1: binary32,
+ *         kind 2: binary32 read as the bf16 value it rounds to (nearest even), as the
+ *         k-means assignment reads centroids. 2-byte (kind 0) or 4-byte aligned.
+ *   out   device int32 [B,H,2], 4-byte aligned: out[2 bh] = E = the largest
+ *         floor(log2 |x|), out[2 bh + 1] = q = the smallest exponent of a lowest set
+ *         significand bit (every element is an integer multiple of 2^q), both over the
+ *         nonzero finite elements of (b,h); an all-zero (b,h) gives (INT32_MIN, INT32_MAX).
+ *         The span of a union is max(E) - min(q) of the parts.
+ *   B, H, rows, d >= 1 with B*H*rows*d < 2^31; X and out must not overlap.
+ * Deterministic (maxima and minima). Errors: VC_E_NULLPTR, VC_E_PARAM (kind), VC_E_SHAPE,
+ * VC_E_UNSUPPORTED (alignment, no gfx950), VC_E_ALIAS, VC_E_HIP.
+ * ------------------------------------------------------------------------ */
+vc_status vc_exponent_span(const void* X, int kind, int B, int H, int rows, int d, int32_t* out, void* stream);
+
 /* ABI version of this header (bumped on any incompatible change). */
 int vc_abi_version(void);
 #define VC_ABI_VERSION 2
@@ -92,8 +142,8 @@ int vc_abi_version(void);
  * (exact products; accumulation error measured far inside the binary32 bound the
  * test uses), keeps a rigorous per-distance error bound, and re-ranks in binary64
  * every token whose best candidate is not separated from the rest by the bounds, so
- * labels equal the exact argmin whenever the binary64 squared distances are exact
- * (always, for values whose per-token exponent span is below 2^18).
+ * labels equal the exact argmin whenever the binary64 squared distances are exact (the
+ * "Exactness" conditions above; vc_exponent_span checks them).
  * ------------------------------------------------------------------------ */
 size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K);
 vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,

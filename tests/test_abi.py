@@ -204,6 +204,7 @@ def test_valid_calls_need_a_gfx950_device(L):
     assert L.vc_debug_mfma_f8(A, B, C, D, 1, None) == 5
     assert L.vc_debug_expcast(A, B, C, D, 4, None) == 5
     assert L.vc_debug_mfma_peak(1, 1, 0, ctypes.c_void_p(1 << 20), None) == 5
+    assert L.vc_exponent_span(A, 0, 1, 1, 4, 4, B, None) == 5
 
 
 def test_quantize_noalloc_rejects_bad_arguments(L):
@@ -242,3 +243,21 @@ def test_cluster_incremental_rejects_bad_arguments(L):
     assert call(wsb=8) == 4
     assert call(M=ctypes.c_void_p((5 << 20) + 4)) == 5
     assert call(M=ctypes.c_void_p(2 << 20)) == 7        # mass aliases labels
+
+
+def test_exponent_span_rejects_bad_arguments(L):
+    def call(**kw):
+        a = dict(X=ctypes.c_void_p(1 << 20), kind=0, B=1, H=2, rows=64, d=128, out=ctypes.c_void_p(2 << 20))
+        a.update(kw)
+        return L.vc_exponent_span(a["X"], a["kind"], a["B"], a["H"], a["rows"], a["d"], a["out"], None)
+    assert call(X=None) == 1
+    assert call(out=None) == 1
+    assert call(kind=3) == 3
+    assert call(kind=-1) == 3
+    assert call(rows=0) == 2
+    assert call(d=0) == 2
+    assert call(B=1 << 16, H=1 << 10, rows=32, d=1) == 2         # 2^31 elements
+    assert call(X=ctypes.c_void_p((1 << 20) + 1)) == 5            # bf16 needs 2-byte alignment
+    assert call(kind=1, X=ctypes.c_void_p((1 << 20) + 2)) == 5    # binary32 needs 4
+    assert call(out=ctypes.c_void_p((2 << 20) + 2)) == 5
+    assert call(out=ctypes.c_void_p((1 << 20) + 64)) == 7         # out inside X

@@ -672,3 +672,70 @@ def test_cluster_incremental_bitexact(d, N, K, decay, assign):
             assert np.array_equal(pd.cpu().numpy()[0, h], p_or), (step, h)
             assert np.array_equal(Cd.cpu().numpy()[0, h], c_or), (step, h)
             assert np.array_equal(Md.cpu().numpy()[0, h], m_or), (step, h)
+
+
+def _span_reference(x64: np.ndarray):
+    """(largest floor(log2|x|), smallest exponent of a lowest set significand bit) over the
+    nonzero finite values, from frexp on binary64 (exact for bf16 and binary32 values)."""
+    v = np.abs(x64[np.isfinite(x64) & (x64 != 0)])
+    if v.size == 0:
+        return (-(2 ** 31), 2 ** 31 - 1)
+    m, e = np.frexp(v)
+    M = (m * 2.0 ** 53).astype(np.uint64)           # exact: at most 24 significant bits
+    tz = np.zeros(M.shape, np.int64)
+    r = M.copy()
+    while True:
+        odd = (r & np.uint64(1)) == 1
+        if odd.all():
+            break
+        tz += ~odd
+        r = np.where(odd, r, r >> np.uint64(1))
+    return (int((e - 1).max()), int((e - 53 + tz).min()))
+
+
+def test_exponent_span_matches_reference():
+    """vc_exponent_span on bf16 and binary32 tensors (and binary32 read as bf16) against an
+    independent frexp computation: random values over a wide exponent range, subnormals,
+    signed zeros, infinities and NaNs (ignored), one all-zero head."""
+    rng = np.random.default_rng(61)
+    B, H, R, d = 2, 3, 70, 24
+    x = (rng.standard_normal((B, H, R, d)) * np.exp2(rng.integers(-40, 40, (B, H, R, d)))).astype(np.float32)
+    x[0, 1] = 0.0
+    x[0, 1, 3, 3] = -0.0
+    x[1, 0, 0, :4] = [np.float32(1e-40), np.float32(-3e-45), np.inf, np.nan]   # binary32 subnormals, specials
+    x[1, 2, 5, 5] = np.float32(3.0e38)
+    xb = synth.bf16_bits(np.nan_to_num(x, nan=0.0, posinf=0.0))
+    xb[1, 1, 0, 0] = 0x0001                                                    # smallest bf16 subnormal
+    xb[1, 1, 0, 1] = 0x7F80                                                    # bf16 infinity: ignored
+    got_b = vc.vc_exponent_span(to_dev_bf16(xb)).cpu().numpy()
+    got_f = vc.vc_exponent_span(to_dev(x)).cpu().numpy()
+    got_r = vc.vc_exponent_span(to_dev(x), as_bf16=True).cpu().numpy()
+    xr = synth.bf16_to_f32(synth.bf16_bits(np.nan_to_num(x, nan=0.0, posinf=0.0))).astype(np.float64)
+    for b in range(B):
+        for h in range(H):
+            assert tuple(got_b[b, h]) == _span_reference(synth.bf16_to_f32(xb[b, h]).astype(np.float64)), (b, h)
+            assert tuple(got_f[b, h]) == _span_reference(x[b, h].astype(np.float64)), (b, h)
+            assert tuple(got_r[b, h]) == _span_reference(xr[b, h]), (b, h)
+    assert tuple(got_b[0, 1]) == (-(2 ** 31), 2 ** 31 - 1)
+
+
+def test_exponent_span_of_the_video_workload_heads():
+    """The checker on Wan-shaped heads (V, keys, and the bf16 centroids after k-means), printed
+    against the exactness conditions of include/vc.h; the values must equal the reference."""
+    N, d, K = 70400, 128, 550
+    hs = [synth.gen_head("wan", 2, 0, h, N, d) for h in (0, 23)]
+    V = np.stack([w["V"] for w in hs])[None]
+    Kt = np.stack([w["K"] for w in hs])[None]
+    lab, perm, C = _gpu_cluster(V, K, 2, True)
+    sv = vc.vc_exponent_span(to_dev_bf16(V)).cpu().numpy()[0]
+    sk = vc.vc_exponent_span(to_dev_bf16(Kt)).cpu().numpy()[0]
+    sc = vc.vc_exponent_span(to_dev(C), as_bf16=True).cpu().numpy()[0]
+    lim_sum = 52 - int(np.ceil(np.log2(N)))
+    for i in range(2):
+        assert tuple(sv[i]) == _span_reference(synth.bf16_to_f32(V[0, i]).astype(np.float64))
+        assert tuple(sc[i]) == _span_reference(synth.bf16_to_f32(synth.bf16_bits(C[0, i])).astype(np.float64))
+        dist_span = max(sv[i][0], sc[i][0]) - min(sv[i][1], sc[i][1])
+        print("[span] head %d: V (E %d, q %d, span %d), K span %d, V with bf16 centroids span %d; sums exact "
+              "below %d: V %s, K %s; distances exact below 21: %s"
+              % (i, sv[i][0], sv[i][1], sv[i][0] - sv[i][1], sk[i][0] - sk[i][1], dist_span, lim_sum,
+                 sv[i][0] - sv[i][1] <= lim_sum, sk[i][0] - sk[i][1] <= lim_sum, dist_span <= 21), flush=True)
