@@ -46,8 +46,10 @@ float log2e_over_sqrt_d(int d) {
   return f;
 }
 
+// B*H is a grid dimension of several kernels (at most 65535)
 bool shape_ok(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || (N % 128) != 0 || (d != 64 && d != 128)) return false;
+  if ((long long)B * H > 65535) return false;
   const long long el = (long long)B * H * N * d;
   return el < (1LL << 31);
 }
@@ -218,7 +220,7 @@ extern "C" vc_status vc_exponent_span(const void* X, int kind, int B, int H, int
                                       void* stream) {
   if (!X || !out) return VC_E_NULLPTR;
   if (kind < 0 || kind > 2) return VC_E_PARAM;
-  if (B < 1 || H < 1 || rows < 1 || d < 1) return VC_E_SHAPE;
+  if (B < 1 || H < 1 || rows < 1 || d < 1 || (long long)B * H > 65535) return VC_E_SHAPE;
   const long long per_head = (long long)rows * d;
   if ((long long)B * H * per_head >= (1LL << 31)) return VC_E_SHAPE;
   const size_t esz = kind == 0 ? 2 : 4;

@@ -28,7 +28,7 @@
  *     reported as VC_E_HIP; faults inside kernels surface at the caller's next
  *     synchronisation, as for any HIP work.
  *   - Supported shapes: d in {64, 128}; block == 128; N a positive multiple of
- *     128; B, H >= 1; B*H*N*d < 2^31. Buffers must be 16-byte aligned.
+ *     128; B, H >= 1; B*H <= 65535; B*H*N*d < 2^31. Buffers must be 16-byte aligned.
  *   - NaN or infinite inputs are not supported: outputs are then unspecified, but
  *     every kernel still terminates.
  */
@@ -110,7 +110,7 @@ const char* vc_status_string(vc_status s);
  *         significand bit (every element is an integer multiple of 2^q), both over the
  *         nonzero finite elements of (b,h); an all-zero (b,h) gives (INT32_MIN, INT32_MAX).
  *         The span of a union is max(E) - min(q) of the parts.
- *   B, H, rows, d >= 1 with B*H*rows*d < 2^31; X and out must not overlap.
+ *   B, H, rows, d >= 1 with B*H <= 65535 and B*H*rows*d < 2^31; X and out must not overlap.
  * Deterministic (maxima and minima). Errors: VC_E_NULLPTR, VC_E_PARAM (kind), VC_E_SHAPE,
  * VC_E_UNSUPPORTED (alignment, no gfx950), VC_E_ALIAS, VC_E_HIP.
  * ------------------------------------------------------------------------ */

@@ -85,6 +85,7 @@ def test_quantize_rejects_bad_arguments(L):
     assert _quant(L, d=96) == 2
     assert _quant(L, block=64) == 2
     assert _quant(L, B=0) == 2
+    assert _quant(L, B=256, H=256, N=128, d=64) == 2   # B*H beyond the 65535 grid limit
     assert _quant(L, flags=64) == 3
     assert _quant(L, wsb=16) == 4
     assert _quant(L, Qq=ctypes.c_void_p((1 << 20) + 4)) == 5   # misaligned
@@ -257,6 +258,7 @@ def test_exponent_span_rejects_bad_arguments(L):
     assert call(rows=0) == 2
     assert call(d=0) == 2
     assert call(B=1 << 16, H=1 << 10, rows=32, d=1) == 2         # 2^31 elements
+    assert call(B=256, H=256, rows=1, d=1) == 2                   # B*H above the grid limit
     assert call(X=ctypes.c_void_p((1 << 20) + 1)) == 5            # bf16 needs 2-byte alignment
     assert call(kind=1, X=ctypes.c_void_p((1 << 20) + 2)) == 5    # binary32 needs 4
     assert call(out=ctypes.c_void_p((2 << 20) + 2)) == 5
