@@ -549,6 +549,26 @@ def test_inkernel_expcast_bytes_bitexact_tiny(e5m2):
           % ("e5m2" if e5m2 else "e4m3", ["%.5f" % a for a in exact_agree]))
 
 
+@pytest.mark.parametrize("d,mx", [(64, False), (128, True), (64, True)])
+def test_inkernel_expcast_bytes_bitexact_d64_and_mxfp4(d, mx):
+    """The same byte check for the other kernel instantiations that ship ExpCast: d = 64 (one
+    matrix-core instruction per score, C = 0) and the 4-bit (MXFP4) value residual, whose V
+    tiles and PV instruction differ but whose scores and bytes must not; blocks 0, 3 and 7."""
+    N = 1024
+    w = synth.gen("tiny", d=d)
+    perm = synth.rand_perm(N, 2)
+    fl = FLAGS_ALL | (vc.VC_F_MXFP4 if mx else 0)
+    out = gpu_quantize(w["Q"], w["K"], w["V"], perm[None, None], fl)
+    q_or = oracle.quantize(w["Q"][0, 0], w["K"][0, 0], w["V"][0, 0], perm,
+                           oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH | (oracle.FLAG_MXFP4 if mx else 0))
+    rows = np.arange(N, dtype=np.int32)
+    for blk in (0, 3, 7):
+        O, codes = _gpu_attention(out, N, d, 1, 1, True, True, dump_block=blk, mx=mx)
+        O_or, c_or = emul(q_or, rows, beta=BETA, mode=oracle.MODE_EXPCAST, dump_block=blk)
+        assert np.array_equal(codes[0, 0], c_or), (blk, np.count_nonzero(codes[0, 0] != c_or))
+        assert rel_l2(_o_f64(O[0, 0]), O_or) <= TOL, blk
+
+
 # ------------------------------------------------------------------ properties at any size
 def test_perm_is_stable_sort_of_labels():
     w = synth.gen("wan", seed=13, B=1, H=3, N=4096, d=128)
