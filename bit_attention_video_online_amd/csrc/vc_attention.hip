@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
   // mu_hi x w_hi, slots 8..15 (lanes 32-63) mu_hi x w_lo, and the second MFMA mu_lo x w_hi.
   // Log layout per wave [slot][query]: 32 lanes touch 256 contiguous bytes.
   float2* const rlog = rlog_all + wave * (8 * 32);
-  auto flush = [&](int nvalid) {
+  auto flush = [&](int nvalid, float mref) {
     float2 t[8];
     for (int k = 0; k < 8; k++) t[k] = rlog[k * 32 + r32];
     // pairs of weights: hi = bf16(w) and lo = bf16(w - hi), two per conversion; lanes of
@@ -294,8 +294,8 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     v8i w0, w1;
     for (int k2 = 0; k2 < 4; k2++) {
       f32x2 w;
-      w.x = 2 * k2 < nvalid ? t[2 * k2].x * __builtin_amdgcn_exp2f(t[2 * k2].y - m) : 0.0f;
-      w.y = 2 * k2 + 1 < nvalid ? t[2 * k2 + 1].x * __builtin_amdgcn_exp2f(t[2 * k2 + 1].y - m) : 0.0f;
+      w.x = 2 * k2 < nvalid ? t[2 * k2].x * __builtin_amdgcn_exp2f(t[2 * k2].y - mref) : 0.0f;
+      w.y = 2 * k2 + 1 < nvalid ? t[2 * k2 + 1].x * __builtin_amdgcn_exp2f(t[2 * k2 + 1].y - mref) : 0.0f;
       const bf16x2 hb = __builtin_convertvector(w, bf16x2);
       uint32_t hp;
       __builtin_memcpy(&hp, &hb, 4);
@@ -371,7 +371,6 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     using Other = std::integral_constant<int, 1 - p>;
     const uint8_t* vt = p ? vst1 : vst0;  // V_j
     const float sigma = sq * uniform_load(sKh, j);
-    if (RESTORE && j > 0 && (j & 7) == 0) flush(8);  // chunk j/8 - 1 is complete
     if (j + 2 < nb) issue_k(j + 2, P);                 // replaces K_j, consumed in iteration j-1
     if (j + 1 < nb) issue_v(j + 1, Other{});           // replaces V_{j-1}
     // chunk c = j/8 replaces chunk c-1, which every wave flushed before the last barrier
@@ -460,6 +459,7 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
     pv_part(vt, 1, pf[1]);
     s_part(Other{}, 2);
     __builtin_amdgcn_s_setprio(0);
+    if (RESTORE && j > 0 && (j & 7) == 0) flush(8, mp);  // chunk j/8 - 1, scaled to the new max
     r = EXPCAST ? rs[0] : lane_sum2(r);
 
     lsum = __builtin_fmaf(alpha, lsum, r);
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kAThreads, 8 / kWaves) void attn_fwd(const uint8_t*
       wait_copies();
       wg_barrier();
     }
-    flush(nb - 8 * clast);
+    flush(nb - 8 * clast, m);
   }
 
   // ---- epilogue: O = bf16(sV * A / l); element i of block db is channel 32 db + 8(i/4) + 4h + i%4
