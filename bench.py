@@ -560,7 +560,7 @@ def main():
         print(json.dumps({"calibration_copy_bytes": x.numel()}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; the path shards by (batch, head) with no exchange, "
+        print("bench.py: runs on exactly one GPU; the path shards by (batch, head) with no exchange, "
               "but multi-GPU runs are not part of it (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
