@@ -10,18 +10,17 @@
 // Kernels, per iteration:
 //   cl_prep    chat = bf16(C) (bf16 bits), |chat|^2
 //   cl_assign_mfma  distances |c|^2 - 2 v.c with the dot products on bf16 MFMA, a
-//              rigorous per-distance error bound, and a binary64 re-rank of every token
-//              whose best candidate is not separated from the rest by the bounds (exact
-//              for bf16 data of moderate dynamic range).
+//              rigorous per-distance error bound, and an exact re-rank (binary64 pairs) of
+//              every token whose best candidate is not separated from the rest by the bounds.
 //   cl_hist / cl_scan_k / cl_scan_c / cl_scatter   stable counting sort of the labels (pi)
-//   cl_update  C_k = fl32(sum of members / count), binary64 sums in pi order
+//   cl_update  C_k = fl32(exact sum of members / count), sums as binary64 pairs in pi order
 // Size-penalised variant (cheap balancing; the paper page's ablation measures balanced
 // k-means and sets it aside for its cost): every distance gets b_k = fl32(lambda n_k),
 // n_k the size of cluster k after the previous assignment, folded into |chat_k|^2 by
 // cl_prep, so the assignment loop is unchanged; only the certainty bound and the exact
 // re-rank take b_k into account.
 // No atomics on floating-point data: every result is run-to-run deterministic.
-#include "vc_device.h"
+#include "vc_exact.h"
 
 namespace vc {
 
@@ -90,7 +89,7 @@ __device__ __forceinline__ double others_lower_bound(double x, double vn, double
 // bf16 products are exact and the accumulation error of the instruction chain was
 // measured at <= 2^-21.3 sum|v_c chat_c| on adversarial wide-range data, far inside
 // the binary32 recursive-summation bound gamma_d sum|v_c chat_c| used below (doubled),
-// so the same certainty test and binary64 re-rank apply.
+// so the same certainty test and exact re-rank apply.
 // Work-group: 4 waves x 64 tokens (four 16-token groups), so every staged centroid chunk
 // serves 256 tokens. Centroid chunks of 64 rows of
 // bf16 are staged in LDS with a padded row stride (conflict-free 16-byte fragment
@@ -236,6 +235,13 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
   auto better = [](double d2, double l2, int k2, double d, double l, int k) {
     return d2 < d || (d2 == d && (l2 < l || (l2 == l && k2 < k)));
   };
+  // normalised exact distance pair plus the size penalty b_k = fl32(lam n_k), normalised again
+  auto with_bias = [&](const dpair& d, int k) {
+    if (!nkh) return d;
+    double h, e;
+    two_sum(d.hi, (double)(lam * (float)nkh[k]), h, e);
+    return dp_norm(dpair{h, d.lo + e});
+  };
   if (tid < kAssignTokens && t0 + tid < N) {
     float a1 = rec[tid][0].d1, a2 = rec[tid][0].d2, a3 = rec[tid][0].d3;  // the three smallest keys
     auto insert = [&](float x) {  // keys are distinct, so the sorted triple stays exact
@@ -264,45 +270,70 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
         const uint16_t* vr = Vh + (size_t)(t0 + tid) * D;
         auto exact = [&](int k, double& dk, double& lk) {
           const uint16_t* cr = Ch + (size_t)k * D;
-          double sum = 0.0;
+          dpair sum{0.0, 0.0};
           for (int c8 = 0; c8 < D; c8 += 8) {
             const uint4 va = *reinterpret_cast<const uint4*>(vr + c8), ca = *reinterpret_cast<const uint4*>(cr + c8);
             const uint32_t wv[4] = {va.x, va.y, va.z, va.w}, wc[4] = {ca.x, ca.y, ca.z, ca.w};
             for (int e = 0; e < 4; e++) {
               const double dl = (double)__uint_as_float(wv[e] << 16) - (double)__uint_as_float(wc[e] << 16);
               const double dh = (double)__uint_as_float(wv[e] & 0xffff0000u) - (double)__uint_as_float(wc[e] & 0xffff0000u);
-              sum = fma(dl, dl, sum);
-              sum = fma(dh, dh, sum);
+              dp_add_sq(sum, dl);
+              dp_add_sq(sum, dh);
             }
           }
-          double lo = 0.0;
-          if (nkh) {
-            const double b0 = (double)(lam * (float)nkh[k]);
-            const double hi = sum + b0, bb = hi - sum;
-            lo = (sum - (hi - bb)) + (b0 - bb);
-            sum = hi;
-          }
-          dk = sum; lk = lo;
+          const dpair r = with_bias(dp_norm(sum), k);
+          dk = r.hi; lk = r.lo;
         };
-        double dA, lA, dB, lB;
-        exact(k1, dA, lA);
-        exact(k2, dB, lB);
-        label = better(dB, lB, k2, dA, lA, k1) ? k2 : k1;
+        // binary64 first: the terms are non-negative, so each computed distance (with b_k: one
+        // more rounding) is within (D + 2) 2^-53 of its exact value, relatively; when the two
+        // differ by more than both bounds their order is the exact one, otherwise the exact
+        // pairs decide
+        const uint16_t *ca = Ch + (size_t)k1 * D, *cb = Ch + (size_t)k2 * D;
+        double sA = 0.0, sB = 0.0;
+        for (int c8 = 0; c8 < D; c8 += 8) {
+          const uint4 va = *reinterpret_cast<const uint4*>(vr + c8), xa = *reinterpret_cast<const uint4*>(ca + c8),
+                      xb = *reinterpret_cast<const uint4*>(cb + c8);
+          const uint32_t wv[4] = {va.x, va.y, va.z, va.w}, wa[4] = {xa.x, xa.y, xa.z, xa.w},
+                         wb[4] = {xb.x, xb.y, xb.z, xb.w};
+          for (int e = 0; e < 4; e++) {
+            const double vl = (double)__uint_as_float(wv[e] << 16), vh = (double)__uint_as_float(wv[e] & 0xffff0000u);
+            const double al = vl - (double)__uint_as_float(wa[e] << 16);
+            const double ah = vh - (double)__uint_as_float(wa[e] & 0xffff0000u);
+            const double bl = vl - (double)__uint_as_float(wb[e] << 16);
+            const double bh = vh - (double)__uint_as_float(wb[e] & 0xffff0000u);
+            sA = fma(al, al, sA);
+            sA = fma(ah, ah, sA);
+            sB = fma(bl, bl, sB);
+            sB = fma(bh, bh, sB);
+          }
+        }
+        if (nkh) {
+          sA += (double)(lam * (float)nkh[k1]);
+          sB += (double)(lam * (float)nkh[k2]);
+        }
+        if (fabs(sA - sB) > (D + 4) * 0x1p-52 * fmax(sA, sB)) {
+          label = sB < sA ? k2 : k1;
+        } else {
+          double dA, lA, dB, lB;
+          exact(k1, dA, lA);
+          exact(k2, dB, lB);
+          label = better(dB, lB, k2, dA, lA, k1) ? k2 : k1;
+        }
       }
     }
     if (label >= 0) labels[(size_t)bh * N + t0 + tid] = label;
     else unsure[atomicAdd(&n_unsure, 1)] = tid;
   }
   __syncthreads();
-  // exact re-rank (binary64) of the uncertain tokens, in batches of RB tokens with two
+  // exact re-rank of the uncertain tokens, in batches of RB tokens with two
   // barriers per batch: for each token the eight lanes of a lane group share one centroid
   // row (D/8 features each, so a row is one coalesced read) and the work-group's 32 lane
   // groups take centroids k = 32j + 8 wave + group. The partial sums are combined across the
   // lane group, the groups' winners across the wave, and the four waves' winners through LDS.
-  // These sums of squared bf16 differences are exact in binary64 for inputs of moderate
-  // exponent span, so their order does not change them. With size penalties the distance is
-  // the exact pair (hi, lo) = TwoSum(s, b_k), ranked lexicographically (hi is the rounding
-  // of s + b_k, and rounding is monotone); ties go to the lowest index.
+  // The squared bf16 differences are summed as exact binary64 pairs (TwoProduct, TwoSum),
+  // so their order does not change them; a distance (with size penalties: plus b_k) is the
+  // normalised pair (hi, lo), hi the nearest binary64 of the exact value and lo the exact
+  // rest, ranked lexicographically (rounding is monotone); ties go to the lowest index.
   const int nu = n_unsure;
   constexpr int SL = D / 8;  // features per lane
   const int sub = lane & 7, grp = lane >> 3;
@@ -326,28 +357,19 @@ __global__ __launch_bounds__(256) void cl_assign_mfma(const uint16_t* __restrict
       int bk = 0x7fffffff;
       for (int kk = 0; kk < K; kk += 32) {
         const int k = kk + 8 * wave + grp;
-        double s = 0.0;
+        dpair s{0.0, 0.0};
         if (k < K) {
           double cf[SL];
           load_slice(Ch + (size_t)k * D + sub * SL, cf);
-          for (int c = 0; c < SL; c++) {
-            const double df = vf[c] - cf[c];
-            s = fma(df, df, s);
-          }
+          for (int c = 0; c < SL; c++) dp_add_sq(s, vf[c] - cf[c]);
         }
-        // butterfly over the lane group: every lane of it ends with the same sum
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
+        // butterfly over the lane group: every lane of it ends with the same exact pair
+        dp_merge(s, dp_shfl_xor(s, 1));
+        dp_merge(s, dp_shfl_xor(s, 2));
+        dp_merge(s, dp_shfl_xor(s, 4));
         if (k < K) {
-          double lo = 0.0;
-          if (nkh) {
-            const double b0 = (double)(lam * (float)nkh[k]);
-            const double hi = s + b0, bb = hi - s;
-            lo = (s - (hi - bb)) + (b0 - bb);
-            s = hi;
-          }
-          if (s < best || (s == best && lo < blo)) { best = s; blo = lo; bk = k; }
+          const dpair r = with_bias(dp_norm(s), k);
+          if (r.hi < best || (r.hi == best && r.lo < blo)) { best = r.hi; blo = r.lo; bk = k; }
         }
       }
       for (int o = 8; o < 64; o <<= 1) {
@@ -465,27 +487,21 @@ __global__ __launch_bounds__(256) void cl_scatter(const int32_t* __restrict__ la
 }
 
 // C_k = fl32(exact mean of the member rows). 128 threads: the D channels in 16-byte
-// chunks (D/8 threads per row) times 128*8/D row groups that take every G-th member;
-// exact binary64 partial sums are combined in LDS (order-independent).
+// chunks (D/8 threads per row) times 128*8/D row groups that take every G-th member; the
+// exact partial sums (binary64 pairs) are combined across the row groups of a wave with lane
+// shuffles and across the two waves in LDS (order-independent).
 template <int D>
-__global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
-                                                 const int32_t* __restrict__ cstart, const int32_t* __restrict__ csize,
-                                                 int N, int K, float* __restrict__ C) {
+__device__ __forceinline__ void member_sums(const uint16_t* __restrict__ Vh, const int32_t* __restrict__ ph, int N,
+                                            int n, dpair (*part)[D]) {
   constexpr int CH = D / 8, G = 128 / CH;
-  __shared__ double part[G][D];
-  const int k = blockIdx.x, bh = blockIdx.y;
-  const int n = csize[(size_t)bh * K + k];
-  if (n == 0) return;  // empty cluster keeps its centroid
-  const int s0 = cstart[(size_t)bh * K + k];
-  const uint16_t* Vh = V + (size_t)bh * N * D;
-  const int32_t* ph = perm + (size_t)bh * N + s0;
   const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  dpair acc[8];
+  for (int e = 0; e < 8; e++) acc[e] = dpair{0.0, 0.0};
   auto add_row = [&](const uint4 raw) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
     for (int e = 0; e < 4; e++) {
-      acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-      acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
+      dp_add(acc[2 * e], (double)__uint_as_float(w[e] << 16));
+      dp_add(acc[2 * e + 1], (double)__uint_as_float(w[e] & 0xffff0000u));
     }
   };
   auto load_row = [&](int i) {
@@ -494,20 +510,35 @@ __global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V,
     return *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
   };
   // four member rows in flight per row group (the index and row loads of one member are
-  // dependent; members are independent); the binary64 sums are exact, so the order in
-  // which members are added does not change the result
+  // dependent; members are independent); the sums are exact, so the order in which members
+  // are added does not change the result
   int i = g;
   for (; i + 3 * G < n; i += 4 * G) {
     const uint4 r0 = load_row(i), r1 = load_row(i + G), r2 = load_row(i + 2 * G), r3 = load_row(i + 3 * G);
     add_row(r0); add_row(r1); add_row(r2); add_row(r3);
   }
   for (; i < n; i += G) add_row(load_row(i));
-  for (int e = 0; e < 8; e++) part[g][8 * chunk + e] = acc[e];
+  for (int e = 0; e < 8; e++) {
+    for (int o = CH; o < 64; o <<= 1) dp_merge(acc[e], dp_shfl_xor(acc[e], o));
+    if ((threadIdx.x & 63) < CH) part[threadIdx.x >> 6][8 * chunk + e] = acc[e];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128, 7) void cl_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 const int32_t* __restrict__ cstart, const int32_t* __restrict__ csize,
+                                                 int N, int K, float* __restrict__ C) {
+  __shared__ dpair part[2][D];
+  const int k = blockIdx.x, bh = blockIdx.y;
+  const int n = csize[(size_t)bh * K + k];
+  if (n == 0) return;  // empty cluster keeps its centroid
+  const int s0 = cstart[(size_t)bh * K + k];
+  member_sums<D>(V + (size_t)bh * N * D, perm + (size_t)bh * N + s0, N, n, part);
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += 128) {
-    double s = 0.0;
-    for (int q = 0; q < G; q++) s += part[q][c];
-    C[((size_t)bh * K + k) * D + c] = div_to_f32(s, (double)n);
+    dpair s = part[0][c];
+    dp_merge(s, part[1][c]);
+    C[((size_t)bh * K + k) * D + c] = dp_div_to_f32(s, (double)n);
   }
 }
 
@@ -518,17 +549,15 @@ __global__ __launch_bounds__(128) void cl_update(const uint16_t* __restrict__ V,
 // sums are binary64 roundings (relative error ~1e-13 over a head).
 // Cross-step incremental update (the paper page's weakness list: centroids updated
 // incrementally across denoising steps). Cluster k keeps a decayed member mass M_k; with A =
-// decay * M_k (binary64, exact) and S_k the exact member sum (binary64 partial sums, exact for
-// values of moderate exponent span, combined in LDS), C_k = nearest binary32 of
+// decay * M_k (binary64, exact) and S_k = fl64(exact member sum), C_k = nearest binary32 of
 // (A * C_k + S_k) / (A + n_k) with the product, the sum and the denominator rounded in
 // binary64 op by op, and M_k = fl32(A + n_k). An empty cluster keeps C_k, M_k = fl32(A).
 template <int D>
-__global__ __launch_bounds__(128) void cl_update_inc(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+__global__ __launch_bounds__(128, 6) void cl_update_inc(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ cstart,
                                                      const int32_t* __restrict__ csize, int N, int K, float decay,
                                                      float* __restrict__ C, float* __restrict__ M) {
-  constexpr int CH = D / 8, G = 128 / CH;
-  __shared__ double part[G][D];
+  __shared__ dpair part[2][D];
   const int k = blockIdx.x, bh = blockIdx.y;
   const size_t ck = (size_t)bh * K + k;
   const int n = csize[ck];
@@ -537,36 +566,13 @@ __global__ __launch_bounds__(128) void cl_update_inc(const uint16_t* __restrict_
     if (threadIdx.x == 0) M[ck] = (float)A;
     return;
   }
-  const int s0 = cstart[ck];
-  const uint16_t* Vh = V + (size_t)bh * N * D;
-  const int32_t* ph = perm + (size_t)bh * N + s0;
-  const int chunk = threadIdx.x % CH, g = threadIdx.x / CH;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto add_row = [&](const uint4 raw) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    for (int e = 0; e < 4; e++) {
-      acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-      acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xffff0000u);
-    }
-  };
-  auto load_row = [&](int i) {
-    int row = ph[i];
-    row = ((unsigned)row < (unsigned)N) ? row : 0;
-    return *reinterpret_cast<const uint4*>(Vh + (size_t)row * D + 8 * chunk);
-  };
-  int i = g;
-  for (; i + 3 * G < n; i += 4 * G) {
-    const uint4 r0 = load_row(i), r1 = load_row(i + G), r2 = load_row(i + 2 * G), r3 = load_row(i + 3 * G);
-    add_row(r0); add_row(r1); add_row(r2); add_row(r3);
-  }
-  for (; i < n; i += G) add_row(load_row(i));
-  for (int e = 0; e < 8; e++) part[g][8 * chunk + e] = acc[e];
+  member_sums<D>(V + (size_t)bh * N * D, perm + (size_t)bh * N + cstart[ck], N, n, part);
   __syncthreads();  // every thread has read M[ck] before thread 0 writes it below
   const double den = A + (double)n;
   for (int c = threadIdx.x; c < D; c += 128) {
-    double s = 0.0;
-    for (int q = 0; q < G; q++) s += part[q][c];
-    const double num = A * (double)C[ck * D + c] + s;
+    dpair s = part[0][c];
+    dp_merge(s, part[1][c]);
+    const double num = A * (double)C[ck * D + c] + dp_norm(s).hi;
     C[ck * D + c] = div_to_f32(num, den);
   }
   if (threadIdx.x == 0) M[ck] = (float)den;
@@ -710,8 +716,8 @@ extern "C" int vc_launch_cluster_inc(const void* Vv, int B, int H, int N, int d,
 extern "C" int vc_max_clusters(void) { return kMaxClusters; }
 
 // ---------------------------------------------------------------------------
-// Exponent range of a tensor per (b,h), the quantity the exactness conditions of the binary64
-// sums and distances are stated in: over the nonzero finite elements, the largest exponent
+// Exponent range of a tensor per (b,h), the quantity the exactness conditions of the exact
+// (binary64-pair) sums and distances are stated in: over the nonzero finite elements, the largest exponent
 // e = floor(log2|x|) and the smallest exponent of a lowest set significand bit (every element
 // is an integer multiple of 2^that). kind 0: bf16 bit patterns; 1: binary32; 2: binary32 taken
 // as the bf16 value it rounds to (nearest even), as the assignment reads centroids.

@@ -19,9 +19,11 @@
 // factor 1/d is folded exactly into sQ').
 // Tiles stay in registers (no LDS staging): every load is a 16-byte vector of one token
 // row (rows of V' and K' gathered through pi) and per-channel reductions use lane
-// shuffles plus a small LDS step. Exact sums use binary64, which is exact for these
-// 128-term (or N-term) sums of bfloat16 values whenever their exponent span is moderate.
-#include "vc_device.h"
+// shuffles plus a small LDS step. The 128-term and N-term sums of bfloat16 values are
+// carried as binary64 pairs (hi + lo, error-free additions), exact for wide exponent spans.
+#include "vc_exact.h"
+
+static_assert(vc::kBlock == 128, "block means are scaled by 2^-7");
 
 namespace vc {
 
@@ -141,8 +143,8 @@ __device__ __forceinline__ void fwht_tile(float (&x)[Lay<D>::RPT][8]) {
 
 // reductions over the threads that share a chunk (lane bits >= log2(CH), then waves)
 template <int D>
-__device__ __forceinline__ double chunk_sum_wave(double v) {
-  for (int o = Lay<D>::CH; o < 64; o <<= 1) v += __shfl_xor(v, o);
+__device__ __forceinline__ dpair chunk_sum_wave(dpair v) {
+  for (int o = Lay<D>::CH; o < 64; o <<= 1) dp_merge(v, dp_shfl_xor(v, o));
   return v;
 }
 template <int D>
@@ -179,21 +181,24 @@ __device__ __forceinline__ float quant_rows(float (&x)[Lay<D>::RPT][8], uint8_t*
   return s;
 }
 
-// per-channel exact column sums of the tile (binary64; every partial sum of these bf16
-// values is exact for moderate exponent spans, so the summation order is immaterial);
-// result for channel c in colsum[c] (LDS), valid after the call
+// per-channel exact column sums of the tile as binary64 pairs (exact, so the summation
+// order is immaterial); result for channel c in colsum[c] (LDS), valid after the call
 template <int D>
-__device__ __forceinline__ void column_sums(const float (&x)[Lay<D>::RPT][8], double* part, double* colsum) {
+__device__ __forceinline__ void column_sums(const float (&x)[Lay<D>::RPT][8], dpair* part, dpair* colsum) {
   constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
   const int chunk = threadIdx.x % CH, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int e = 0; e < 8; e++) {
-    double acc = 0.0;
-    for (int i = 0; i < RPT; i++) acc += (double)x[i][e];
+    dpair acc{0.0, 0.0};
+    for (int i = 0; i < RPT; i++) dp_add(acc, (double)x[i][e]);
     acc = chunk_sum_wave<D>(acc);
     if (lane < CH) part[w * D + 8 * chunk + e] = acc;
   }
   __syncthreads();
-  if (threadIdx.x < D) colsum[threadIdx.x] = (part[threadIdx.x] + part[D + threadIdx.x]) + (part[2 * D + threadIdx.x] + part[3 * D + threadIdx.x]);
+  if (threadIdx.x < D) {
+    dpair a = part[threadIdx.x];
+    for (int q = 1; q < 4; q++) dp_merge(a, part[q * D + threadIdx.x]);
+    colsum[threadIdx.x] = a;
+  }
   __syncthreads();
 }
 
@@ -205,12 +210,12 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
                                                          const float* __restrict__ rc, const float* __restrict__ rs,
                                                          int N, uint32_t flags, float cL,
                                                          uint8_t* __restrict__ Qq, float* __restrict__ sQ,
-                                                         uint16_t* __restrict__ mu, double* __restrict__ ksum,
+                                                         uint16_t* __restrict__ mu, dpair* __restrict__ ksum,
                                                          float* __restrict__ vamax) {
   constexpr int CH = Lay<D>::CH, RPT = Lay<D>::RPT;
   __shared__ float red[4];
-  __shared__ double part[4 * D];
-  __shared__ double colsum[D];
+  __shared__ dpair part[4 * D];
+  __shared__ dpair colsum[D];
   __shared__ float pmax[4 * D];
   const int nb = N / kBlock;
   const int j = blockIdx.x, bh = blockIdx.y;
@@ -243,8 +248,8 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
   float m[8];
   if (flags & 2u) {
     column_sums<D>(x, part, colsum);
-    for (int e = 0; e < 8; e++) m[e] = bf16_to_f32(f64_to_bf16(colsum[8 * chunk + e] * (1.0 / kBlock)));
-    if (threadIdx.x < D) mu[((size_t)bh * nb + j) * D + threadIdx.x] = f64_to_bf16(colsum[threadIdx.x] * (1.0 / kBlock));
+    for (int e = 0; e < 8; e++) m[e] = bf16_to_f32(dp_to_bf16_scaled(colsum[8 * chunk + e], -7));  // / kBlock
+    if (threadIdx.x < D) mu[((size_t)bh * nb + j) * D + threadIdx.x] = dp_to_bf16_scaled(colsum[threadIdx.x], -7);
   } else {
     for (int e = 0; e < 8; e++) m[e] = 0.0f;
     if (mu != nullptr && threadIdx.x < D) mu[((size_t)bh * nb + j) * D + threadIdx.x] = 0;
@@ -266,37 +271,38 @@ __global__ __launch_bounds__(kQThreads) void quant_stats(const uint16_t* __restr
 // t / 16 takes every 16th block (two chains); the exact sums make the order immaterial.
 constexpr int kRedCh = 16;
 template <int D>
-__global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags, const double* __restrict__ ksum,
+__global__ __launch_bounds__(kQThreads) void quant_reduce(int N, uint32_t flags, const dpair* __restrict__ ksum,
                                                           const float* __restrict__ vamax, float* __restrict__ kbar,
                                                           float* __restrict__ sV, float* __restrict__ vinv) {
   constexpr int G = kQThreads / kRedCh;
-  __shared__ double ps[kQThreads];
+  __shared__ dpair ps[kQThreads];
   __shared__ float pm[kQThreads];
   const int nb = N / kBlock;
   const int bh = blockIdx.x, c = blockIdx.y * kRedCh + threadIdx.x % kRedCh, g = threadIdx.x / kRedCh;
-  double t0 = 0.0, t1 = 0.0;
+  dpair t0{0.0, 0.0}, t1{0.0, 0.0};
   float a0 = 0.0f, a1 = 0.0f;
   int jb = g;
   for (; jb + G < nb; jb += 2 * G) {  // two independent chains per thread
     if (flags & 1u) {
-      t0 += ksum[((size_t)bh * nb + jb) * D + c];
-      t1 += ksum[((size_t)bh * nb + jb + G) * D + c];
+      dp_merge(t0, ksum[((size_t)bh * nb + jb) * D + c]);
+      dp_merge(t1, ksum[((size_t)bh * nb + jb + G) * D + c]);
     }
     a0 = fmaxf(a0, vamax[((size_t)bh * nb + jb) * D + c]);
     a1 = fmaxf(a1, vamax[((size_t)bh * nb + jb + G) * D + c]);
   }
   if (jb < nb) {
-    if (flags & 1u) t0 += ksum[((size_t)bh * nb + jb) * D + c];
+    if (flags & 1u) dp_merge(t0, ksum[((size_t)bh * nb + jb) * D + c]);
     a0 = fmaxf(a0, vamax[((size_t)bh * nb + jb) * D + c]);
   }
-  ps[threadIdx.x] = t0 + t1;
+  dp_merge(t0, t1);
+  ps[threadIdx.x] = t0;
   pm[threadIdx.x] = fmaxf(a0, a1);
   __syncthreads();
   if (g == 0) {
-    double t = 0.0;
+    dpair t{0.0, 0.0};
     float a = 0.0f;
-    for (int k = 0; k < G; k++) { t += ps[k * kRedCh + threadIdx.x]; a = fmaxf(a, pm[k * kRedCh + threadIdx.x]); }
-    kbar[(size_t)bh * D + c] = (flags & 1u) ? div_to_f32(t, (double)N) : 0.0f;
+    for (int k = 0; k < G; k++) { dp_merge(t, ps[k * kRedCh + threadIdx.x]); a = fmaxf(a, pm[k * kRedCh + threadIdx.x]); }
+    kbar[(size_t)bh * D + c] = (flags & 1u) ? dp_div_to_f32(t, (double)N) : 0.0f;
     float s, inv;
     if (flags & kFlagMxfp4) { s = 1.0f; inv = 0.0f; }  // the group scales carry the range
     else if (a > 0.0f) { s = a / 448.0f; inv = 448.0f / a; } else { s = 1.0f; inv = 0.0f; }
@@ -444,7 +450,7 @@ struct QArgs {
   uint16_t* mu;
   float* mu_scaled;
   uint16_t* mu_pack;
-  double* ksum;
+  dpair* ksum;
   float *vamax, *kbar, *vinv;
 };
 
@@ -466,9 +472,10 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
                                   float* sQ, uint8_t* Kq, float* sK, uint8_t* Vq, float* sV, void* mu, float* mu_scaled,
                                   void* mu_pack, void* ws, hipStream_t st) {
   const int nb = N / kBlock, BH = B * H;
-  // workspace: ksum double [BH,nb,d] | vamax float [BH,nb,d] | kbar float [BH,d] | vinv float [BH,d] | mu (if caller's NULL)
+  // workspace: ksum binary64 pairs [BH,nb,d] | vamax float [BH,nb,d] | kbar float [BH,d] | vinv float [BH,d] |
+  // mu (if caller's NULL)
   char* w = (char*)ws;
-  double* ksum = (double*)w; w += sizeof(double) * (size_t)BH * nb * d;
+  dpair* ksum = (dpair*)w; w += sizeof(dpair) * (size_t)BH * nb * d;
   float* vamax = (float*)w; w += sizeof(float) * (size_t)BH * nb * d;
   float* kbar = (float*)w; w += sizeof(float) * (size_t)BH * d;
   float* vinv = (float*)w; w += sizeof(float) * (size_t)BH * d;
@@ -507,6 +514,6 @@ extern "C" int vc_launch_quantize(const void* Q, const void* K, const void* V, c
 
 extern "C" size_t vc_quantize_ws_bytes(int B, int H, int N, int d) {
   size_t BH = (size_t)B * H, nb = (size_t)N / kBlock;
-  return sizeof(double) * BH * nb * d + sizeof(float) * BH * nb * d + 2 * sizeof(float) * BH * d +
+  return sizeof(dpair) * BH * nb * d + sizeof(float) * BH * nb * d + 2 * sizeof(float) * BH * d +
          sizeof(uint16_t) * BH * nb * d + 256;
 }

@@ -67,35 +67,35 @@ enum {
 const char* vc_status_string(vc_status s);
 
 /* ------------------------------------------------------------------------
- * Exactness of the binary64 arithmetic. The k-means re-rank and pair decision, the
- * centroid, block-mean and key-mean sums are binary64 sums of bf16 values; the readings
- * they implement (exact argmin, exact means rounded once) hold whenever those sums are
- * exact. In terms of vc_exponent_span below -- E(X) the largest exponent and q(X) the
- * lowest significand bit over the nonzero elements of a (b,h), s(X) = E(X) - q(X) --
- * sufficient conditions per (b,h) are:
- *   - sums of n elements of X are exact when s(X) <= 52 - ceil(log2 n) (every partial
- *     sum is a multiple of 2^q(X) below n 2^(E(X)+1) <= 2^(q(X)+53)). vc_quantize: the
- *     key mean needs s(K) <= 52 - ceil(log2 N) (of the rotated keys when RoPE tables are
- *     given), the block means s(V) <= 45. vc_cluster, vc_cluster_balanced,
- *     vc_cluster_incremental: the member sums need s(V) <= 52 - ceil(log2 N) (35 at
- *     N = 70 400).
- *   - the exact squared distances sum_c (v_c - c_c)^2 (d terms) of the k-means ranking
- *     are exact when the span of V together with the bf16-rounded centroids the
- *     assignment reads (vc_exponent_span kind 2) is at most (49 - ceil(log2 d)) / 2,
- *     i.e. 21 for d = 64 and 128 (each difference is a multiple of 2^q below 2^(E+2));
- *     and the binary32 error bound that proves most labels without them assumes every
- *     nonzero |v| and |c| in [2^-56, 2^56) (no overflow or underflow in the products and
- *     norms): E <= 55 and q >= -56. With iters > 1 the centroids an assignment reads are
- *     the previous update's; run one iteration per call to check each.
- * Outside these conditions the kernels still terminate and the binary64 values are
- * within n 2^-53 (relative to the sum of magnitudes) of the exact ones: a label can then
- * differ from the exact argmin only where the two best exact squared distances of a
- * token differ by less than about 2^-45 of their size, and a mean only where its exact
- * value lies that close to a rounding boundary. Real-valued data usually exceeds these
- * sufficient conditions (a few elements near zero widen the span) while such near ties
- * stay rare: two Wan-shaped test heads have V spans of 35 and 36 and K spans of 29 and
- * 30, and every Wan head matches the oracle bit for bit. The oracle is exact for every
- * finite input.
+ * Exactness of the sums. The k-means re-rank and pair decision, the centroid, block-mean
+ * and key-mean sums are sums of bf16 values (and of squared differences of bf16 values)
+ * carried as binary64 pairs hi + lo: every term enters hi through an error-free addition
+ * (TwoSum; squares through the FMA-based TwoProduct) and the rounding error goes to lo.
+ * The readings they implement (exact argmin, exact means rounded once) hold whenever lo's
+ * own additions are exact. In terms of vc_exponent_span below -- E(X) the largest exponent
+ * and q(X) the lowest significand bit over the nonzero elements of a (b,h), s(X) = E(X) -
+ * q(X) -- sufficient conditions per (b,h) are:
+ *   - sums of n elements of X are exact when s(X) <= 103 - 2 ceil(log2 n) (every error
+ *     sent to lo is a multiple of 2^q(X) of at most 2^-53 of a partial sum below
+ *     n 2^(E(X)+1), and there are at most 2n of them). vc_quantize: the key mean needs
+ *     s(K) <= 103 - 2 ceil(log2 N) (69 at N = 70 400; of the rotated keys when RoPE tables
+ *     are given), the block means s(V) <= 89. vc_cluster, vc_cluster_balanced,
+ *     vc_cluster_incremental: the member sums need s(V) <= 103 - 2 ceil(log2 N).
+ *   - the squared distances sum_c (v_c - c_c)^2 (d <= 128 terms) of the k-means ranking
+ *     are exact when the span of V together with the bf16-rounded centroids the assignment
+ *     reads (vc_exponent_span kind 2) is at most 42; with size penalties, each nonzero
+ *     b_k = fl32(lambda n_k) must also lie in [2^(2q+23), 2^(2E+12)] (q, E of that union).
+ *     The binary32 error bound that proves most labels without them assumes every nonzero
+ *     |v| and |c| in [2^-56, 2^56) (no overflow or underflow in the products and norms):
+ *     E <= 55 and q >= -56. With iters > 1 the centroids an assignment reads are the
+ *     previous update's; run one iteration per call to check each.
+ * Outside these conditions the kernels still terminate and each pair is within about
+ * n^2 2^-104 (relative to the sum of the terms' magnitudes) of the exact value: a label can
+ * then differ from the exact argmin only where the two best exact squared distances differ
+ * by less than about 2^-88 of their size, and a mean only where its exact value lies that
+ * close to a rounding boundary. Measured on two Wan-shaped test heads: V spans 35 and 36,
+ * K spans 29 and 30, V with its bf16 centroids 35 and 36 -- inside every condition. The
+ * oracle is exact for every finite input.
  * ------------------------------------------------------------------------ */
 
 /* ------------------------------------------------------------------------
@@ -140,9 +140,9 @@ int vc_abi_version(void);
  *
  * Scores: the assignment kernel ranks clusters from bf16 matrix-core dot products
  * (exact products; accumulation error measured far inside the binary32 bound the
- * test uses), keeps a rigorous per-distance error bound, and re-ranks in binary64
- * every token whose best candidate is not separated from the rest by the bounds, so
- * labels equal the exact argmin whenever the binary64 squared distances are exact (the
+ * test uses), keeps a rigorous per-distance error bound, and re-ranks every token whose
+ * best candidate is not separated from the rest by the bounds on squared distances summed
+ * as binary64 pairs, so labels equal the exact argmin whenever those pairs are exact (the
  * "Exactness" conditions above; vc_exponent_span checks them).
  * ------------------------------------------------------------------------ */
 size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K);
@@ -171,8 +171,8 @@ vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters
  *   (VC_E_ALIAS) and must be 16-byte aligned (VC_E_UNSUPPORTED)
  *
  * Exactness as for vc_cluster: the certainty bound also covers the rounding of the
- * penalised norms, and re-ranked distances are compared as the exact pair
- * TwoSum(binary64 squared distance, b_k).
+ * penalised norms, and re-ranked distances are compared as the exact pair of (squared
+ * distance + b_k), normalised.
  * ------------------------------------------------------------------------ */
 vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
                               float lambda, int32_t* counts, float* centroids, int32_t* labels, int32_t* perm,
@@ -186,7 +186,8 @@ vc_status vc_cluster_balanced(const void* V, int B, int H, int N, int d, int K, 
  * Every cluster carries a decayed member mass M_k beside its centroid. With the members
  * n_k of cluster k under the labels (re-assigned first when `assign` != 0: nearest
  * bf16(C_k), as vc_cluster assigns; else the given labels, read-only, a label outside
- * [0,K) read as 0), S_k their exact value sum, and A = decay * M_k (binary64):
+ * [0,K) read as 0), S_k the binary64 rounding of their exact value sum, and A = decay *
+ * M_k (binary64):
  *   C_k = nearest binary32 of (A * C_k + S_k) / (A + n_k), the product, the sum and the
  *         denominator rounded in binary64 one operation at a time;
  *   M_k = fl32(A + n_k); an empty cluster keeps C_k and gets M_k = fl32(A).
@@ -280,7 +281,7 @@ vc_status vc_quantize(const void* Q, const void* K, const void* V, const int32_t
  *
  *   a shape whose vc_quantize_workspace_bytes exceeds VC_QUANTIZE_NOALLOC_SCRATCH_BYTES is
  *   rejected with VC_E_WORKSPACE before anything is launched (B*H*(N/128)*d up to about
- *   4.79 M elements, e.g. B=1, H=40, N=70,400, d=128 fits);
+ *   3.05 M elements, 22 bytes each; B=1, H=40, N=70,400, d=128 needs 59.1 MiB and fits);
  *   every call on one device shares that device's array, which keeps the last call's
  *   contents (nothing in it needs clearing: each call writes all it reads): calls that
  *   overlap in time on one device, on any streams, race and must be serialised by the

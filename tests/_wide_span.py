@@ -1,0 +1,187 @@
+"""Constructed inputs whose exact sums need more than binary64's 53 significant bits, with
+the exact expected results from rational arithmetic (fractions.Fraction):
+
+* columns whose exact mean lies a hair (far below binary64 resolution) above or below a
+  binary32 or bfloat16 rounding tie, so that the correctly rounded mean depends on bits a
+  binary64 running sum drops;
+* columns whose exact sum lies a hair beside a binary64 tie that sits on a binary32 tie
+  after the division (the incremental centroid update rounds the sum to binary64 first);
+* tokens whose nearest centroids differ in squared distance only below binary64
+  resolution.
+
+Every value is an exact bfloat16 value. The columns contain many exactly cancelling pairs of
+widely different magnitudes, so a binary64 running sum rounds in many places. Nothing here
+implements the method: the expected values are plain rational arithmetic.
+"""
+from fractions import Fraction as Fr
+
+import numpy as np
+
+import synth
+
+
+def _round_even(x: Fr, p: int) -> Fr:
+    """x rounded to p significant bits, ties to even (normal range)."""
+    if x == 0:
+        return Fr(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fr(2) ** e > a:
+        e -= 1
+    while Fr(2) ** (e + 1) <= a:
+        e += 1
+    g = Fr(2) ** (e - p + 1)
+    q = a / g
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fr(1, 2) or (r == Fr(1, 2) and n % 2 == 1):
+        n += 1
+    return (1 if x > 0 else -1) * n * g
+
+
+def f32_of(x: Fr) -> np.float32:
+    return np.float32(float(_round_even(x, 24)))
+
+
+def bf16_of(x: Fr) -> int:
+    return int(synth.bf16_bits(np.array([float(_round_even(x, 8))], np.float32))[0])
+
+
+def _bf16_value(rng, lo_exp: int, hi_exp: int) -> float:
+    """a random bfloat16 value with 8 significant bits, magnitude in [2^lo_exp, 2^(hi_exp+1))"""
+    e = int(rng.integers(lo_exp, hi_exp + 1))
+    return float(int(rng.integers(128, 256)) * 2.0 ** (e - 7))
+
+
+def _split_bf16(m: int, shift: int) -> list:
+    """m * 2^shift (m < 2^24) as a sum of at most three bfloat16 values (8-bit chunks)."""
+    out = []
+    for k in (16, 8, 0):
+        c = (m >> k) & 0xFF
+        if c:
+            out.append(float(c * 2.0 ** (shift + k)))
+    return out
+
+
+def _fill_column(rng, n: int, pieces: list, pair_exp: tuple, n_twos: int) -> np.ndarray:
+    """n values: n_twos entries 2.0, the given pieces, cancelling pairs +x/-x in the other
+    rows (random magnitudes), zeros where a row is left over; rows shuffled."""
+    col = np.zeros(n, np.float64)
+    rows = rng.permutation(n)
+    col[rows[:n_twos]] = 2.0
+    k = n_twos
+    for p in pieces:
+        col[rows[k]] = p
+        k += 1
+    while k + 1 < n:
+        x = _bf16_value(rng, *pair_exp) * (1 if rng.random() < 0.5 else -1)
+        col[rows[k]], col[rows[k + 1]] = x, -x
+        k += 2
+    return col
+
+
+def mean_columns(rng, n: int, ncols: int, target: str, small: bool = False):
+    """Columns of n values (n a power of two >= 128) whose exact mean is T + s 2^-g with T a
+    rounding tie of the target format ("f32": binary32, "bf16": bfloat16) just above 1, s =
+    +-1 and g well below binary64 resolution. Returns (X [n, ncols] float64 of bf16 values,
+    exact means as Fractions, correctly rounded means: float32 or bf16 bit patterns).
+    small=True keeps every value below 2 in magnitude (pieces below 0.25, pairs below 0.5)."""
+    p = n.bit_length() - 1
+    assert n == 1 << p and n >= 128
+    X = np.zeros((n, ncols), np.float64)
+    exact, rounded = [], []
+    for c in range(ncols):
+        s = 1 if rng.random() < 0.5 else -1
+        if target == "f32":
+            odd = 2 * int(rng.integers(0, 1 << (11 if small else 15))) + 1
+            tie = 1 + Fr(odd, 1 << 24)
+            g = int(rng.integers(56, 70))
+            pieces = _split_bf16(odd, p - 24)
+        else:
+            odd = 2 * int(rng.integers(0, 64)) + 1
+            tie = 1 + Fr(odd, 1 << 8)
+            g = int(rng.integers(55, 68))
+            pieces = _split_bf16(odd, p - 8)
+        pieces.append(float(s * 2.0 ** (p - g)))
+        pair_exp = (-30, -2) if small else (-30, 6)
+        X[:, c] = _fill_column(rng, n, pieces, pair_exp, n // 2)
+        m = tie + s * Fr(1, 1 << g)
+        assert sum(Fr(float(v)) for v in X[:, c]) == n * m
+        exact.append(m)
+        rounded.append(f32_of(m) if target == "f32" else bf16_of(m))
+    return X, exact, rounded
+
+
+def f64_tie_columns(rng, n: int, ncols: int):
+    """Columns of n values whose exact sum is X + h + s t: X = n T with T a binary32 tie, h
+    half a binary64 unit of X and t far smaller, so fl64(exact sum) is X + 2h for s = +1 and X
+    for s = -1, and fl32(fl64(sum) / n) is T's upper neighbour for s = +1 and T's even
+    neighbour for s = -1. Returns (X [n, ncols] float64 of bf16 values, expected binary32
+    results of fl32(fl64(S) / n))."""
+    p = n.bit_length() - 1
+    assert n == 1 << p and n >= 128
+    out = np.zeros((n, ncols), np.float64)
+    exp = []
+    for c in range(ncols):
+        s = 1 if rng.random() < 0.5 else -1
+        odd = 2 * int(rng.integers(0, 1 << 15)) + 1
+        T = 1 + Fr(odd, 1 << 24)
+        h = Fr(2) ** (p - 53)
+        t = Fr(2) ** (p - 53 - int(rng.integers(10, 25)))
+        pieces = _split_bf16(odd, p - 24) + [float(h), float(s * t)]
+        out[:, c] = _fill_column(rng, n, pieces, (-30, 6), n // 2)
+        S = n * T + h + s * t
+        assert sum(Fr(float(v)) for v in out[:, c]) == S
+        S64 = _round_even(S, 53)
+        exp.append(f32_of(S64 / n))
+    return out, exp
+
+
+def running_sum(col: np.ndarray) -> float:
+    """binary64 running sum in row order (what a plain accumulator computes)."""
+    s = 0.0
+    for v in col:
+        s += float(v)
+    return s
+
+
+def near_tie_tokens(rng, N: int, d: int, ntriples: int):
+    """Tokens and centroids whose squared distances tie in every bit binary64 keeps.
+
+    Centroid triple j (indices 3j, 3j+1, 3j+2) shares a base vector b_j (bf16 values of
+    magnitude about 1 on the base channels) and adds L = 2^10 on a "far" channel; the token
+    near triple j is b_j plus tiny values (2^-20 or 2^-19) on a few "tiny" channels where the
+    centroids hold 0 or a tiny offset. Every distance from such a token to its triple is L^2
+    plus a sum of squares of order 2^-40: equal after binary64 rounding, different exactly.
+    Triples alternate between a three-way near tie (all three within 2^-36) and a two-way one
+    (the third centroid 64 further away). Returns (V bf16 bits [N, d], C0 float32
+    [3 ntriples, d], which triple each token is near)."""
+    far = [0, 1, 2]
+    tiny = list(range(3, 11))
+    base = list(range(11, d))
+    L = 2.0 ** 10
+    C = np.zeros((3 * ntriples, d), np.float64)
+    bvec = np.zeros((ntriples, d), np.float64)
+    for j in range(ntriples):
+        bvec[j, base] = [_bf16_value(rng, -1, 0) * (1 if rng.random() < 0.5 else -1) for _ in base]
+        for m in range(3):
+            C[3 * j + m] = bvec[j]
+        C[3 * j + 0, far[0]] = L
+        C[3 * j + 1, far[0]] = -L
+        C[3 * j + 2, far[1]] = L
+        # tiny offsets on a few tiny channels: each centroid its own pattern
+        for m in range(3):
+            for ch in rng.choice(tiny, 3, replace=False):
+                C[3 * j + m, ch] = float(rng.choice([2.0 ** -21, -(2.0 ** -21), 2.0 ** -20]))
+        if j % 2 == 1:
+            C[3 * j + 2, far[2]] = 8.0  # the third one clearly further: a two-way near tie
+    near = rng.integers(0, ntriples, N)
+    V = bvec[near].copy()
+    for t in range(N):
+        for ch in rng.choice(tiny, 4, replace=False):
+            V[t, ch] = float(rng.choice([2.0 ** -20, -(2.0 ** -20), 2.0 ** -19]))
+    return synth.bf16_bits(V.astype(np.float32)), C.astype(np.float32), near
+
+
+def exact_sqdist(v: np.ndarray, c: np.ndarray) -> Fr:
+    return sum((Fr(float(a)) - Fr(float(b))) ** 2 for a, b in zip(v, c))

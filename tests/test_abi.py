@@ -221,7 +221,7 @@ def test_quantize_noalloc_rejects_bad_arguments(L):
     assert call(Q=None) == 1
     assert call(N=200) == 2
     assert call(flags=64) == 3
-    # beyond the 64 MiB scratch: B*H*(N/128)*d = 40 * 1024 * 128 elements need 70 MiB
+    # beyond the 64 MiB scratch: B*H*(N/128)*d = 40 * 1024 * 128 elements need 110 MiB
     assert call(B=1, H=40, N=131072) == 4
     assert call(Qq=ctypes.c_void_p((1 << 20) + 4)) == 5
     assert call(Qq=FAKE) == 7

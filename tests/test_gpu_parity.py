@@ -740,8 +740,9 @@ def test_exponent_span_matches_reference():
 
 
 def test_exponent_span_of_the_video_workload_heads():
-    """The checker on Wan-shaped heads (V, keys, and the bf16 centroids after k-means), printed
-    against the exactness conditions of include/vc.h; the values must equal the reference."""
+    """The checker on Wan-shaped heads (V, keys, and the bf16 centroids after k-means): the
+    values must equal the reference, and these heads lie inside the exactness conditions of
+    include/vc.h (sums of N terms: span <= 103 - 2 ceil(log2 N); distances: span <= 42)."""
     N, d, K = 70400, 128, 550
     hs = [synth.gen_head("wan", 2, 0, h, N, d) for h in (0, 23)]
     V = np.stack([w["V"] for w in hs])[None]
@@ -750,12 +751,13 @@ def test_exponent_span_of_the_video_workload_heads():
     sv = vc.vc_exponent_span(to_dev_bf16(V)).cpu().numpy()[0]
     sk = vc.vc_exponent_span(to_dev_bf16(Kt)).cpu().numpy()[0]
     sc = vc.vc_exponent_span(to_dev(C), as_bf16=True).cpu().numpy()[0]
-    lim_sum = 52 - int(np.ceil(np.log2(N)))
+    lim_sum = 103 - 2 * int(np.ceil(np.log2(N)))
     for i in range(2):
         assert tuple(sv[i]) == _span_reference(synth.bf16_to_f32(V[0, i]).astype(np.float64))
         assert tuple(sc[i]) == _span_reference(synth.bf16_to_f32(synth.bf16_bits(C[0, i])).astype(np.float64))
         dist_span = max(sv[i][0], sc[i][0]) - min(sv[i][1], sc[i][1])
         print("[span] head %d: V (E %d, q %d, span %d), K span %d, V with bf16 centroids span %d; sums exact "
-              "below %d: V %s, K %s; distances exact below 21: %s"
+              "up to %d: V %s, K %s; distances exact up to 42: %s"
               % (i, sv[i][0], sv[i][1], sv[i][0] - sv[i][1], sk[i][0] - sk[i][1], dist_span, lim_sum,
-                 sv[i][0] - sv[i][1] <= lim_sum, sk[i][0] - sk[i][1] <= lim_sum, dist_span <= 21), flush=True)
+                 sv[i][0] - sv[i][1] <= lim_sum, sk[i][0] - sk[i][1] <= lim_sum, dist_span <= 42), flush=True)
+        assert sv[i][0] - sv[i][1] <= lim_sum and sk[i][0] - sk[i][1] <= lim_sum and dist_span <= 42
