@@ -246,7 +246,9 @@ vc_status vc_cluster_cost(const void* V, const float* centroids, const int32_t* 
  *            lanes 32..63; key blocks past N/128 are zero. May be NULL.
  * Arithmetic: block and channel scales are fl32(amax/448) with codes
  * e4m3(fl32(x * fl32(448/amax))) (round to nearest even); amax = 0 gives scale 1
- * and zero codes. kbar = fl32(exact mean), mu = bf16(exact block mean).
+ * and zero codes; a nonzero amax below 448 / FLT_MAX (about 1.3e-36) overflows 448/amax,
+ * and that block's or channel's codes are then unspecified. kbar = fl32(exact mean),
+ * mu = bf16(exact block mean), on the subnormal grids where the means are that small.
  * VC_F_MXFP4 (the 4-bit residual of the pages' workstation path, as OCP MXFP4): the
  * residual R gets E2M1 codes with one E8M0 scale per group of 32 keys of a channel, the
  * scale being the smallest 2^e with max|R| <= 6 * 2^e (no clipping; 2^0 for an all-zero

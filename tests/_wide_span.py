@@ -185,3 +185,25 @@ def near_tie_tokens(rng, N: int, d: int, ntriples: int):
 
 def exact_sqdist(v: np.ndarray, c: np.ndarray) -> Fr:
     return sum((Fr(float(a)) - Fr(float(b))) ** 2 for a, b in zip(v, c))
+
+
+def tiny_values(rng, n: int, d: int) -> np.ndarray:
+    """n x d bfloat16 values m 2^-133 (m in 1..255, random signs): bfloat16 subnormals and the
+    smallest normals, whose means round on the subnormal grids of binary32 and bfloat16."""
+    m = rng.integers(1, 256, (n, d)).astype(np.float64)
+    return m * 2.0 ** -133 * np.where(rng.random((n, d)) < 0.6, 1.0, -1.0)
+
+
+def f32_of_tiny(x: Fr) -> np.float32:
+    """binary32 nearest to x, ties to even, on the subnormal grid 2^-149 below 2^-126."""
+    if abs(x) >= Fr(2) ** -126:
+        return f32_of(x)
+    return np.float32(float(Fr(round(x * Fr(2) ** 149)) / Fr(2) ** 149))
+
+
+def bf16_of_tiny(x: Fr) -> int:
+    """bfloat16 nearest to x, ties to even, on the subnormal grid 2^-133 below 2^-126."""
+    if abs(x) >= Fr(2) ** -126:
+        return bf16_of(x)
+    v = Fr(round(x * Fr(2) ** 133)) / Fr(2) ** 133
+    return int(synth.bf16_bits(np.array([float(v)], np.float32))[0]) | (0x8000 if x < 0 and v == 0 else 0)

@@ -189,3 +189,33 @@ def test_cluster_near_ties_beyond_binary64(d, lam):
         assert np.array_equal(lg[0, h], l_or), (h, np.count_nonzero(lg[0, h] != l_or))
         assert np.array_equal(pg[0, h], p_or), h
         assert np.array_equal(Cg[0, h], c_or), h
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_means_on_subnormal_grids(d):
+    """Values m 2^-133 (bfloat16 subnormals and the smallest normals): the k-means centroid
+    (one cluster of 384 tokens) on the binary32 subnormal grid and the quantiser's block
+    means on the bfloat16 subnormal grid, against the oracle and the rational results (the
+    residual codes are outside the quantiser's range here: 448/amax overflows)."""
+    from fractions import Fraction as F
+    B, H, N = 1, 2, 384
+    rng = np.random.default_rng(110 + d)
+    X = np.stack([ws.tiny_values(rng, N, d).astype(np.float32) for _ in range(H)])[None]
+    V = synth.bf16_bits(X)
+    C0 = np.zeros((B, H, 1, d), np.float32)
+    C = to_dev(C0)
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty_like(lab)
+    vc.vc_cluster(to_dev_bf16(V), 1, 1, False, C, lab, perm)
+    Q = np.stack([synth.gen_head("wan", 111, 0, h, N, d)["Q"] for h in range(H)])[None]
+    flags = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
+    out = gpu_quantize(Q, Q, V, None, flags)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    for h in range(H):
+        exp = np.array([ws.f32_of_tiny(sum(F(float(x)) for x in X[0, h, :, c]) / N) for c in range(d)], np.float32)
+        _, _, c_or = oracle.kmeans(V[0, h], 1, 1, cold=False, C=C0[0, h])
+        assert np.array_equal(c_or[0], exp), h
+        assert np.array_equal(Cg[0, h], c_or), h
+        q = oracle.quantize(Q[0, h], Q[0, h], V[0, h], None, int(flags))
+        assert np.array_equal(bf16_bits(out["mu"])[0, h], q["mu"]), h

@@ -2,8 +2,9 @@
 on bits far below binary64 resolution, the incremental update's binary64 rounding of an exact
 sum that sits next to a binary64 tie, and nearest centroids that differ in squared distance
 only far below binary64 resolution. Expected values are rational arithmetic on constructed
-inputs (tests/_wide_span.py); each case also checks that a plain binary64 running sum gets
-a share of them wrong, so the inputs do exercise more than binary64."""
+inputs (tests/_wide_span.py); the first four cases also check that a plain binary64 running
+sum gets a share of them wrong, so the inputs do exercise more than binary64. The last one
+takes means onto the subnormal grids of binary32 and bfloat16."""
 import numpy as np
 
 import oracle
@@ -91,3 +92,22 @@ def test_nearest_centroid_beyond_binary64():
     other = np.where((np.arange(3 * T)[None] // 3) == near[:, None], np.inf, D64).min(1)
     assert np.all(other > own + 32)
     assert wrong64 >= N // 4, wrong64
+
+
+def test_means_on_subnormal_grids():
+    """Means of values m 2^-133 (bfloat16 subnormals and the smallest normals): the centroid
+    rounds to the binary32 subnormal grid 2^-149 and the block means to the bfloat16 grid
+    2^-133, nearest even."""
+    from fractions import Fraction as F
+    rng = np.random.default_rng(6)
+    n, d = 384, 32
+    X = ws.tiny_values(rng, n, d).astype(np.float32)
+    C = oracle.kmeans_update(synth.bf16_bits(X), np.zeros(n, np.int32), np.zeros((1, d), np.float32))
+    exp = np.array([ws.f32_of_tiny(sum(F(float(x)) for x in X[:, c]) / n) for c in range(d)], np.float32)
+    assert np.array_equal(C[0], exp)
+    assert np.all(np.abs(C[0]) < 2.0 ** -126)
+    Q = synth.gen_head("wan", 3, 0, 0, n, d)["Q"]
+    q = oracle.quantize(Q, Q, synth.bf16_bits(X), None, oracle.FLAG_KSMOOTH | oracle.FLAG_VSMOOTH)
+    mexp = np.array([[ws.bf16_of_tiny(sum(F(float(x)) for x in X[128 * b:128 * (b + 1), c]) / 128) for c in range(d)]
+                     for b in range(n // 128)])
+    assert np.array_equal(q["mu"].astype(np.int64), mexp)
