@@ -524,6 +524,8 @@ __device__ __forceinline__ void member_sums(const uint16_t* __restrict__ Vh, con
   }
 }
 
+// at least seven waves per SIMD (72 VGPRs): the pair sums keep more live values than the loads
+// need, and the extra waves hide the dependent index and row loads (measured against five and six)
 template <int D>
 __global__ __launch_bounds__(128, 7) void cl_update(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                  const int32_t* __restrict__ cstart, const int32_t* __restrict__ csize,
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(128, 7) void cl_update(const uint16_t* __restrict__
 // (A * C_k + S_k) / (A + n_k) with the product, the sum and the denominator rounded in
 // binary64 op by op, and M_k = fl32(A + n_k). An empty cluster keeps C_k, M_k = fl32(A).
 template <int D>
-__global__ __launch_bounds__(128, 6) void cl_update_inc(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+__global__ __launch_bounds__(128, 6) void cl_update_inc(  // six waves per SIMD: seven would spillconst uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ cstart,
                                                      const int32_t* __restrict__ csize, int N, int K, float decay,
                                                      float* __restrict__ C, float* __restrict__ M) {
