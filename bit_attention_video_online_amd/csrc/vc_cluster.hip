@@ -554,8 +554,9 @@ __global__ __launch_bounds__(128, 7) void cl_update(const uint16_t* __restrict__
 // decay * M_k (binary64, exact) and S_k = fl64(exact member sum), C_k = nearest binary32 of
 // (A * C_k + S_k) / (A + n_k) with the product, the sum and the denominator rounded in
 // binary64 op by op, and M_k = fl32(A + n_k). An empty cluster keeps C_k, M_k = fl32(A).
+// six waves per SIMD (74 VGPRs): seven would spill
 template <int D>
-__global__ __launch_bounds__(128, 6) void cl_update_inc(  // six waves per SIMD: seven would spillconst uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+__global__ __launch_bounds__(128, 6) void cl_update_inc(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                      const int32_t* __restrict__ cstart,
                                                      const int32_t* __restrict__ csize, int N, int K, float decay,
                                                      float* __restrict__ C, float* __restrict__ M) {
