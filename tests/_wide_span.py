@@ -54,22 +54,26 @@ def _bf16_value(rng, lo_exp: int, hi_exp: int) -> float:
 
 
 def _split_bf16(m: int, shift: int) -> list:
-    """m * 2^shift (m < 2^24) as a sum of at most three bfloat16 values (8-bit chunks)."""
+    """m * 2^shift (0 <= m < 2^32) as a sum of at most four bfloat16 values (8-bit chunks)."""
     out = []
-    for k in (16, 8, 0):
+    for k in (24, 16, 8, 0):
         c = (m >> k) & 0xFF
         if c:
             out.append(float(c * 2.0 ** (shift + k)))
     return out
 
 
-def _fill_column(rng, n: int, pieces: list, pair_exp: tuple, n_twos: int) -> np.ndarray:
-    """n values: n_twos entries 2.0, the given pieces, cancelling pairs +x/-x in the other
-    rows (random magnitudes), zeros where a row is left over; rows shuffled."""
+def _fill_column(rng, n: int, pieces: list, pair_exp: tuple) -> np.ndarray:
+    """n values summing to n + sum(pieces): n // 2 entries 2.0 (and one 1.0 for odd n), the
+    given pieces, cancelling pairs +x/-x in the other rows (random magnitudes), zeros where a
+    row is left over; rows shuffled."""
     col = np.zeros(n, np.float64)
     rows = rng.permutation(n)
-    col[rows[:n_twos]] = 2.0
-    k = n_twos
+    col[rows[:n // 2]] = 2.0
+    k = n // 2
+    if n % 2:
+        col[rows[k]] = 1.0
+        k += 1
     for p in pieces:
         col[rows[k]] = p
         k += 1
@@ -81,30 +85,28 @@ def _fill_column(rng, n: int, pieces: list, pair_exp: tuple, n_twos: int) -> np.
 
 
 def mean_columns(rng, n: int, ncols: int, target: str, small: bool = False):
-    """Columns of n values (n a power of two >= 128) whose exact mean is T + s 2^-g with T a
-    rounding tie of the target format ("f32": binary32, "bf16": bfloat16) just above 1, s =
-    +-1 and g well below binary64 resolution. Returns (X [n, ncols] float64 of bf16 values,
-    exact means as Fractions, correctly rounded means: float32 or bf16 bit patterns).
-    small=True keeps every value below 2 in magnitude (pieces below 0.25, pairs below 0.5)."""
-    p = n.bit_length() - 1
-    assert n == 1 << p and n >= 128
+    """Columns of n values (16 <= n < 2^16) whose exact mean is T + s 2^-g with T a rounding tie
+    of the target format ("f32": binary32, "bf16": bfloat16) just above 1, s = +-1 and g well
+    below binary64 resolution. Returns (X [n, ncols] float64 of bf16 values, exact means as
+    Fractions, correctly rounded means: float32 or bf16 bit patterns). small=True keeps every
+    value below 2 in magnitude (n >= 512: pieces below 0.25, pairs below 0.5)."""
+    assert 16 <= n < 1 << 16
     X = np.zeros((n, ncols), np.float64)
     exact, rounded = [], []
     for c in range(ncols):
         s = 1 if rng.random() < 0.5 else -1
         if target == "f32":
             odd = 2 * int(rng.integers(0, 1 << (11 if small else 15))) + 1
-            tie = 1 + Fr(odd, 1 << 24)
+            tie, fb = 1 + Fr(odd, 1 << 24), 24
             g = int(rng.integers(56, 70))
-            pieces = _split_bf16(odd, p - 24)
         else:
             odd = 2 * int(rng.integers(0, 64)) + 1
-            tie = 1 + Fr(odd, 1 << 8)
+            tie, fb = 1 + Fr(odd, 1 << 8), 8
             g = int(rng.integers(55, 68))
-            pieces = _split_bf16(odd, p - 8)
-        pieces.append(float(s * 2.0 ** (p - g)))
+        # n T = n + (n odd) 2^-fb and n s 2^-g, each split into bf16 pieces
+        pieces = _split_bf16(n * odd, -fb) + [s * v for v in _split_bf16(n, -g)]
         pair_exp = (-30, -2) if small else (-30, 6)
-        X[:, c] = _fill_column(rng, n, pieces, pair_exp, n // 2)
+        X[:, c] = _fill_column(rng, n, pieces, pair_exp)
         m = tie + s * Fr(1, 1 << g)
         assert sum(Fr(float(v)) for v in X[:, c]) == n * m
         exact.append(m)
@@ -129,7 +131,7 @@ def f64_tie_columns(rng, n: int, ncols: int):
         h = Fr(2) ** (p - 53)
         t = Fr(2) ** (p - 53 - int(rng.integers(10, 25)))
         pieces = _split_bf16(odd, p - 24) + [float(h), float(s * t)]
-        out[:, c] = _fill_column(rng, n, pieces, (-30, 6), n // 2)
+        out[:, c] = _fill_column(rng, n, pieces, (-30, 6))
         S = n * T + h + s * t
         assert sum(Fr(float(v)) for v in out[:, c]) == S
         S64 = _round_even(S, 53)

@@ -23,16 +23,17 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _clustered_head(rng, d, K, n, columns):
-    """K clusters of n tokens each: channel g holds 64 for the tokens of cluster g (identity
-    channels 0..K-1), the other channels take columns(rng, n, d - K) per cluster. Returns
-    (V float64 [K n, d], labels, per-cluster expected values of the other channels)."""
-    N = K * n
-    V = np.zeros((N, d))
-    lab = rng.permutation(np.repeat(np.arange(K), n)).astype(np.int32)
+def _clustered_head(rng, d, sizes, columns):
+    """len(sizes) clusters, cluster g of sizes[g] tokens: channel g holds 64 for the tokens of
+    cluster g (identity channels 0..K-1), the other channels take columns(rng, n, d - K) per
+    cluster. Returns (V float64 [sum(sizes), d], labels, per-cluster expected values of the
+    other channels)."""
+    K = len(sizes)
+    V = np.zeros((sum(sizes), d))
+    lab = rng.permutation(np.repeat(np.arange(K), sizes)).astype(np.int32)
     exp = []
     for g in range(K):
-        X, e = columns(rng, n, d - K)
+        X, e = columns(rng, sizes[g], d - K)
         rows = np.flatnonzero(lab == g)
         V[rows, g] = 64.0
         V[rows, K:] = X
@@ -41,18 +42,21 @@ def _clustered_head(rng, d, K, n, columns):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_cluster_means_beyond_binary64(d):
+@pytest.mark.parametrize("sizes", [(256, 256, 256, 256), (200, 312, 97, 415)])
+def test_cluster_means_beyond_binary64(d, sizes):
     """vc_cluster, one warm iteration from the identity centroids: labels, perm and centroids
-    against the oracle, centroids against the exact means rounded once."""
-    B, H, K, n = 1, 2, 4, 256
-    rng = np.random.default_rng(70 + d)
-    heads = [_clustered_head(rng, d, K, n, lambda r, m, c: ws.mean_columns(r, m, c, "f32")[::2]) for _ in range(H)]
+    against the oracle, centroids against the exact means rounded once; cluster sizes powers of
+    two (the quotient is exact before its rounding) and not (it is not)."""
+    B, H, K = 1, 2, len(sizes)
+    N = sum(sizes)
+    rng = np.random.default_rng(70 + d + sizes[1])
+    heads = [_clustered_head(rng, d, sizes, lambda r, m, c: ws.mean_columns(r, m, c, "f32")[::2]) for _ in range(H)]
     V = np.stack([synth.bf16_bits(h[0].astype(np.float32)) for h in heads])[None]
     C0 = np.zeros((B, H, K, d), np.float32)
     for g in range(K):
         C0[..., g, g] = 64.0
     C = to_dev(C0)
-    lab = torch.empty((B, H, K * n), dtype=torch.int32, device="cuda")
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
     perm = torch.empty_like(lab)
     vc.vc_cluster(to_dev_bf16(V), K, 1, False, C, lab, perm)
     torch.cuda.synchronize()
@@ -73,7 +77,7 @@ def test_cluster_incremental_beyond_binary64(d):
     where the exact sum sits next to a binary64 tie."""
     B, H, K, n = 1, 2, 4, 256
     rng = np.random.default_rng(80 + d)
-    heads = [_clustered_head(rng, d, K, n, ws.f64_tie_columns) for _ in range(H)]
+    heads = [_clustered_head(rng, d, (n,) * K, ws.f64_tie_columns) for _ in range(H)]
     V = np.stack([synth.bf16_bits(h[0].astype(np.float32)) for h in heads])[None]
     lab0 = np.stack([h[1] for h in heads])[None]
     C0 = rng.standard_normal((B, H, K, d)).astype(np.float32)
