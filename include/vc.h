@@ -131,7 +131,9 @@ int vc_abi_version(void);
  * C_k = V[floor((2k+1)N/(2K))].
  *
  *   V          bf16 [B,H,N,d]                      input
- *   K          clusters per head, 1 <= K <= N
+ *   K          clusters per head, 1 <= K <= min(N, vc_max_clusters()) (8192: the label
+ *              histogram of a token chunk lives in LDS); else VC_E_PARAM
+ *   iters      1 <= iters <= 1000, else VC_E_PARAM
  *   centroids  float [B,H,K,d]  in: warm-start state (ignored when cold_start),
  *                               out: centroids after the last update
  *   labels     int32 [B,H,N]    out: labels of the last assignment
@@ -145,6 +147,7 @@ int vc_abi_version(void);
  * as binary64 pairs, so labels equal the exact argmin whenever those pairs are exact (the
  * "Exactness" conditions above; vc_exponent_span checks them).
  * ------------------------------------------------------------------------ */
+int vc_max_clusters(void); /* 8192: the largest K vc_cluster, vc_cluster_balanced and vc_cluster_incremental accept */
 size_t vc_cluster_workspace_bytes(int B, int H, int N, int d, int K);
 vc_status vc_cluster(const void* V, int B, int H, int N, int d, int K, int iters, int cold_start,
                      float* centroids, int32_t* labels, int32_t* perm,

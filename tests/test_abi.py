@@ -137,7 +137,10 @@ def test_cluster_rejects_bad_arguments(L):
     assert call(N=100) == 2
     assert call(K=0) == 3
     assert call(K=257) == 3          # more clusters than tokens
+    assert L.vc_max_clusters() == 8192
+    assert call(N=16384, K=8193) == 3  # more clusters than the label histogram holds
     assert call(iters=0) == 3
+    assert call(iters=1001) == 3
     assert call(wsb=8) == 4
     assert call(lab=ctypes.c_void_p(3 << 20)) == 7   # labels alias perm
 
