@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -214,6 +215,24 @@ def measure_mfma_peak(grid=2048, iters=20000, reps=3):
             best = t if best is None else min(best, t)
         res[name] = round(flops / best / 1e12, 1)
     return res
+
+
+def exactness_spans(vc, torch, Kd, Vd, Cw, C1, N, d):
+    """Exponent spans (largest exponent minus lowest significand bit, per (b,h), maximum over
+    heads) of the step's inputs, against the sufficient conditions under which the k-means and
+    quantiser sums are exact: sums of N terms need span <= 103 - 2 ceil(log2 N); the squared
+    distances need the span of V together with the bf16-rounded centroids each assignment
+    reads (the warm state Cw, then C1 after the first update) <= 50 - log2 d."""
+    sv, sk = vc.vc_exponent_span(Vd), vc.vc_exponent_span(Kd)
+    sc = [vc.vc_exponent_span(c, as_bf16=True) for c in (Cw, C1)]
+    span = lambda s: int((s[..., 0] - s[..., 1]).max())
+    dist = max(int((torch.maximum(sv[..., 0], c[..., 0]) - torch.minimum(sv[..., 1], c[..., 1])).max()) for c in sc)
+    lim_sum = 103 - 2 * int(math.ceil(math.log2(N)))
+    lim_dist = 50 - int(math.log2(d))
+    out = {"V_span": span(sv), "K_span": span(sk), "V_with_centroids_span": dist, "sum_span_limit": lim_sum,
+           "distance_span_limit": lim_dist}
+    out["inside"] = out["V_span"] <= lim_sum and out["K_span"] <= lim_sum and dist <= lim_dist
+    return out
 
 
 def stage_rates(B, H, N, d, Kc, iters, avg):
@@ -662,6 +681,15 @@ def main():
     mfma = measure_mfma_peak()
     log("[bench] sustained FP8 matrix-core rate (TFLOP/s): %s" % mfma)
 
+    exactness = None
+    if not args.attention_only and args.quant_prep == "none":
+        C1 = Cw.clone()
+        vc.vc_cluster(Vd, Kc, 1, False, C1, lab, perm, ws=ws_c)  # what the second assignment reads
+        exactness = exactness_spans(vc, torch, Kd, Vd, Cw, C1, N, d)
+        del C1
+        vc.vc_cluster(Vd, Kc, 2, False, C.copy_(Cw), lab, perm, ws=ws_c)  # the step's labels again
+        torch.cuda.synchronize()
+
     errors = gpu_head0 = None
     if not args.attention_only and args.error_rows > 0:
         errors, gpu_head0 = error_columns(args, vc, torch, B, H, N, d, Kc, Qd, Kd, Vd, lab, perm, C, q, O, flags_q)
@@ -694,6 +722,8 @@ def main():
     }
     if errors is not None:
         res["errors"] = errors
+    if exactness is not None:
+        res["exactness_spans"] = exactness
     if args.quant_prep != "none":
         res["config"]["workload"] += " (quantiser with %s%s)" % (
             {"rope": "RoPE", "hadamard": "the Q/K Hadamard rotation",

@@ -81,9 +81,12 @@ const char* vc_status_string(vc_status s);
  *     s(K) <= 103 - 2 ceil(log2 N) (69 at N = 70 400; of the rotated keys when RoPE tables
  *     are given), the block means s(V) <= 89. vc_cluster, vc_cluster_balanced,
  *     vc_cluster_incremental: the member sums need s(V) <= 103 - 2 ceil(log2 N).
- *   - the squared distances sum_c (v_c - c_c)^2 (d <= 128 terms) of the k-means ranking
- *     are exact when the span of V together with the bf16-rounded centroids the assignment
- *     reads (vc_exponent_span kind 2) is at most 42; with size penalties, each nonzero
+ *   - the squared distances sum_c (v_c - c_c)^2 (d terms) of the k-means ranking are
+ *     exact when the span of V together with the bf16-rounded centroids the assignment
+ *     reads (vc_exponent_span kind 2) is at most 50 - log2 d, i.e. 43 for d = 128 and 44 for
+ *     d = 64 (each difference is a multiple of 2^q below 2^(E+2), each square a pair of
+ *     multiples of 2^(2q), and the 2d errors sent to lo stay below 2^(2q+53)); with size
+ *     penalties, each nonzero
  *     b_k = fl32(lambda n_k) must also lie in [2^(2q+23), 2^(2E+12)] (q, E of that union).
  *     The binary32 error bound that proves most labels without them assumes every nonzero
  *     |v| and |c| in [2^-56, 2^56) (no overflow or underflow in the products and norms):
@@ -93,9 +96,9 @@ const char* vc_status_string(vc_status s);
  * n^2 2^-104 (relative to the sum of the terms' magnitudes) of the exact value: a label can
  * then differ from the exact argmin only where the two best exact squared distances differ
  * by less than about 2^-88 of their size, and a mean only where its exact value lies that
- * close to a rounding boundary. Measured on two Wan-shaped test heads: V spans 35 and 36,
- * K spans 29 and 30, V with its bf16 centroids 35 and 36 -- inside every condition. The
- * oracle is exact for every finite input.
+ * close to a rounding boundary. Measured on the Wan-shaped benchmark step (all 40 heads): V
+ * spans up to 42, K up to 32, V with the bf16 centroids of either assignment up to 42 --
+ * inside every condition. The oracle is exact for every finite input.
  * ------------------------------------------------------------------------ */
 
 /* ------------------------------------------------------------------------

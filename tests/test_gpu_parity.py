@@ -742,7 +742,8 @@ def test_exponent_span_matches_reference():
 def test_exponent_span_of_the_video_workload_heads():
     """The checker on Wan-shaped heads (V, keys, and the bf16 centroids after k-means): the
     values must equal the reference, and these heads lie inside the exactness conditions of
-    include/vc.h (sums of N terms: span <= 103 - 2 ceil(log2 N); distances: span <= 42)."""
+    include/vc.h (sums of N terms: span <= 103 - 2 ceil(log2 N); distances: span <= 50 - log2 d,
+    43 at d = 128)."""
     N, d, K = 70400, 128, 550
     hs = [synth.gen_head("wan", 2, 0, h, N, d) for h in (0, 23)]
     V = np.stack([w["V"] for w in hs])[None]
@@ -757,7 +758,7 @@ def test_exponent_span_of_the_video_workload_heads():
         assert tuple(sc[i]) == _span_reference(synth.bf16_to_f32(synth.bf16_bits(C[0, i])).astype(np.float64))
         dist_span = max(sv[i][0], sc[i][0]) - min(sv[i][1], sc[i][1])
         print("[span] head %d: V (E %d, q %d, span %d), K span %d, V with bf16 centroids span %d; sums exact "
-              "up to %d: V %s, K %s; distances exact up to 42: %s"
+              "up to %d: V %s, K %s; distances exact up to 43: %s"
               % (i, sv[i][0], sv[i][1], sv[i][0] - sv[i][1], sk[i][0] - sk[i][1], dist_span, lim_sum,
-                 sv[i][0] - sv[i][1] <= lim_sum, sk[i][0] - sk[i][1] <= lim_sum, dist_span <= 42), flush=True)
-        assert sv[i][0] - sv[i][1] <= lim_sum and sk[i][0] - sk[i][1] <= lim_sum and dist_span <= 42
+                 sv[i][0] - sv[i][1] <= lim_sum, sk[i][0] - sk[i][1] <= lim_sum, dist_span <= 43), flush=True)
+        assert sv[i][0] - sv[i][1] <= lim_sum and sk[i][0] - sk[i][1] <= lim_sum and dist_span <= 43
