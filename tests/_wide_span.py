@@ -147,13 +147,14 @@ def running_sum(col: np.ndarray) -> float:
     return s
 
 
-def near_tie_tokens(rng, N: int, d: int, ntriples: int):
+def near_tie_tokens(rng, N: int, d: int, ntriples: int, tiny_exp: int = -20):
     """Tokens and centroids whose squared distances tie in every bit binary64 keeps.
 
     Centroid triple j (indices 3j, 3j+1, 3j+2) shares a base vector b_j (bf16 values of
     magnitude about 1 on the base channels) and adds L = 2^10 on a "far" channel; the token
-    near triple j is b_j plus tiny values (2^-20 or 2^-19) on a few "tiny" channels where the
-    centroids hold 0 or a tiny offset. Every distance from such a token to its triple is L^2
+    near triple j is b_j plus tiny values (2^t or 2^(t+1), t = tiny_exp) on a few "tiny"
+    channels where the centroids hold 0 or a tiny offset (2^(t-1) or 2^t); the exponent span
+    of tokens and centroids together is 10 - (t - 1). Every distance from such a token to its triple is L^2
     plus a sum of squares of order 2^-40: equal after binary64 rounding, different exactly.
     Triples alternate between a three-way near tie (all three within 2^-36) and a two-way one
     (the third centroid 64 further away). Returns (V bf16 bits [N, d], C0 float32
@@ -174,14 +175,14 @@ def near_tie_tokens(rng, N: int, d: int, ntriples: int):
         # tiny offsets on a few tiny channels: each centroid its own pattern
         for m in range(3):
             for ch in rng.choice(tiny, 3, replace=False):
-                C[3 * j + m, ch] = float(rng.choice([2.0 ** -21, -(2.0 ** -21), 2.0 ** -20]))
+                C[3 * j + m, ch] = float(rng.choice([2.0 ** (tiny_exp - 1), -(2.0 ** (tiny_exp - 1)), 2.0 ** tiny_exp]))
         if j % 2 == 1:
             C[3 * j + 2, far[2]] = 8.0  # the third one clearly further: a two-way near tie
     near = rng.integers(0, ntriples, N)
     V = bvec[near].copy()
     for t in range(N):
         for ch in rng.choice(tiny, 4, replace=False):
-            V[t, ch] = float(rng.choice([2.0 ** -20, -(2.0 ** -20), 2.0 ** -19]))
+            V[t, ch] = float(rng.choice([2.0 ** tiny_exp, -(2.0 ** tiny_exp), 2.0 ** (tiny_exp + 1)]))
     return synth.bf16_bits(V.astype(np.float32)), C.astype(np.float32), near
 
 

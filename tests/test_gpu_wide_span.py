@@ -223,3 +223,39 @@ def test_means_on_subnormal_grids(d):
         assert np.array_equal(Cg[0, h], c_or), h
         q = oracle.quantize(Q[0, h], Q[0, h], V[0, h], None, int(flags))
         assert np.array_equal(bf16_bits(out["mu"])[0, h], q["mu"]), h
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_cluster_near_ties_at_the_distance_span_limit(d):
+    """Near ties as above with tokens and centroids spanning exactly 50 - log2 d binary
+    exponents (the limit up to which the squared distances are exact, include/vc.h): the
+    checker reports that span, and labels, perm and centroids equal the oracle's and the
+    exact argmin."""
+    B, H, N, T = 1, 2, 1152, 8
+    K = 3 * T
+    span = 50 - int(np.log2(d))
+    rng = np.random.default_rng(120 + d)
+    hs = [ws.near_tie_tokens(rng, N, d, T, tiny_exp=11 - span) for _ in range(H)]
+    V = np.stack([x[0] for x in hs])[None]
+    C0 = np.stack([x[1] for x in hs])[None]
+    sv = vc.vc_exponent_span(to_dev_bf16(V)).cpu().numpy()[0]
+    sc = vc.vc_exponent_span(to_dev(C0), as_bf16=True).cpu().numpy()[0]
+    for h in range(H):
+        assert max(sv[h][0], sc[h][0]) - min(sv[h][1], sc[h][1]) == span, (h, sv[h], sc[h])
+    C = to_dev(C0)
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty_like(lab)
+    vc.vc_cluster(to_dev_bf16(V), K, 1, False, C, lab, perm)
+    torch.cuda.synchronize()
+    lg, pg, Cg = lab.cpu().numpy(), perm.cpu().numpy(), C.cpu().numpy()
+    for h in range(H):
+        Vf = synth.bf16_to_f32(V[0, h]).astype(np.float64)
+        near = hs[h][2]
+        for t in range(0, N, 7):
+            cand = [3 * near[t] + m for m in range(3)]
+            ex = [ws.exact_sqdist(Vf[t], C0[0, h, k]) for k in cand]
+            assert lg[0, h, t] == cand[int(np.argmin(ex))], (h, t)
+        l_or, p_or, c_or = oracle.kmeans(V[0, h], K, 1, cold=False, C=C0[0, h])
+        assert np.array_equal(lg[0, h], l_or), (h, np.count_nonzero(lg[0, h] != l_or))
+        assert np.array_equal(pg[0, h], p_or), h
+        assert np.array_equal(Cg[0, h], c_or), h
