@@ -13,6 +13,8 @@ Every value is an exact bfloat16 value. The columns contain many exactly cancell
 widely different magnitudes, so a binary64 running sum rounds in many places. Nothing here
 implements the method: the expected values are plain rational arithmetic.
 """
+from __future__ import annotations
+
 from fractions import Fraction as Fr
 
 import numpy as np
@@ -84,12 +86,13 @@ def _fill_column(rng, n: int, pieces: list, pair_exp: tuple) -> np.ndarray:
     return col
 
 
-def mean_columns(rng, n: int, ncols: int, target: str, small: bool = False):
+def mean_columns(rng, n: int, ncols: int, target: str, small: bool = False, g: int | None = None):
     """Columns of n values (16 <= n < 2^16) whose exact mean is T + s 2^-g with T a rounding tie
     of the target format ("f32": binary32, "bf16": bfloat16) just above 1, s = +-1 and g well
     below binary64 resolution. Returns (X [n, ncols] float64 of bf16 values, exact means as
     Fractions, correctly rounded means: float32 or bf16 bit patterns). small=True keeps every
-    value below 2 in magnitude (n >= 512: pieces below 0.25, pairs below 0.5)."""
+    value below 2 in magnitude (n >= 512: pieces below 0.25, pairs below 0.5). g, when given,
+    fixes the offset's exponent (else it is drawn from 56..69 for binary32, 55..67 for bf16)."""
     assert 16 <= n < 1 << 16
     X = np.zeros((n, ncols), np.float64)
     exact, rounded = [], []
@@ -98,16 +101,16 @@ def mean_columns(rng, n: int, ncols: int, target: str, small: bool = False):
         if target == "f32":
             odd = 2 * int(rng.integers(0, 1 << (11 if small else 15))) + 1
             tie, fb = 1 + Fr(odd, 1 << 24), 24
-            g = int(rng.integers(56, 70))
+            gg = int(rng.integers(56, 70)) if g is None else g
         else:
             odd = 2 * int(rng.integers(0, 64)) + 1
             tie, fb = 1 + Fr(odd, 1 << 8), 8
-            g = int(rng.integers(55, 68))
+            gg = int(rng.integers(55, 68)) if g is None else g
         # n T = n + (n odd) 2^-fb and n s 2^-g, each split into bf16 pieces
-        pieces = _split_bf16(n * odd, -fb) + [s * v for v in _split_bf16(n, -g)]
+        pieces = _split_bf16(n * odd, -fb) + [s * v for v in _split_bf16(n, -gg)]
         pair_exp = (-30, -2) if small else (-30, 6)
         X[:, c] = _fill_column(rng, n, pieces, pair_exp)
-        m = tie + s * Fr(1, 1 << g)
+        m = tie + s * Fr(1, 1 << gg)
         assert sum(Fr(float(v)) for v in X[:, c]) == n * m
         exact.append(m)
         rounded.append(f32_of(m) if target == "f32" else bf16_of(m))

@@ -259,3 +259,37 @@ def test_cluster_near_ties_at_the_distance_span_limit(d):
         assert np.array_equal(lg[0, h], l_or), (h, np.count_nonzero(lg[0, h] != l_or))
         assert np.array_equal(pg[0, h], p_or), h
         assert np.array_equal(Cg[0, h], c_or), h
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_cluster_means_at_the_sum_span_limit(d):
+    """Centroid means whose values span exactly 103 - 2 ceil(log2 N) binary exponents over
+    the head (the limit up to which the member sums are exact, include/vc.h; 83 at N = 1024):
+    the checker reports that span, and the centroids equal the oracle's and the exact means
+    rounded once."""
+    B, H, K, n = 1, 2, 4, 256
+    N = K * n
+    span = 103 - 2 * int(np.ceil(np.log2(N)))
+    rng = np.random.default_rng(130 + d)
+    # E = 6 (the identity channels' 64); lowest bit 8 - g of the offset pieces n 2^-g
+    g = 8 - (6 - span)
+    heads = [_clustered_head(rng, d, (n,) * K, lambda r, m, c: ws.mean_columns(r, m, c, "f32", g=g)[::2])
+             for _ in range(H)]
+    V = np.stack([synth.bf16_bits(h[0].astype(np.float32)) for h in heads])[None]
+    sv = vc.vc_exponent_span(to_dev_bf16(V)).cpu().numpy()[0]
+    for h in range(H):
+        assert sv[h][0] - sv[h][1] == span, (h, sv[h])
+    C0 = np.zeros((B, H, K, d), np.float32)
+    for k in range(K):
+        C0[..., k, k] = 64.0
+    C = to_dev(C0)
+    lab = torch.empty((B, H, N), dtype=torch.int32, device="cuda")
+    perm = torch.empty_like(lab)
+    vc.vc_cluster(to_dev_bf16(V), K, 1, False, C, lab, perm)
+    torch.cuda.synchronize()
+    Cg = C.cpu().numpy()
+    for h in range(H):
+        _, _, c_or = oracle.kmeans(V[0, h], K, 1, cold=False, C=C0[0, h])
+        assert np.array_equal(Cg[0, h], c_or), (h, np.count_nonzero(Cg[0, h] != c_or))
+        for k in range(K):
+            assert np.array_equal(Cg[0, h, k, K:], heads[h][2][k]), (h, k)
