@@ -293,3 +293,48 @@ def test_cluster_means_at_the_sum_span_limit(d):
         assert np.array_equal(Cg[0, h], c_or), (h, np.count_nonzero(Cg[0, h] != c_or))
         for k in range(K):
             assert np.array_equal(Cg[0, h, k, K:], heads[h][2][k]), (h, k)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_means_at_the_sum_span_limits(d):
+    """Block means with V spanning exactly 89 binary exponents (the limit for 128-term sums)
+    and the key mean with K spanning exactly 83 (the limit for N = 1024 terms), both next to
+    rounding ties: the checker reports those spans, the oracle's means equal the rational
+    ones, and every quantiser output equals the oracle's."""
+    B, H, N = 1, 2, 1024
+    nb = N // 128
+    rng = np.random.default_rng(140 + d)
+    Qs, Ks, Vs, perms, mus, kbars = [], [], [], [], [], []
+    for h in range(H):
+        Vp = np.zeros((N, d))
+        mu = np.zeros((nb, d), np.int64)
+        for b in range(nb):  # E = 6 (pairs), lowest bit 7 - g of the offsets 128 2^-g: span g - 1
+            X, _, r = ws.mean_columns(rng, 128, d, "bf16", g=90)
+            Vp[128 * b:128 * (b + 1)] = X
+            mu[b] = r
+        perm = synth.rand_perm(N, 141, 0, h)
+        V = np.zeros_like(Vp)
+        V[perm] = Vp
+        Kx, _, kb = ws.mean_columns(rng, N, d, "f32", small=True, g=92)  # E = 1, lowest bit 10 - g
+        Qs.append(synth.gen_head("wan", 142, 0, h, N, d)["Q"])
+        Ks.append(synth.bf16_bits(Kx.astype(np.float32)))
+        Vs.append(synth.bf16_bits(V.astype(np.float32)))
+        perms.append(perm)
+        mus.append(mu)
+        kbars.append(np.array(kb, np.float32))
+    Q, K, V, P = (np.stack(x)[None] for x in (Qs, Ks, Vs, perms))
+    sv = vc.vc_exponent_span(to_dev_bf16(V)).cpu().numpy()[0]
+    sk = vc.vc_exponent_span(to_dev_bf16(K)).cpu().numpy()[0]
+    for h in range(H):
+        assert sv[h][0] - sv[h][1] == 103 - 2 * 7 and sk[h][0] - sk[h][1] == 103 - 2 * 10, (h, sv[h], sk[h])
+    flags = vc.VC_F_KSMOOTH | vc.VC_F_VSMOOTH
+    out = gpu_quantize(Q, K, V, P, flags)
+    g = {k: (bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
+    for h in range(H):
+        q = oracle.quantize(Q[0, h], K[0, h], V[0, h], P[0, h], int(flags))
+        assert np.array_equal(q["mu"].astype(np.int64), mus[h])
+        assert np.array_equal(q["kbar"], kbars[h])
+        assert np.array_equal(bf16_bits(out["mu"])[0, h].astype(np.int64), mus[h]), h
+        for k in ("Qq", "sQ", "Kq", "sK", "sV", "mu_scaled"):
+            assert np.array_equal(g[k][0, h], q[k]), (h, k)
+        assert np.array_equal(vq_rowmajor(g["Vq"])[0, h], q["Vq"]), h
