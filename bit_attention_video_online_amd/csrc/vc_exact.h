@@ -7,8 +7,8 @@
 // leaves goes to lo. hi + lo is then the exact sum as long as lo's own additions do not
 // round, i.e. while every term is an integer multiple of 2^q and the magnitudes of all
 // the errors collected in lo stay below 2^(q+53): for n terms below 2^(E+1) that holds
-// when E - q <= 104 - 2 ceil(log2 n) (every error is at most 2^-53 of a partial sum, which
-// is below n 2^(E+1); merges of partial pairs add no more errors than terms). Under that
+// when E - q <= 103 - 2 ceil(log2 n) (every error is at most 2^-53 of a partial sum, which
+// is below n 2^(E+1), and terms plus merges of partial pairs give at most 2n errors). Under that
 // condition the result is independent of the order of the terms and of how the partial
 // pairs are combined. All arithmetic here is op by op (the library is built without FMA
 // contraction), which TwoSum relies on.
